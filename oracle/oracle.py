@@ -1,0 +1,307 @@
+"""fp64 CPU oracle for packed native-resolution joint attention.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, the smoke check in
+``__graft_entry__.py`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+or run this module. The library (``packed_attention_nr_amd``) never imports it
+and this module imports nothing from the library: the two share no code.
+
+What it computes is the plain definition of one NR-MMDiT attention core, as the
+Mage-Flow pages describe it:
+
+* packing: every sample's text tokens and flattened latent-grid tokens sit back
+  to back in one contiguous batch, with per-sample cumulative offsets
+  (findtube.ai transcript "Mage-Flow: Efficient Native-Resolution Image
+  Generation and Editing" at [00:03:16] and [00:04:03]; picx.dev summary
+  "Mage-Flow: An Efficient Native-Resolution Foundation Model ...", section
+  "Native-Resolution MMDiT (NR-MMDiT)", bullet "Native-resolution packing");
+* modality-specific normalisation of the joint-attention inputs (picx.dev,
+  section "Native-Resolution MMDiT (NR-MMDiT)", first bullet; transcript at
+  [00:00:00]), taken here as RMSNorm of Q and K per head with one gain vector
+  per (Q or K, text or image);
+* a per-sample 2D rotary embedding of image tokens by their own (row, col)
+  (transcript at [00:03:16]; aiany.app entry, "Key Capabilities");
+* joint text+image self-attention restricted to each sample, i.e. block
+  diagonal over the cumulative offsets (picx.dev, same section: FlashAttention
+  with per-sample cumulative offsets).
+
+The method (variable-length flash attention) reaches exactly this definition up
+to rounding, so the oracle is the definition written out in float64 with
+numpy; matrix products use numpy's BLAS matmul. Readings taken where the pages
+are silent (each also listed in the design doc):
+
+* token order inside a sample: text first, then the image grid row-major;
+* RMSNorm: over the d elements of one (token, head); eps inside the square
+  root, added to the mean square; gain applied after normalisation; no bias;
+  V is not normalised;
+* order: RMSNorm, then gain, then RoPE;
+* RoPE: the first d/2 dimensions rotate by the row index and the last d/2 by
+  the column index, 0-based; inside each half, adjacent pairs (2j, 2j+1)
+  rotate by angle pos * theta^(-4j/d), j < d/4; text tokens are not rotated;
+* softmax scale 1/sqrt(d), no causal mask, no dropout, natural-log lse.
+
+Parity status of each function (how it is pinned by tests other than itself):
+``layout`` (pure-Python enumeration, token counts), ``rms_norm`` (closed
+forms), ``rope_apply`` (hand values at d=4 and d=8, norm preservation,
+relative-position property), ``attention_forward`` (pure-Python brute force,
+torch fp64 library attention, closed forms, packing invariants),
+``attention_backward`` / ``rope_backward`` / ``rms_norm_backward``
+(central finite differences, torch fp64 autograd, closed forms).
+The RoPE pair layout, frequency schedule and position origin themselves are
+readings, not statements of the pages: against the pages they are parity
+unpinned; the code is pinned only against that written reading.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "Layout", "layout", "rope_frequencies", "rope_angles", "rope_apply",
+    "rope_backward", "rms_norm", "rms_norm_backward", "token_gains",
+    "prologue", "attention_forward", "attention_backward", "forward",
+    "backward",
+]
+
+QUERY_BLOCK = 2048  # rows of the score matrix formed at once (memory bound only)
+
+
+# --------------------------------------------------------------------------
+# Packing layout
+# --------------------------------------------------------------------------
+@dataclass
+class Layout:
+    cu_seqlens: np.ndarray   # int64 [S+1], cu[0] = 0, cu[S] = N
+    segment: np.ndarray      # int64 [N], sample index of each token
+    is_image: np.ndarray     # bool  [N]
+    row: np.ndarray          # int64 [N], 0 for text tokens
+    col: np.ndarray          # int64 [N], 0 for text tokens
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+
+def layout(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int]) -> Layout:
+    """Packing of samples into one contiguous token batch.
+
+    Sample i occupies tokens cu[i] .. cu[i+1]-1 where cu[i+1] = cu[i] + T_i + h_i*w_i:
+    first its T_i text tokens, then its h_i x w_i latent grid flattened row-major,
+    the grid token at (r, c) being token cu[i] + T_i + r*w_i + c.
+    (picx.dev, "Native-Resolution MMDiT (NR-MMDiT)": images flattened into
+    variable-length token sequences, packed with text, per-sample cumulative
+    offsets; transcript [00:03:16]: a single contiguous batch.)
+    """
+    T = np.asarray(text_len, dtype=np.int64)
+    h = np.asarray(grid_h, dtype=np.int64)
+    w = np.asarray(grid_w, dtype=np.int64)
+    L = T + h * w
+    cu = np.zeros(len(L) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(L)
+    N = int(cu[-1])
+    segment = np.zeros(N, dtype=np.int64)
+    is_image = np.zeros(N, dtype=bool)
+    row = np.zeros(N, dtype=np.int64)
+    col = np.zeros(N, dtype=np.int64)
+    for i in range(len(L)):
+        segment[cu[i]:cu[i + 1]] = i
+        n_img = int(h[i] * w[i])
+        if n_img:
+            idx = cu[i] + T[i] + np.arange(n_img)
+            is_image[idx] = True
+            row[idx] = np.arange(n_img) // w[i]
+            col[idx] = np.arange(n_img) % w[i]
+    return Layout(cu, segment, is_image, row, col)
+
+
+# --------------------------------------------------------------------------
+# 2D rotary embedding (image tokens only)
+# --------------------------------------------------------------------------
+def rope_frequencies(d: int, theta: float = 10000.0) -> np.ndarray:
+    """omega_j = theta^(-4j/d) for j < d/4: each half of the head dimension is a
+    1D rotary embedding of size d/2 (frequencies theta^(-2j/(d/2)))."""
+    if d % 4:
+        raise ValueError("head_dim must be a multiple of 4 for 2D RoPE")
+    j = np.arange(d // 4, dtype=np.float64)
+    return np.power(float(theta), -4.0 * j / d)
+
+
+def rope_angles(lay: Layout, d: int, theta: float = 10000.0) -> np.ndarray:
+    """Rotation angle of each of the d/2 dimension pairs of each token, [N, d/2].
+
+    Pair p < d/4 (dimensions 2p, 2p+1) turns by row * omega_p; pair d/4 + j
+    (dimensions d/2 + 2j, d/2 + 2j + 1) turns by col * omega_j. Text tokens get
+    angle 0, i.e. no rotation. (Transcript [00:03:16]: per-sample 2D rotary
+    positional embeddings keeping each sample's own pixel layout.)
+    """
+    om = rope_frequencies(d, theta)
+    r = np.where(lay.is_image, lay.row, 0).astype(np.float64)
+    c = np.where(lay.is_image, lay.col, 0).astype(np.float64)
+    return np.concatenate([r[:, None] * om[None, :], c[:, None] * om[None, :]], axis=1)
+
+
+def rope_apply(x: np.ndarray, angles: np.ndarray) -> np.ndarray:
+    """Rotate each pair (x[2p], x[2p+1]) of every head by angles[t, p]:
+    (a, b) -> (a cos phi - b sin phi, a sin phi + b cos phi). x is [N, H, d]."""
+    cos = np.cos(angles)[:, None, :]
+    sin = np.sin(angles)[:, None, :]
+    a = x[..., 0::2]
+    b = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = a * cos - b * sin
+    out[..., 1::2] = a * sin + b * cos
+    return out
+
+
+def rope_backward(dy: np.ndarray, angles: np.ndarray) -> np.ndarray:
+    """Gradient through ``rope_apply``: the transpose of a rotation, i.e. the
+    rotation by -phi applied to the incoming gradient."""
+    return rope_apply(dy, -angles)
+
+
+# --------------------------------------------------------------------------
+# Per-modality RMSNorm of Q and K
+# --------------------------------------------------------------------------
+def token_gains(gains: np.ndarray, lay: Layout, which: str) -> np.ndarray:
+    """Per-token gain vector [N, d] from the four gain rows
+    (0 q_text, 1 q_image, 2 k_text, 3 k_image)."""
+    g = np.asarray(gains, dtype=np.float64)
+    base = 0 if which == "q" else 2
+    return np.where(lay.is_image[:, None], g[base + 1][None, :], g[base][None, :])
+
+
+def rms_norm(x: np.ndarray, g_tok: np.ndarray, eps: float):
+    """y = x * rho * g with rho = (mean over the d elements of x^2 + eps)^(-1/2),
+    per (token, head). Returns (y, rho) with rho of shape [N, H]."""
+    ms = np.mean(x * x, axis=-1)
+    rho = 1.0 / np.sqrt(ms + eps)
+    return x * rho[..., None] * g_tok[:, None, :], rho
+
+
+def rms_norm_backward(x: np.ndarray, g_tok: np.ndarray, rho: np.ndarray, dy: np.ndarray):
+    """Gradients of y = x * rho(x) * g.
+
+    dx = rho * g * dy - (rho^3 / d) * x * sum_k g_k dy_k x_k
+    dg (per token and head) = dy * x * rho, left unsummed: [N, H, d].
+    """
+    d = x.shape[-1]
+    gdy = g_tok[:, None, :] * dy
+    dot = np.sum(gdy * x, axis=-1)
+    dx = rho[..., None] * gdy - (rho ** 3 / d)[..., None] * x * dot[..., None]
+    dg = dy * x * rho[..., None]
+    return dx, dg
+
+
+def prologue(q, k, gains, lay: Layout, eps: float = 1e-6, theta: float = 10000.0):
+    """Q-hat and K-hat: RMSNorm with the modality's gain, then 2D RoPE."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    d = q.shape[-1]
+    ang = rope_angles(lay, d, theta)
+    yq, rq = rms_norm(q, token_gains(gains, lay, "q"), eps)
+    yk, rk = rms_norm(k, token_gains(gains, lay, "k"), eps)
+    return rope_apply(yq, ang), rope_apply(yk, ang), rq, rk
+
+
+# --------------------------------------------------------------------------
+# Block-diagonal joint attention
+# --------------------------------------------------------------------------
+def _heads_first(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64).transpose(1, 0, 2))
+
+
+def attention_forward(qh, kh, v, cu_seqlens, q_block: int = QUERY_BLOCK):
+    """Per sample i and head h: O = softmax(Q_i K_i^T / sqrt(d)) V_i over that
+    sample's tokens only (text and image jointly, no mask inside a sample), and
+    lse = ln sum_j exp(S_tj). Returns O [N, H, d] and lse [N, H]."""
+    Q, K, V = _heads_first(qh), _heads_first(kh), _heads_first(v)
+    H, N, d = Q.shape
+    scale = 1.0 / np.sqrt(d)
+    O = np.zeros((H, N, d))
+    lse = np.zeros((H, N))
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        for h in range(H):
+            Kh, Vh = K[h, a:b], V[h, a:b]
+            for q0 in range(a, b, q_block):
+                q1 = min(q0 + q_block, b)
+                s = (Q[h, q0:q1] @ Kh.T) * scale
+                m = s.max(axis=1, keepdims=True)
+                p = np.exp(s - m)
+                l = p.sum(axis=1, keepdims=True)
+                O[h, q0:q1] = (p @ Vh) / l
+                lse[h, q0:q1] = (m + np.log(l))[:, 0]
+    return O.transpose(1, 0, 2).copy(), lse.T.copy()
+
+
+def attention_backward(qh, kh, v, dout, cu_seqlens, q_block: int = QUERY_BLOCK):
+    """Gradients of sum(dO * O) for the attention above, per sample and head:
+    P = softmax(S), S = Q K^T / sqrt(d);  dV = P^T dO;  dP = dO V^T;
+    dS = P * (dP - rowsum(P * dP));  dQ = dS K / sqrt(d);  dK = dS^T Q / sqrt(d).
+    Returns dQ-hat, dK-hat, dV, each [N, H, d]."""
+    Q, K, V, dO = (_heads_first(t) for t in (qh, kh, v, dout))
+    H, N, d = Q.shape
+    scale = 1.0 / np.sqrt(d)
+    dQ = np.zeros((H, N, d))
+    dK = np.zeros((H, N, d))
+    dV = np.zeros((H, N, d))
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        for h in range(H):
+            Kh, Vh = K[h, a:b], V[h, a:b]
+            for q0 in range(a, b, q_block):
+                q1 = min(q0 + q_block, b)
+                Qb, dOb = Q[h, q0:q1], dO[h, q0:q1]
+                s = (Qb @ Kh.T) * scale
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                dV[h, a:b] += p.T @ dOb
+                dp = dOb @ Vh.T
+                ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+                dQ[h, q0:q1] = (ds @ Kh) * scale
+                dK[h, a:b] += (ds.T @ Qb) * scale
+    back = lambda t: t.transpose(1, 0, 2).copy()
+    return back(dQ), back(dK), back(dV)
+
+
+# --------------------------------------------------------------------------
+# Whole forward / backward of the attention core
+# --------------------------------------------------------------------------
+def forward(text_len, grid_h, grid_w, q, k, v, gains, eps=1e-6, theta=10000.0,
+            lay: Optional[Layout] = None):
+    """Pre-norm Q, K, V [N, H, d] -> dict with q_hat, k_hat, rstd_q, rstd_k,
+    o [N, H, d] and lse [N, H] (all float64)."""
+    if lay is None:
+        lay = layout(text_len, grid_h, grid_w)
+    qh, kh, rq, rk = prologue(q, k, gains, lay, eps, theta)
+    o, lse = attention_forward(qh, kh, v, lay.cu_seqlens)
+    return dict(layout=lay, q_hat=qh, k_hat=kh, rstd_q=rq, rstd_k=rk, o=o, lse=lse)
+
+
+def backward(text_len, grid_h, grid_w, q, k, v, gains, dout, eps=1e-6,
+             theta=10000.0, lay: Optional[Layout] = None):
+    """Gradients of sum(dout * O) with respect to the pre-norm q, k, v and the
+    four gain rows. Returns dict with dq, dk, dv [N, H, d], dgains [4, d], and
+    the intermediate dq_hat, dk_hat."""
+    if lay is None:
+        lay = layout(text_len, grid_h, grid_w)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    d = q.shape[-1]
+    ang = rope_angles(lay, d, theta)
+    gq, gk = token_gains(gains, lay, "q"), token_gains(gains, lay, "k")
+    yq, rq = rms_norm(q, gq, eps)
+    yk, rk = rms_norm(k, gk, eps)
+    qh, kh = rope_apply(yq, ang), rope_apply(yk, ang)
+    dqh, dkh, dv = attention_backward(qh, kh, v, dout, lay.cu_seqlens)
+    dq, dgq = rms_norm_backward(q, gq, rq, rope_backward(dqh, ang))
+    dk, dgk = rms_norm_backward(k, gk, rk, rope_backward(dkh, ang))
+    img = lay.is_image
+    dgains = np.stack([
+        dgq[~img].sum(axis=(0, 1)), dgq[img].sum(axis=(0, 1)),
+        dgk[~img].sum(axis=(0, 1)), dgk[img].sum(axis=(0, 1)),
+    ])
+    return dict(dq=dq, dk=dk, dv=dv, dgains=dgains, dq_hat=dqh, dk_hat=dkh)
