@@ -1,0 +1,228 @@
+"""Benchmark of the packed joint-attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixed6]
+
+One step = one pass of the whole path over one synthetic pack: the host pack
+plan and its upload, the forward (QK-norm + 2D RoPE prologue, var-len
+attention) and the backward (D = rowsum(dO*O), var-len attention backward,
+prologue backward with gain gradients). HIP events recorded on the launch
+stream between the stages give each kernel's duration inside the timed region.
+Prints one JSON line.
+
+metric: bf16 forward+backward attention throughput in TFLOP/s, counting
+4*H*d*sum(L_i^2) for the forward and 10*H*d*sum(L_i^2) for the backward,
+divided by the whole step time (plan, prologues and preprocess included).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "packed varlen attn TFLOP/s (bf16 fwd+bwd) & % MFMA peak; ms/layer at 1024²"
+
+
+def sum_l2(inp):
+    L = inp.seqlens().astype(np.int64)
+    return int((L * L).sum())
+
+
+def cpu_baseline(inp, heads, seconds_target=20.0):
+    """Time the fp64 oracle (fwd+bwd) on a subset of heads; report TFLOP/s of
+    the same algorithmic count, scaled to the metric's unit."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    hs = list(range(heads))
+    q, k, v, do = (x[:, hs] for x in (inp.q, inp.k, inp.v, inp.dout))
+    t0 = time.perf_counter()
+    f = oracle.forward(inp.text_len, inp.grid_h, inp.grid_w, q, k, v, inp.gains)
+    oracle.backward(inp.text_len, inp.grid_h, inp.grid_w, q, k, v, inp.gains, do, lay=f["layout"])
+    dt = time.perf_counter() - t0
+    flops = 14.0 * heads * inp.head_dim * sum_l2(inp)
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(threads),
+                kind="oracle",
+                sample=f"fp64 numpy oracle forward+backward of {heads} of {inp.heads} heads "
+                       f"of the same pack ({dt:.1f} s); throughput of that sample")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixed6", choices=["mixed6", "gen2048", "small64"])
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the work would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import packed_attention_nr_amd as pam
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = workloads.get(args.workload)
+    inp = workloads.draw(args.workload)
+    N, H, d = inp.num_tokens, inp.heads, inp.head_dim
+    sl2 = sum_l2(inp)
+    fwd_flop = 4.0 * H * d * sl2
+    bwd_flop = 10.0 * H * d * sl2
+
+    bf = torch.bfloat16
+    up = lambda a: torch.from_numpy(a).to(device=dev, dtype=bf)
+    q, k, v, do = up(inp.q), up(inp.k), up(inp.v), up(inp.dout)
+    gains = torch.from_numpy(inp.gains).to(dev)
+    o = torch.empty((N, H, d), dtype=bf, device=dev)
+    q_hat, k_hat = torch.empty_like(o), torch.empty_like(o)
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev)
+    rstd = torch.empty((2, N, H), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(o), torch.empty_like(o), torch.empty_like(o)
+    dgains = torch.empty((4, d), dtype=torch.float32, device=dev)
+
+    plan0, blob0 = pam.mmdit_pack_plan(inp.text_len, inp.grid_h, inp.grid_w, H, d, pam.MMDIT_BF16)
+    ws = torch.empty(int(plan0.bwd_workspace_bytes), dtype=torch.uint8, device=dev)
+    blob_dev = [torch.empty(int(plan0.blob_bytes), dtype=torch.uint8, device=dev) for _ in range(2)]
+    pinned = [torch.empty(int(plan0.blob_bytes), dtype=torch.uint8).pin_memory() for _ in range(2)]
+    copied = [torch.cuda.Event() for _ in range(2)]
+    for e in copied:
+        e.record()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    S = pam.FWD_STAGES
+    B = pam.BWD_STAGES
+
+    def step(i, evs=None):
+        # a1: host plan + upload of its blob (pinned ring of two buffers)
+        plan, blob = pam.mmdit_pack_plan(inp.text_len, inp.grid_h, inp.grid_w, H, d, pam.MMDIT_BF16)
+        slot = i & 1
+        copied[slot].synchronize()
+        pinned[slot].numpy()[:] = blob
+        blob_dev[slot].copy_(pinned[slot], non_blocking=True)
+        copied[slot].record()
+        bd = blob_dev[slot]
+        rec = (lambda j: evs[j].record(stream)) if evs else (lambda j: None)
+        fa = dict(q=q, k=k, v=v, q_stride=H * d, k_stride=H * d, v_stride=H * d, gains=gains,
+                  o=o, lse=lse, q_hat=q_hat, k_hat=k_hat, rstd=rstd)
+        rec(0)
+        pam.mmdit_attn_fwd(plan, bd, stages=S["prologue"], **fa)
+        rec(1)
+        pam.mmdit_attn_fwd(plan, bd, stages=S["attention"], **fa)
+        rec(2)
+        ba = dict(q=q, k=k, v=v, q_hat=q_hat, k_hat=k_hat, o=o, dout=do, q_stride=H * d,
+                  k_stride=H * d, v_stride=H * d, dout_stride=H * d, gains=gains, lse=lse,
+                  rstd=rstd, dq=dq, dk=dk, dv=dv, dgains=dgains, workspace=ws)
+        pam.mmdit_attn_bwd(plan, bd, stages=B["pre"], **ba)
+        rec(3)
+        pam.mmdit_attn_bwd(plan, bd, stages=B["attention"], **ba)
+        rec(4)
+        pam.mmdit_attn_bwd(plan, bd, stages=B["prologue"], **ba)
+        rec(5)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    names = ["prologue_fwd", "attn_fwd", "bwd_pre", "attn_bwd", "prologue_bwd"]
+    kt = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+          for j, n in enumerate(names)}
+    value = (fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12
+    bwd_tflops = bwd_flop / (kt["attn_bwd"] * 1e-3) / 1e12
+    fwd_tflops = fwd_flop / (kt["attn_fwd"] * 1e-3) / 1e12
+    pro_bytes = 8.0 * N * H * d
+    pro_gbs = pro_bytes / (kt["prologue_fwd"] * 1e-3) / 1e9
+
+    # ms/layer at 1024^2: the whole forward call (prologue + attention) on the
+    # 1024^2 generation pack (512 text + 64x64 latents, H=24, d=128).
+    g = workloads.draw("gen1024")
+    gpack = pam.Pack(g.text_len, g.grid_h, g.grid_w, g.heads, g.head_dim, "bf16", device=dev)
+    gq, gk, gv = up(g.q), up(g.k), up(g.v)
+    ggains = torch.from_numpy(g.gains).to(dev)
+    for _ in range(5):
+        pam.forward(gpack, gq, gk, gv, ggains, save_for_backward=False)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 50
+    gout = dict(o=torch.empty((g.num_tokens, g.heads, g.head_dim), dtype=bf, device=dev),
+                lse=torch.empty((g.heads, g.num_tokens), dtype=torch.float32, device=dev))
+    gws = gpack.workspace("fwd")
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        pam.mmdit_attn_fwd(gpack.plan, gpack.blob_dev, q=gq, k=gk, v=gv, q_stride=g.heads * g.head_dim,
+                           k_stride=g.heads * g.head_dim, v_stride=g.heads * g.head_dim,
+                           gains=ggains, workspace=gws, **gout)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_layer_1024 = e0.elapsed_time(e1) / reps
+    gen_fwd_tflops = 4.0 * g.heads * g.head_dim * sum_l2(g) / (ms_layer_1024 * 1e-3) / 1e12
+
+    if args.copy_calibration:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V/dO, gains 1+0.1*N(0,1))",
+        "config": {"workload": w.title, "tokens": N, "samples": len(inp.text_len),
+                   "seqlens": inp.seqlens().tolist(), "heads": H, "head_dim": d,
+                   "parallelism": "none (1 GPU)"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "kernel_ms": {n: round(t, 4) for n, t in kt.items()},
+        "attn_fwd_tflops": round(fwd_tflops, 2),
+        "attn_fwd_frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "attn_bwd_tflops": round(bwd_tflops, 2),
+        "attn_bwd_frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+        "prologue_fwd_gbs": round(pro_gbs, 1),
+        "prologue_fwd_frac_hbm": round(pro_gbs / PEAK_HBM_GBS, 4),
+        "ms_per_layer_1024": round(ms_layer_1024, 4),
+        "gen1024_fwd_tflops": round(gen_fwd_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "attn_bwd_bf16_kernel<128>",
+                     "achieved": round(bwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

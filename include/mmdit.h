@@ -1,0 +1,172 @@
+/*
+ * mmdit.h - C ABI of the packed native-resolution joint-attention core
+ * (the attention part of an NR-MMDiT block) for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes, per the Mage-Flow pages:
+ *   - packing: every sample's text tokens and flattened image-latent grid are
+ *     laid back to back in one contiguous batch with per-sample cumulative
+ *     offsets, under a fixed token budget, with no padding
+ *     (findtube.ai transcript "Mage-Flow: Efficient Native-Resolution Image
+ *     Generation and Editing" at [00:03:16] and [00:04:03]; picx.dev summary
+ *     "Mage-Flow: An Efficient Native-Resolution Foundation Model for Image
+ *     Generation and Editing", section "Native-Resolution MMDiT (NR-MMDiT)");
+ *   - modality-specific normalisation before joint attention (same picx.dev
+ *     section, first bullet; transcript at [00:00:00]): RMSNorm of Q and K
+ *     over each head's d elements, with one gain vector per (Q or K, text or
+ *     image);
+ *   - per-sample 2D rotary embedding of image tokens from their own (row, col)
+ *     (transcript at [00:03:16]; aiany.app entry, "Key Capabilities");
+ *   - joint text+image self-attention confined to each sample (variable-length
+ *     attention over the cumulative offsets; picx.dev, same section), and its
+ *     backward for training.
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *   - token order inside a sample: text tokens, then the latent grid row-major;
+ *   - RMSNorm: rho = (mean_k x_k^2 + eps)^(-1/2), y = x * rho * g; then RoPE;
+ *   - RoPE: dims [0, d/2) turn by the row index, dims [d/2, d) by the column
+ *     index (0-based); inside each half, adjacent pairs (2j, 2j+1) turn by
+ *     pos * theta^(-4j/d); text tokens are not rotated;
+ *   - softmax scale 1/sqrt(d), no causal mask, natural-log lse.
+ *
+ * Tensor layout: Q, K, V, O and their gradients are [N][H][d] (token-major,
+ * then head, then the d elements contiguous). "stride" arguments give the
+ * number of ELEMENTS between consecutive tokens (>= H*d, a multiple of 8), so
+ * Q/K/V may be views into a fused [N][3][H][d] projection output. Output
+ * tensors are always dense [N][H][d]. lse and D are [H][N] fp32.
+ *
+ * Ownership and threading: the caller owns every buffer (host descriptor
+ * arrays, the host plan blob, its device copy, tensors, workspace). The
+ * library never allocates or frees device memory and never synchronises:
+ * mmdit_attn_fwd / mmdit_attn_bwd only enqueue kernels on the caller's HIP
+ * stream and return; buffers must stay alive until the stream passes them.
+ * All entry points are reentrant. Errors: every argument is validated on the
+ * host before anything is launched; on a non-OK return nothing was enqueued
+ * and no output was touched, and mmdit_last_error() (thread-local) says why.
+ */
+#ifndef MMDIT_H
+#define MMDIT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MMDIT_ABI_VERSION 1
+
+typedef enum {
+  MMDIT_OK = 0,
+  MMDIT_ERR_INVALID_ARG = 1,       /* NULL / negative / misaligned / inconsistent argument */
+  MMDIT_ERR_UNSUPPORTED = 2,       /* valid but not built: e.g. head_dim not 64 or 128 */
+  MMDIT_ERR_BUFFER_TOO_SMALL = 3,  /* host blob or workspace smaller than required */
+  MMDIT_ERR_BUDGET = 4,            /* total tokens exceed the descriptor's token budget */
+  MMDIT_ERR_HIP = 5                /* a HIP launch failed; see mmdit_last_error() */
+} mmdit_status;
+
+typedef enum { MMDIT_F32 = 0, MMDIT_BF16 = 1 } mmdit_dtype;
+
+/* Description of one pack (host memory, read during mmdit_pack_plan only).
+ * Sample i holds text_len[i] text tokens followed by a grid_h[i] x grid_w[i]
+ * latent grid (both 0 for a text-only sample); every sample has >= 1 token. */
+typedef struct {
+  int32_t num_samples;          /* S >= 1 */
+  const int32_t *text_len;      /* [S], >= 0 */
+  const int32_t *grid_h;        /* [S], >= 0, < 32768 */
+  const int32_t *grid_w;        /* [S], >= 0, < 32768; zero iff grid_h is zero */
+  int32_t num_heads;            /* H >= 1 */
+  int32_t head_dim;             /* d: 64 or 128 */
+  int32_t dtype;                /* mmdit_dtype of Q, K, V, O and gradients */
+  float rope_theta;             /* > 0, e.g. 10000 */
+  float rms_eps;                /* >= 0, e.g. 1e-6 */
+  int64_t token_budget;         /* 0 = none; else total tokens must be <= budget */
+} mmdit_pack_desc;
+
+/* Plan: plain data filled by mmdit_pack_plan; valid for every fwd/bwd call on
+ * a pack with the same descriptor. The blob (host_blob) it describes must be
+ * copied by the caller to device memory (16-byte aligned) once, and that copy
+ * passed as plan_blob_dev. Blob sections (offsets in bytes, 256-aligned):
+ *   cu_seqlens  int32 [S+1]
+ *   tok_meta    int32 [N]   bit 31 = image, bits 30..16 = row, bits 15..0 = col
+ *   fwd_items   int32 [num_fwd_items][4] = {seg_start, seg_end, tile_start, sample}
+ *               one per q_tile-row query tile, longest segment first
+ *   bwd_items   int32 [num_bwd_items][4], same for kv_tile-row key tiles
+ *   rope        fp32  [rope_rows][d/4][2] = {cos, sin}(pos * theta^(-4j/d)),
+ *               computed in double precision and rounded once. */
+typedef struct {
+  int32_t num_samples, total_tokens, max_seqlen, num_heads, head_dim, dtype;
+  int32_t q_tile, kv_tile, num_fwd_items, num_bwd_items, rope_rows, reserved;
+  float rope_theta, rms_eps;
+  uint64_t blob_bytes;
+  uint64_t off_cu_seqlens, off_tok_meta, off_fwd_items, off_bwd_items, off_rope;
+  uint64_t fwd_workspace_bytes;  /* needed by mmdit_attn_fwd when q_hat/k_hat are NULL */
+  uint64_t bwd_workspace_bytes;  /* needed by mmdit_attn_bwd */
+  uint64_t fingerprint;          /* hash of every field above; checked on each call */
+} mmdit_plan;
+
+/* Build the plan of one pack. host_blob == NULL: size query only (plan is
+ * filled, plan->blob_bytes says how much host memory the blob needs). Runs on
+ * the host, touches no device. Errors: INVALID_ARG, UNSUPPORTED (head_dim),
+ * BUDGET, BUFFER_TOO_SMALL (host_blob_bytes < plan->blob_bytes). */
+mmdit_status mmdit_pack_plan(const mmdit_pack_desc *desc, mmdit_plan *plan,
+                             void *host_blob, uint64_t host_blob_bytes);
+
+/* Stage selection for mmdit_fwd_args.stages / mmdit_bwd_args.stages. 0 = all.
+ * A later stage alone reads what the earlier ones wrote (e.g. ATTENTION alone
+ * reads the caller's q_hat / k_hat). */
+#define MMDIT_STAGE_PROLOGUE      1u  /* fwd: RMSNorm + RoPE of Q and K -> q_hat, k_hat */
+#define MMDIT_STAGE_ATTENTION     2u  /* fwd: var-len attention -> o, lse */
+#define MMDIT_STAGE_BWD_PRE       1u  /* bwd: D = rowsum(dO * O), clear dQ-hat accumulator */
+#define MMDIT_STAGE_BWD_ATTENTION 2u  /* bwd: dQ-hat, dK-hat (fp32 workspace), dV */
+#define MMDIT_STAGE_BWD_PROLOGUE  4u  /* bwd: inverse RoPE + RMSNorm backward -> dq, dk, dgains */
+
+typedef struct {
+  const void *q, *k, *v;              /* [N][H][d] device, dtype; pre-norm */
+  int64_t q_stride, k_stride, v_stride;
+  const float *gains;                 /* [4][d] fp32 device: q_text, q_image, k_text, k_image */
+  void *o;                            /* [N][H][d] dtype, dense */
+  float *lse;                         /* [H][N] fp32 natural-log logsumexp; may be NULL */
+  void *q_hat, *k_hat;                /* [N][H][d] dtype, dense; kept for the backward.
+                                         Both NULL: use the workspace (inference). */
+  float *rstd;                        /* [2][N][H] fp32 (Q then K) or NULL */
+  uint32_t stages;                    /* 0 = all */
+} mmdit_fwd_args;
+
+/* Forward: o = per-sample softmax(q_hat k_hat^T / sqrt(d)) v with q_hat, k_hat
+ * the normalised and rotated q, k. workspace may be NULL when q_hat and k_hat
+ * are given; else workspace_bytes >= plan->fwd_workspace_bytes. hip_stream is
+ * a hipStream_t (NULL = the default stream). Deterministic: the same inputs
+ * give bitwise the same outputs. */
+mmdit_status mmdit_attn_fwd(const mmdit_plan *plan, const void *plan_blob_dev,
+                            const mmdit_fwd_args *args, void *workspace,
+                            uint64_t workspace_bytes, void *hip_stream);
+
+typedef struct {
+  const void *q, *k, *v;              /* pre-norm inputs of the forward, with strides */
+  const void *q_hat, *k_hat, *o;      /* dense [N][H][d], as written by the forward */
+  const void *dout;                   /* [N][H][d] dtype, stride dout_stride */
+  int64_t q_stride, k_stride, v_stride, dout_stride;
+  const float *gains;                 /* [4][d] fp32 */
+  const float *lse;                   /* [H][N] fp32 from the forward (required) */
+  const float *rstd;                  /* [2][N][H] from the forward, or NULL = recompute */
+  void *dq, *dk, *dv;                 /* [N][H][d] dtype, dense: gradients w.r.t. pre-norm q, k, v */
+  float *dgains;                      /* [4][d] fp32, overwritten; NULL = skip */
+  uint32_t stages;                    /* 0 = all */
+} mmdit_bwd_args;
+
+/* Backward of mmdit_attn_fwd for the loss sum(dout * o). workspace_bytes >=
+ * plan->bwd_workspace_bytes. Workspace layout after the call (fp32): dQ-hat
+ * [N][H][d] at offset 0, dK-hat [N][H][d] right after it, then D [H][N].
+ * dq (and so dgains) may differ in the last bits from run to run: dQ-hat is
+ * accumulated with fp32 atomics. */
+mmdit_status mmdit_attn_bwd(const mmdit_plan *plan, const void *plan_blob_dev,
+                            const mmdit_bwd_args *args, void *workspace,
+                            uint64_t workspace_bytes, void *hip_stream);
+
+const char *mmdit_status_str(mmdit_status s);
+const char *mmdit_last_error(void);   /* detail of this thread's last non-OK return */
+int32_t mmdit_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MMDIT_H */

@@ -1,0 +1,275 @@
+"""Python binding of libmmdit (packed native-resolution joint attention on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libmmdit.so; torch provides device memory and the HIP stream. The
+three C entry points keep their names here (``mmdit_pack_plan``,
+``mmdit_attn_fwd``, ``mmdit_attn_bwd``); ``Pack``, ``forward`` and ``backward``
+are small conveniences that allocate outputs with torch and call them.
+
+Importing this module does not need a GPU. Loading the library fails loudly
+(ImportError) when libmmdit.so has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "MmditError", "lib", "mmdit_pack_plan", "mmdit_attn_fwd", "mmdit_attn_bwd",
+    "mmdit_status_str", "mmdit_last_error", "mmdit_abi_version", "Pack",
+    "forward", "backward", "FWD_STAGES", "BWD_STAGES", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmmdit.so")
+
+MMDIT_F32, MMDIT_BF16 = 0, 1
+STAGE_PROLOGUE, STAGE_ATTENTION = 1, 2
+STAGE_BWD_PRE, STAGE_BWD_ATTENTION, STAGE_BWD_PROLOGUE = 1, 2, 4
+FWD_STAGES = {"prologue": STAGE_PROLOGUE, "attention": STAGE_ATTENTION}
+BWD_STAGES = {"pre": STAGE_BWD_PRE, "attention": STAGE_BWD_ATTENTION, "prologue": STAGE_BWD_PROLOGUE}
+
+
+class PackDesc(C.Structure):
+    _fields_ = [("num_samples", C.c_int32), ("text_len", C.POINTER(C.c_int32)),
+                ("grid_h", C.POINTER(C.c_int32)), ("grid_w", C.POINTER(C.c_int32)),
+                ("num_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32),
+                ("rope_theta", C.c_float), ("rms_eps", C.c_float), ("token_budget", C.c_int64)]
+
+
+class Plan(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "num_samples", "total_tokens", "max_seqlen", "num_heads", "head_dim", "dtype",
+        "q_tile", "kv_tile", "num_fwd_items", "num_bwd_items", "rope_rows", "reserved")] + [
+        ("rope_theta", C.c_float), ("rms_eps", C.c_float)] + [(n, C.c_uint64) for n in (
+        "blob_bytes", "off_cu_seqlens", "off_tok_meta", "off_fwd_items", "off_bwd_items",
+        "off_rope", "fwd_workspace_bytes", "bwd_workspace_bytes", "fingerprint")]
+
+
+class FwdArgs(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
+                ("q_stride", C.c_int64), ("k_stride", C.c_int64), ("v_stride", C.c_int64),
+                ("gains", C.c_void_p), ("o", C.c_void_p), ("lse", C.c_void_p),
+                ("q_hat", C.c_void_p), ("k_hat", C.c_void_p), ("rstd", C.c_void_p),
+                ("stages", C.c_uint32)]
+
+
+class BwdArgs(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
+                ("q_hat", C.c_void_p), ("k_hat", C.c_void_p), ("o", C.c_void_p),
+                ("dout", C.c_void_p),
+                ("q_stride", C.c_int64), ("k_stride", C.c_int64), ("v_stride", C.c_int64),
+                ("dout_stride", C.c_int64),
+                ("gains", C.c_void_p), ("lse", C.c_void_p), ("rstd", C.c_void_p),
+                ("dq", C.c_void_p), ("dk", C.c_void_p), ("dv", C.c_void_p),
+                ("dgains", C.c_void_p), ("stages", C.c_uint32)]
+
+
+class MmditError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{mmdit_status_str(status)} ({status}): {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libmmdit.so (once). Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m packed_attention_nr_amd.build` (hipcc, gfx950)")
+        # torch's bundled HIP runtime has the same soname as ROCm's: loading
+        # torch first makes libmmdit bind to that one runtime instead of
+        # bringing a second one into the process.
+        import torch  # noqa: F401
+        L = C.CDLL(LIB_PATH)
+        L.mmdit_pack_plan.restype = C.c_int
+        L.mmdit_pack_plan.argtypes = [C.POINTER(PackDesc), C.POINTER(Plan), C.c_void_p, C.c_uint64]
+        L.mmdit_attn_fwd.restype = C.c_int
+        L.mmdit_attn_fwd.argtypes = [C.POINTER(Plan), C.c_void_p, C.POINTER(FwdArgs), C.c_void_p,
+                                     C.c_uint64, C.c_void_p]
+        L.mmdit_attn_bwd.restype = C.c_int
+        L.mmdit_attn_bwd.argtypes = [C.POINTER(Plan), C.c_void_p, C.POINTER(BwdArgs), C.c_void_p,
+                                     C.c_uint64, C.c_void_p]
+        L.mmdit_status_str.restype = C.c_char_p
+        L.mmdit_status_str.argtypes = [C.c_int]
+        L.mmdit_last_error.restype = C.c_char_p
+        L.mmdit_last_error.argtypes = []
+        L.mmdit_abi_version.restype = C.c_int32
+        L.mmdit_abi_version.argtypes = []
+        if L.mmdit_abi_version() != 1:
+            raise ImportError("libmmdit ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def mmdit_status_str(status: int) -> str:
+    return lib().mmdit_status_str(status).decode()
+
+
+def mmdit_last_error() -> str:
+    return lib().mmdit_last_error().decode()
+
+
+def mmdit_abi_version() -> int:
+    return int(lib().mmdit_abi_version())
+
+
+def _check(status: int):
+    if status != 0:
+        raise MmditError(status, mmdit_last_error())
+
+
+def mmdit_pack_plan(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int],
+                    num_heads: int, head_dim: int, dtype: int, rope_theta: float = 10000.0,
+                    rms_eps: float = 1e-6, token_budget: int = 0):
+    """Run mmdit_pack_plan. Returns (plan, blob) with blob a uint8 numpy array
+    holding the host copy of the plan blob."""
+    t = np.ascontiguousarray(text_len, dtype=np.int32)
+    h = np.ascontiguousarray(grid_h, dtype=np.int32)
+    w = np.ascontiguousarray(grid_w, dtype=np.int32)
+    if not (len(t) == len(h) == len(w)):
+        raise ValueError("text_len, grid_h and grid_w must have the same length")
+    P = C.POINTER(C.c_int32)
+    desc = PackDesc(len(t), t.ctypes.data_as(P), h.ctypes.data_as(P), w.ctypes.data_as(P),
+                    int(num_heads), int(head_dim), int(dtype), float(rope_theta), float(rms_eps),
+                    int(token_budget))
+    plan = Plan()
+    _check(lib().mmdit_pack_plan(C.byref(desc), C.byref(plan), None, 0))
+    blob = np.zeros(plan.blob_bytes, dtype=np.uint8)
+    _check(lib().mmdit_pack_plan(C.byref(desc), C.byref(plan), blob.ctypes.data, blob.nbytes))
+    return plan, blob
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def mmdit_attn_fwd(plan: Plan, blob_dev, *, q=None, k=None, v=None, q_stride=0, k_stride=0,
+                   v_stride=0, gains=None, o=None, lse=None, q_hat=None, k_hat=None, rstd=None,
+                   workspace=None, stages: int = 0, stream=None):
+    """Run mmdit_attn_fwd with torch tensors (device pointers taken from them)."""
+    a = FwdArgs(_ptr(q), _ptr(k), _ptr(v), int(q_stride), int(k_stride), int(v_stride),
+                _ptr(gains), _ptr(o), _ptr(lse), _ptr(q_hat), _ptr(k_hat), _ptr(rstd), int(stages))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mmdit_attn_fwd(C.byref(plan), _ptr(blob_dev), C.byref(a), _ptr(workspace),
+                                ws_bytes, _stream(stream)))
+
+
+def mmdit_attn_bwd(plan: Plan, blob_dev, *, q=None, k=None, v=None, q_hat=None, k_hat=None,
+                   o=None, dout=None, q_stride=0, k_stride=0, v_stride=0, dout_stride=0,
+                   gains=None, lse=None, rstd=None, dq=None, dk=None, dv=None, dgains=None,
+                   workspace=None, stages: int = 0, stream=None):
+    """Run mmdit_attn_bwd with torch tensors (device pointers taken from them)."""
+    a = BwdArgs(_ptr(q), _ptr(k), _ptr(v), _ptr(q_hat), _ptr(k_hat), _ptr(o), _ptr(dout),
+                int(q_stride), int(k_stride), int(v_stride), int(dout_stride), _ptr(gains),
+                _ptr(lse), _ptr(rstd), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgains), int(stages))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mmdit_attn_bwd(C.byref(plan), _ptr(blob_dev), C.byref(a), _ptr(workspace),
+                                ws_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Conveniences: a pack with its device blob; forward / backward with torch-
+# allocated outputs.
+# ---------------------------------------------------------------------------
+def _torch_dtype(dtype: int):
+    import torch
+    return torch.bfloat16 if dtype == MMDIT_BF16 else torch.float32
+
+
+def _token_stride(t, N, H, d, name):
+    if t.dim() != 3 or tuple(t.shape) != (N, H, d):
+        raise ValueError(f"{name} must have shape ({N}, {H}, {d}), got {tuple(t.shape)}")
+    if t.stride(2) != 1 or t.stride(1) != d:
+        raise ValueError(f"{name}: heads and head_dim must be contiguous")
+    return t.stride(0)
+
+
+class Pack:
+    """Plan of one pack plus its device blob (copied once)."""
+
+    def __init__(self, text_len, grid_h, grid_w, num_heads, head_dim, dtype="bf16",
+                 rope_theta=10000.0, rms_eps=1e-6, token_budget=0, device="cuda"):
+        import torch
+        self.dtype_code = MMDIT_BF16 if dtype in ("bf16", MMDIT_BF16) else MMDIT_F32
+        self.plan, self.blob = mmdit_pack_plan(text_len, grid_h, grid_w, num_heads, head_dim,
+                                               self.dtype_code, rope_theta, rms_eps, token_budget)
+        self.blob_dev = torch.from_numpy(self.blob).to(device)
+        self.N = self.plan.total_tokens
+        self.H = self.plan.num_heads
+        self.d = self.plan.head_dim
+        self.device = device
+        self.torch_dtype = _torch_dtype(self.dtype_code)
+
+    def workspace(self, kind: str):
+        import torch
+        n = self.plan.fwd_workspace_bytes if kind == "fwd" else self.plan.bwd_workspace_bytes
+        return torch.empty(max(int(n), 16), dtype=torch.uint8, device=self.device)
+
+
+def forward(pack: Pack, q, k, v, gains, *, save_for_backward: bool = True, stream=None):
+    """O (and lse, q_hat, k_hat, rstd when saving for the backward)."""
+    import torch
+    N, H, d = pack.N, pack.H, pack.d
+    qs = _token_stride(q, N, H, d, "q")
+    ks = _token_stride(k, N, H, d, "k")
+    vs = _token_stride(v, N, H, d, "v")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != pack.torch_dtype:
+            raise TypeError(f"{n} must be {pack.torch_dtype}")
+    if gains.dtype != torch.float32 or tuple(gains.shape) != (4, d) or not gains.is_contiguous():
+        raise TypeError("gains must be a contiguous float32 tensor of shape (4, d)")
+    dev = q.device
+    o = torch.empty((N, H, d), dtype=pack.torch_dtype, device=dev)
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev)
+    out = dict(o=o, lse=lse)
+    if save_for_backward:
+        q_hat = torch.empty_like(o)
+        k_hat = torch.empty_like(o)
+        rstd = torch.empty((2, N, H), dtype=torch.float32, device=dev)
+        mmdit_attn_fwd(pack.plan, pack.blob_dev, q=q, k=k, v=v, q_stride=qs, k_stride=ks,
+                       v_stride=vs, gains=gains, o=o, lse=lse, q_hat=q_hat, k_hat=k_hat,
+                       rstd=rstd, stream=stream)
+        out.update(q_hat=q_hat, k_hat=k_hat, rstd=rstd)
+    else:
+        ws = pack.workspace("fwd")
+        mmdit_attn_fwd(pack.plan, pack.blob_dev, q=q, k=k, v=v, q_stride=qs, k_stride=ks,
+                       v_stride=vs, gains=gains, o=o, lse=lse, workspace=ws, stream=stream)
+    return out
+
+
+def backward(pack: Pack, q, k, v, gains, saved: dict, dout, *, workspace=None, stream=None):
+    """dq, dk, dv (w.r.t. the pre-norm inputs) and dgains for loss sum(dout * o)."""
+    import torch
+    N, H, d = pack.N, pack.H, pack.d
+    qs = _token_stride(q, N, H, d, "q")
+    ks = _token_stride(k, N, H, d, "k")
+    vs = _token_stride(v, N, H, d, "v")
+    gs = _token_stride(dout, N, H, d, "dout")
+    if dout.dtype != pack.torch_dtype:
+        raise TypeError(f"dout must be {pack.torch_dtype}")
+    dev = q.device
+    dq = torch.empty((N, H, d), dtype=pack.torch_dtype, device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    dgains = torch.empty((4, d), dtype=torch.float32, device=dev)
+    ws = pack.workspace("bwd") if workspace is None else workspace
+    mmdit_attn_bwd(pack.plan, pack.blob_dev, q=q, k=k, v=v, q_hat=saved["q_hat"],
+                   k_hat=saved["k_hat"], o=saved["o"], dout=dout, q_stride=qs, k_stride=ks,
+                   v_stride=vs, dout_stride=gs, gains=gains, lse=saved["lse"],
+                   rstd=saved.get("rstd"), dq=dq, dk=dk, dv=dv, dgains=dgains, workspace=ws,
+                   stream=stream)
+    return dict(dq=dq, dk=dk, dv=dv, dgains=dgains, workspace=ws)

@@ -1,0 +1,315 @@
+// C ABI entry points: host-side validation of every argument, then kernel
+// launches on the caller's stream. Nothing is launched unless every check
+// passes; no device memory is allocated, freed or synchronised here.
+#include <cmath>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace mmdit {
+
+static thread_local std::string g_last_error;
+
+mmdit_status fail(mmdit_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte range [lo, hi) touched by a tensor of n rows with `stride` elements
+// between rows and `row` elements per row.
+struct Span {
+  const char *name;
+  uintptr_t lo, hi;
+  bool written;
+};
+
+static Span span(const char *name, const void *p, int64_t n, int64_t stride, int64_t row, int elt,
+                 bool written) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  const uintptr_t bytes = (uintptr_t)(((n - 1) * stride + row) * elt);
+  return Span{name, lo, lo + bytes, written};
+}
+
+// Every written buffer must be disjoint from every other buffer of the call.
+static mmdit_status check_aliasing(const std::vector<Span> &spans) {
+  for (size_t i = 0; i < spans.size(); ++i) {
+    if (!spans[i].written) continue;
+    for (size_t j = 0; j < spans.size(); ++j) {
+      if (i == j) continue;
+      if (spans[i].lo < spans[j].hi && spans[j].lo < spans[i].hi)
+        return fail(MMDIT_ERR_INVALID_ARG, "output %s overlaps %s", spans[i].name, spans[j].name);
+    }
+  }
+  return MMDIT_OK;
+}
+
+static mmdit_status check_plan(const mmdit_plan *plan, const void *blob) {
+  if (!plan) return fail(MMDIT_ERR_INVALID_ARG, "plan must not be NULL");
+  if (plan_fingerprint(*plan) != plan->fingerprint)
+    return fail(MMDIT_ERR_INVALID_ARG, "plan fingerprint mismatch: not made by mmdit_pack_plan, or modified");
+  if (!blob || !aligned16(blob))
+    return fail(MMDIT_ERR_INVALID_ARG, "plan_blob_dev must be a non-NULL 16-byte aligned device pointer");
+  return MMDIT_OK;
+}
+
+static mmdit_status check_tensor(const char *name, const void *p, int64_t stride, int64_t hd) {
+  if (!p) return fail(MMDIT_ERR_INVALID_ARG, "%s must not be NULL", name);
+  if (!aligned16(p)) return fail(MMDIT_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  if (stride < hd || stride % 8 != 0)
+    return fail(MMDIT_ERR_INVALID_ARG, "%s stride %lld must be >= H*d (%lld) and a multiple of 8", name,
+                (long long)stride, (long long)hd);
+  return MMDIT_OK;
+}
+
+static mmdit_status check_ptr(const char *name, const void *p) {
+  if (!p) return fail(MMDIT_ERR_INVALID_ARG, "%s must not be NULL", name);
+  if (!aligned16(p)) return fail(MMDIT_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  return MMDIT_OK;
+}
+
+static PlanDev plan_dev(const mmdit_plan &p, const void *blob) {
+  const char *b = static_cast<const char *>(blob);
+  PlanDev d;
+  d.cu_seqlens = reinterpret_cast<const int32_t *>(b + p.off_cu_seqlens);
+  d.tok_meta = reinterpret_cast<const int32_t *>(b + p.off_tok_meta);
+  d.fwd_items = reinterpret_cast<const int4 *>(b + p.off_fwd_items);
+  d.bwd_items = reinterpret_cast<const int4 *>(b + p.off_bwd_items);
+  d.rope = reinterpret_cast<const float2 *>(b + p.off_rope);
+  d.num_samples = p.num_samples;
+  d.total_tokens = p.total_tokens;
+  d.num_heads = p.num_heads;
+  d.head_dim = p.head_dim;
+  d.num_fwd_items = p.num_fwd_items;
+  d.num_bwd_items = p.num_bwd_items;
+  d.rope_rows = p.rope_rows;
+  d.rms_eps = p.rms_eps;
+  return d;
+}
+
+static uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
+
+static mmdit_status hip_fail(const char *what, hipError_t e) {
+  return fail(MMDIT_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+}
+
+static mmdit_status attn_fwd(const mmdit_plan *plan, const void *blob, const mmdit_fwd_args *a,
+                             void *ws, uint64_t ws_bytes, void *stream) {
+  mmdit_status st = check_plan(plan, blob);
+  if (st) return st;
+  if (!a) return fail(MMDIT_ERR_INVALID_ARG, "args must not be NULL");
+  const uint32_t all = MMDIT_STAGE_PROLOGUE | MMDIT_STAGE_ATTENTION;
+  const uint32_t stages = a->stages ? a->stages : all;
+  if (stages & ~all) return fail(MMDIT_ERR_INVALID_ARG, "unknown forward stage bits 0x%x", stages);
+  const bool pro = stages & MMDIT_STAGE_PROLOGUE, att = stages & MMDIT_STAGE_ATTENTION;
+  const int64_t N = plan->total_tokens, H = plan->num_heads, d = plan->head_dim, HD = H * d;
+  const int elt = plan->dtype == MMDIT_BF16 ? 2 : 4;
+
+  void *qh = a->q_hat, *kh = a->k_hat;
+  if ((qh == nullptr) != (kh == nullptr))
+    return fail(MMDIT_ERR_INVALID_ARG, "q_hat and k_hat must both be given or both be NULL");
+  std::vector<Span> spans;
+  if (!qh) {
+    if (!(pro && att))
+      return fail(MMDIT_ERR_INVALID_ARG, "running one forward stage alone needs caller-owned q_hat and k_hat");
+    if (!ws || !aligned16(ws))
+      return fail(MMDIT_ERR_INVALID_ARG, "workspace must be a non-NULL 16-byte aligned device pointer");
+    if (ws_bytes < plan->fwd_workspace_bytes)
+      return fail(MMDIT_ERR_BUFFER_TOO_SMALL, "forward workspace needs %llu bytes, got %llu",
+                  (unsigned long long)plan->fwd_workspace_bytes, (unsigned long long)ws_bytes);
+    qh = ws;
+    kh = static_cast<char *>(ws) + align256((uint64_t)N * HD * elt);
+  } else {
+    if ((st = check_ptr("q_hat", qh)) || (st = check_ptr("k_hat", kh))) return st;
+  }
+  spans.push_back(span("q_hat", qh, N, HD, HD, elt, pro));
+  spans.push_back(span("k_hat", kh, N, HD, HD, elt, pro));
+  if (pro) {
+    if ((st = check_tensor("q", a->q, a->q_stride, HD)) || (st = check_tensor("k", a->k, a->k_stride, HD)) ||
+        (st = check_ptr("gains", a->gains)))
+      return st;
+    spans.push_back(span("q", a->q, N, a->q_stride, HD, elt, false));
+    spans.push_back(span("k", a->k, N, a->k_stride, HD, elt, false));
+    spans.push_back(span("gains", a->gains, 4, d, d, 4, false));
+    if (a->rstd) {
+      if ((st = check_ptr("rstd", a->rstd))) return st;
+      spans.push_back(span("rstd", a->rstd, 2 * N, H, H, 4, true));
+    }
+  }
+  if (att) {
+    if ((st = check_tensor("v", a->v, a->v_stride, HD)) || (st = check_ptr("o", a->o))) return st;
+    spans.push_back(span("v", a->v, N, a->v_stride, HD, elt, false));
+    spans.push_back(span("o", a->o, N, HD, HD, elt, true));
+    if (a->lse) {
+      if ((st = check_ptr("lse", a->lse))) return st;
+      spans.push_back(span("lse", a->lse, H, N, N, 4, true));
+    }
+  }
+  if ((st = check_aliasing(spans))) return st;
+
+  const PlanDev pd = plan_dev(*plan, blob);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pro) {
+    PrologueFwdArgs pa{a->q, a->k, a->q_stride, a->k_stride, a->gains, qh, kh, a->rstd};
+    hipError_t e = launch_prologue_fwd(plan->dtype, pd, pa, s);
+    if (e != hipSuccess) return hip_fail("prologue", e);
+  }
+  if (att) {
+    AttnFwdArgs fa{qh, kh, a->v, a->v_stride, a->o, a->lse,
+                   (float)(1.4426950408889634 / std::sqrt((double)d))};
+    hipError_t e = launch_attn_fwd(plan->dtype, pd, fa, s);
+    if (e != hipSuccess) return hip_fail("attention forward", e);
+  }
+  return MMDIT_OK;
+}
+
+static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmdit_bwd_args *a,
+                             void *ws, uint64_t ws_bytes, void *stream) {
+  mmdit_status st = check_plan(plan, blob);
+  if (st) return st;
+  if (!a) return fail(MMDIT_ERR_INVALID_ARG, "args must not be NULL");
+  const uint32_t all = MMDIT_STAGE_BWD_PRE | MMDIT_STAGE_BWD_ATTENTION | MMDIT_STAGE_BWD_PROLOGUE;
+  const uint32_t stages = a->stages ? a->stages : all;
+  if (stages & ~all) return fail(MMDIT_ERR_INVALID_ARG, "unknown backward stage bits 0x%x", stages);
+  const bool pre = stages & MMDIT_STAGE_BWD_PRE, att = stages & MMDIT_STAGE_BWD_ATTENTION,
+             pro = stages & MMDIT_STAGE_BWD_PROLOGUE;
+  const int64_t N = plan->total_tokens, H = plan->num_heads, d = plan->head_dim, HD = H * d;
+  const int elt = plan->dtype == MMDIT_BF16 ? 2 : 4;
+  if (!ws || !aligned16(ws))
+    return fail(MMDIT_ERR_INVALID_ARG, "workspace must be a non-NULL 16-byte aligned device pointer");
+  if (ws_bytes < plan->bwd_workspace_bytes)
+    return fail(MMDIT_ERR_BUFFER_TOO_SMALL, "backward workspace needs %llu bytes, got %llu",
+                (unsigned long long)plan->bwd_workspace_bytes, (unsigned long long)ws_bytes);
+  char *w = static_cast<char *>(ws);
+  float *dq_acc = reinterpret_cast<float *>(w);
+  float *dk_acc = reinterpret_cast<float *>(w + align256((uint64_t)N * HD * 4));
+  float *delta = reinterpret_cast<float *>(w + 2 * align256((uint64_t)N * HD * 4));
+  float *partials = reinterpret_cast<float *>(w + 2 * align256((uint64_t)N * HD * 4) + align256(4ull * H * N));
+  const int nblocks = (int)bwd_partial_blocks(N);
+
+  std::vector<Span> spans;
+  spans.push_back(Span{"workspace", reinterpret_cast<uintptr_t>(ws),
+                       reinterpret_cast<uintptr_t>(ws) + plan->bwd_workspace_bytes, true});
+  if (pre) {
+    if ((st = check_ptr("o", a->o)) || (st = check_tensor("dout", a->dout, a->dout_stride, HD))) return st;
+  }
+  if (pre) spans.push_back(span("o", a->o, N, HD, HD, elt, false));
+  if (pre || att) {
+    if ((st = check_tensor("dout", a->dout, a->dout_stride, HD))) return st;
+    spans.push_back(span("dout", a->dout, N, a->dout_stride, HD, elt, false));
+  }
+  if (att) {
+    if ((st = check_ptr("q_hat", a->q_hat)) || (st = check_ptr("k_hat", a->k_hat)) ||
+        (st = check_tensor("v", a->v, a->v_stride, HD)) || (st = check_ptr("lse", a->lse)) ||
+        (st = check_ptr("dv", a->dv)))
+      return st;
+    spans.push_back(span("q_hat", a->q_hat, N, HD, HD, elt, false));
+    spans.push_back(span("k_hat", a->k_hat, N, HD, HD, elt, false));
+    spans.push_back(span("v", a->v, N, a->v_stride, HD, elt, false));
+    spans.push_back(span("lse", a->lse, H, N, N, 4, false));
+    spans.push_back(span("dv", a->dv, N, HD, HD, elt, true));
+  }
+  if (pro) {
+    if ((st = check_tensor("q", a->q, a->q_stride, HD)) || (st = check_tensor("k", a->k, a->k_stride, HD)) ||
+        (st = check_ptr("gains", a->gains)) || (st = check_ptr("dq", a->dq)) || (st = check_ptr("dk", a->dk)))
+      return st;
+    spans.push_back(span("q", a->q, N, a->q_stride, HD, elt, false));
+    spans.push_back(span("k", a->k, N, a->k_stride, HD, elt, false));
+    spans.push_back(span("gains", a->gains, 4, d, d, 4, false));
+    spans.push_back(span("dq", a->dq, N, HD, HD, elt, true));
+    spans.push_back(span("dk", a->dk, N, HD, HD, elt, true));
+    if (a->rstd) {
+      if ((st = check_ptr("rstd", a->rstd))) return st;
+      spans.push_back(span("rstd", a->rstd, 2 * N, H, H, 4, false));
+    }
+    if (a->dgains) {
+      if ((st = check_ptr("dgains", a->dgains))) return st;
+      spans.push_back(span("dgains", a->dgains, 4, d, d, 4, true));
+    }
+  }
+  if ((st = check_aliasing(spans))) return st;
+
+  const PlanDev pd = plan_dev(*plan, blob);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale = (float)(1.0 / std::sqrt((double)d));
+  if (pre) {
+    BwdPreArgs ba{a->o, a->dout, a->dout_stride, delta, dq_acc};
+    hipError_t e = launch_bwd_pre(plan->dtype, pd, ba, s);
+    if (e != hipSuccess) return hip_fail("backward preprocess", e);
+  }
+  if (att) {
+    AttnBwdArgs ba{a->q_hat, a->k_hat, a->v, a->dout, a->v_stride, a->dout_stride, a->lse, delta,
+                   dq_acc, dk_acc, a->dv, (float)(1.4426950408889634 / std::sqrt((double)d)), scale};
+    hipError_t e = launch_attn_bwd(plan->dtype, pd, ba, s);
+    if (e != hipSuccess) return hip_fail("attention backward", e);
+  }
+  if (pro) {
+    PrologueBwdArgs pa{a->q, a->k, a->q_stride, a->k_stride, a->gains, a->rstd, dq_acc, dk_acc,
+                       a->dq, a->dk, partials, a->dgains, nblocks};
+    hipError_t e = launch_prologue_bwd(plan->dtype, pd, pa, s);
+    if (e != hipSuccess) return hip_fail("prologue backward", e);
+  }
+  return MMDIT_OK;
+}
+
+}  // namespace mmdit
+
+extern "C" {
+
+mmdit_status mmdit_pack_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *host_blob,
+                             uint64_t host_blob_bytes) {
+  mmdit::clear_error();
+  try {
+    return mmdit::build_plan(desc, plan, host_blob, host_blob_bytes);
+  } catch (...) {
+    return mmdit::fail(MMDIT_ERR_INVALID_ARG, "pack plan failed (out of host memory?)");
+  }
+}
+
+mmdit_status mmdit_attn_fwd(const mmdit_plan *plan, const void *plan_blob_dev, const mmdit_fwd_args *args,
+                            void *workspace, uint64_t workspace_bytes, void *hip_stream) {
+  mmdit::clear_error();
+  try {
+    return mmdit::attn_fwd(plan, plan_blob_dev, args, workspace, workspace_bytes, hip_stream);
+  } catch (...) {
+    return mmdit::fail(MMDIT_ERR_INVALID_ARG, "forward failed on the host");
+  }
+}
+
+mmdit_status mmdit_attn_bwd(const mmdit_plan *plan, const void *plan_blob_dev, const mmdit_bwd_args *args,
+                            void *workspace, uint64_t workspace_bytes, void *hip_stream) {
+  mmdit::clear_error();
+  try {
+    return mmdit::attn_bwd(plan, plan_blob_dev, args, workspace, workspace_bytes, hip_stream);
+  } catch (...) {
+    return mmdit::fail(MMDIT_ERR_INVALID_ARG, "backward failed on the host");
+  }
+}
+
+const char *mmdit_status_str(mmdit_status s) {
+  switch (s) {
+    case MMDIT_OK: return "ok";
+    case MMDIT_ERR_INVALID_ARG: return "invalid argument";
+    case MMDIT_ERR_UNSUPPORTED: return "unsupported";
+    case MMDIT_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case MMDIT_ERR_BUDGET: return "token budget exceeded";
+    case MMDIT_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *mmdit_last_error(void) { return mmdit::g_last_error.c_str(); }
+
+int32_t mmdit_abi_version(void) { return MMDIT_ABI_VERSION; }
+
+}  // extern "C"

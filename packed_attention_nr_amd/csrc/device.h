@@ -1,0 +1,124 @@
+// Device helpers for the gfx950 kernels: vector types, bf16 packing, DPP
+// reductions inside a row of 16 lanes, MFMA and LDS transpose-read wrappers.
+//
+// Lane layouts relied on (checked on gfx950 hardware):
+//  * v_mfma_f32_32x32x16_bf16: A lane l holds row l%32 and eight k values
+//    selected by (l/32, j); B lane l holds column l%32 with the same k
+//    selection; accumulator register i of lane l is element
+//    (row 8*(i/4) + 4*(l/32) + i%4, column l%32).
+//  * ds_read_b64_tr_b16: in each group of 16 lanes, lane L fetches 4 bf16 at
+//    its own address (row L/4 and columns 4*(L%4)..+3 of a 4x16 block) and
+//    afterwards lane i holds column i of the block, rows 0..3.
+//  * v_permlane32_swap(x, x) returns (x of lane l%32, x of lane l%32 + 32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mmdit {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+
+// 16-byte global / LDS accesses.
+template <typename T>
+__device__ __forceinline__ uint4 ld16(const T *p) {
+  return *reinterpret_cast<const uint4 *>(p);
+}
+template <typename T>
+__device__ __forceinline__ void st16(T *p, uint4 v) {
+  *reinterpret_cast<uint4 *>(p) = v;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
+
+// fp32 -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16x2 pack2(float a, float b) {
+  bf16x2 r = {(bf16)a, (bf16)b};
+  return r;
+}
+
+// DPP move inside a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W lanes (W = 2..64); every lane of a group gets
+// the bitwise-same sum (each step adds two values symmetrically).
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(W >= 2 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  x += dpp<0xB1>(x);                      // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (W >= 16) x += dpp<0x140>(x); // row_mirror
+  if constexpr (W >= 32) x += __shfl_xor(x, 16);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// max/sum of x over lanes l and l^32 (the two halves of the wave).
+__device__ __forceinline__ float half_max(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed read of a 16(k) x 32(n) bf16 operand fragment from a row-major
+// LDS matrix M[k][n] (row stride `ld` elements): returns, for lane l, the
+// values M[k0 + kappa(l/32, j)][n0 + l%32], j = 0..7, where
+// kappa(g, j) = 8*(j/4) + 4*g + j%4 -- the k order in which a 32x32
+// accumulator holds its rows, so an accumulator converted to bf16 can be the
+// other operand of the same product.
+__device__ __forceinline__ bf16x8 lds_read_tr(const bf16 *m, int ld, int k0, int n0, int lane) {
+  const int G = lane >> 4, i = lane & 15;
+  const int g = G >> 1, nh = G & 1;
+  const bf16 *p = m + (k0 + 4 * g + (i >> 2)) * ld + n0 + nh * 16 + 4 * (i & 3);
+  bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+  bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + 8 * ld));
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Row of the 32x32 accumulator held in register i by lanes of half g.
+__device__ __forceinline__ constexpr int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+// Eight accumulator registers (starting at `base`) packed to bf16: the k
+// fragment kappa(g, 0..7) of a 16-wide slice of the accumulator's rows.
+__device__ __forceinline__ bf16x8 acc_to_bf16(const f32x16 &c, int base) {
+  bf16x8 r;
+  bf16x2 t0 = pack2(c[base + 0], c[base + 1]);
+  bf16x2 t1 = pack2(c[base + 2], c[base + 3]);
+  bf16x2 t2 = pack2(c[base + 4], c[base + 5]);
+  bf16x2 t3 = pack2(c[base + 6], c[base + 7]);
+  r[0] = t0[0]; r[1] = t0[1]; r[2] = t1[0]; r[3] = t1[1];
+  r[4] = t2[0]; r[5] = t2[1]; r[6] = t3[0]; r[7] = t3[1];
+  return r;
+}
+
+__device__ __forceinline__ void tok_pos(int32_t meta, bool &img, int &row, int &col) {
+  img = meta < 0;
+  row = (meta >> 16) & 0x7FFF;
+  col = meta & 0xFFFF;
+}
+
+}  // namespace mmdit

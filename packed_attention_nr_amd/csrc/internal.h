@@ -1,0 +1,117 @@
+// Internal declarations shared by the host code and the HIP kernels of the
+// packed joint-attention library. Not part of the C ABI (include/mmdit.h).
+#pragma once
+
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/mmdit.h"
+
+namespace mmdit {
+
+// Rows of one forward query tile / one backward key tile (work-list granularity).
+constexpr int kFwdTile = 128;
+constexpr int kBwdTile = 128;
+// Limits checked by the plan.
+constexpr int kMaxGridSide = 32768;             // row and col fit in 15 bits of tok_meta
+constexpr int64_t kMaxTokens = 1ll << 30;
+constexpr int64_t kMaxElements = 1ll << 40;     // N*H*d
+// Prologue backward: tokens per block and the cap on blocks (= gain partials).
+constexpr int kPbwdTokensPerBlock = 64;
+constexpr int kPbwdMaxBlocks = 1024;
+
+constexpr uint32_t kBlobMagic = 0x50444D4Du;    // "MMDP"
+constexpr uint64_t kBlobHeaderBytes = 64;
+
+struct BlobHeader {
+  uint32_t magic;
+  int32_t version;
+  int32_t num_samples;
+  int32_t total_tokens;
+  uint64_t fingerprint;
+  uint8_t pad[40];
+};
+static_assert(sizeof(BlobHeader) == kBlobHeaderBytes, "blob header size");
+
+// Error reporting (thread-local message; see mmdit_last_error).
+mmdit_status fail(mmdit_status s, const char *fmt, ...);
+void clear_error();
+
+uint64_t plan_fingerprint(const mmdit_plan &p);
+mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *host_blob,
+                        uint64_t host_blob_bytes);
+uint64_t bwd_partial_blocks(int64_t n_tokens);
+
+// ---------------------------------------------------------------------------
+// Kernel launch arguments (device pointers; plain data passed by value).
+// ---------------------------------------------------------------------------
+struct PlanDev {
+  const int32_t *cu_seqlens;   // [S+1]
+  const int32_t *tok_meta;     // [N]
+  const int4 *fwd_items;       // [num_fwd_items]
+  const int4 *bwd_items;       // [num_bwd_items]
+  const float2 *rope;          // [rope_rows][d/4] (cos, sin)
+  int32_t num_samples, total_tokens, num_heads, head_dim;
+  int32_t num_fwd_items, num_bwd_items, rope_rows;
+  float rms_eps;
+};
+
+struct PrologueFwdArgs {
+  const void *q, *k;
+  int64_t q_stride, k_stride;
+  const float *gains;
+  void *q_hat, *k_hat;
+  float *rstd;                 // [2][N][H] or nullptr
+};
+
+struct AttnFwdArgs {
+  const void *q_hat, *k_hat, *v;
+  int64_t v_stride;
+  void *o;
+  float *lse;                  // [H][N] or nullptr
+  float scale_log2;            // log2(e) / sqrt(d)
+};
+
+struct BwdPreArgs {
+  const void *o, *dout;
+  int64_t dout_stride;
+  float *delta;                // [H][N]
+  float *dq_acc;               // [N][H][d] fp32, zeroed here
+};
+
+struct AttnBwdArgs {
+  const void *q_hat, *k_hat, *v, *dout;
+  int64_t v_stride, dout_stride;
+  const float *lse, *delta;    // [H][N]
+  float *dq_acc;               // [N][H][d] fp32, atomically accumulated (pre-scaled)
+  float *dk_acc;               // [N][H][d] fp32
+  void *dv;                    // [N][H][d] dtype
+  float scale_log2;            // log2(e) / sqrt(d)
+  float scale;                 // 1 / sqrt(d)
+};
+
+struct PrologueBwdArgs {
+  const void *q, *k;
+  int64_t q_stride, k_stride;
+  const float *gains;
+  const float *rstd;           // [2][N][H] or nullptr = recompute
+  const float *dq_hat, *dk_hat;
+  void *dq, *dk;
+  float *partials;             // [blocks][4][d]
+  float *dgains;               // [4][d] or nullptr
+  int32_t num_blocks;
+};
+
+// Launchers: enqueue on `stream`, return the launch status.
+hipError_t launch_prologue_fwd(int dtype, const PlanDev &p, const PrologueFwdArgs &a,
+                               hipStream_t stream);
+hipError_t launch_attn_fwd(int dtype, const PlanDev &p, const AttnFwdArgs &a, hipStream_t stream);
+hipError_t launch_bwd_pre(int dtype, const PlanDev &p, const BwdPreArgs &a, hipStream_t stream);
+hipError_t launch_attn_bwd(int dtype, const PlanDev &p, const AttnBwdArgs &a, hipStream_t stream);
+hipError_t launch_prologue_bwd(int dtype, const PlanDev &p, const PrologueBwdArgs &a,
+                               hipStream_t stream);
+
+}  // namespace mmdit

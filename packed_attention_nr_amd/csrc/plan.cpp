@@ -1,0 +1,203 @@
+// Host-side pack plan: cu_seqlens, per-token metadata, longest-first work
+// lists and the RoPE table, laid out in one blob for a single H2D copy.
+//
+// Packing follows the Mage-Flow pages: each sample's text tokens and its
+// flattened latent grid are concatenated into one contiguous batch with
+// per-sample cumulative offsets, under a fixed token budget (picx.dev summary,
+// section "Native-Resolution MMDiT (NR-MMDiT)", bullet "Native-resolution
+// packing"; findtube.ai transcript at [00:03:16] and [00:04:03]).
+// Work lists and their longest-first order are this library's own scheduling
+// choice (attention cost of a tile grows with its segment's length).
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "internal.h"
+
+namespace mmdit {
+
+uint64_t plan_fingerprint(const mmdit_plan &p) {
+  // FNV-1a over every byte of the plan before the fingerprint field.
+  const unsigned char *b = reinterpret_cast<const unsigned char *>(&p);
+  size_t n = offsetof(mmdit_plan, fingerprint);
+  uint64_t h = 1469598103934665603ull;
+  for (size_t i = 0; i < n; ++i) {
+    h ^= b[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+static uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+int fwd_tile(int dtype, int d) {
+  (void)dtype;
+  (void)d;
+  return kFwdTile;
+}
+int bwd_tile(int dtype, int d) {
+  (void)dtype;
+  (void)d;
+  return kBwdTile;
+}
+
+uint64_t bwd_partial_blocks(int64_t n_tokens) {
+  int64_t b = (n_tokens + kPbwdTokensPerBlock - 1) / kPbwdTokensPerBlock;
+  return (uint64_t)std::max<int64_t>(1, std::min<int64_t>(b, kPbwdMaxBlocks));
+}
+
+mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *host_blob,
+                        uint64_t host_blob_bytes) {
+  if (!desc || !plan) return fail(MMDIT_ERR_INVALID_ARG, "desc and plan must not be NULL");
+  const int S = desc->num_samples;
+  if (S < 1) return fail(MMDIT_ERR_INVALID_ARG, "num_samples must be >= 1");
+  if (!desc->text_len || !desc->grid_h || !desc->grid_w)
+    return fail(MMDIT_ERR_INVALID_ARG, "text_len, grid_h and grid_w must not be NULL");
+  if (desc->num_heads < 1) return fail(MMDIT_ERR_INVALID_ARG, "num_heads must be >= 1");
+  if (desc->dtype != MMDIT_F32 && desc->dtype != MMDIT_BF16)
+    return fail(MMDIT_ERR_INVALID_ARG, "dtype must be MMDIT_F32 or MMDIT_BF16");
+  if (desc->head_dim <= 0 || desc->head_dim % 4 != 0)
+    return fail(MMDIT_ERR_INVALID_ARG, "head_dim must be a positive multiple of 4");
+  if (desc->head_dim != 64 && desc->head_dim != 128)
+    return fail(MMDIT_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!(desc->rope_theta > 0.f) || !std::isfinite(desc->rope_theta))
+    return fail(MMDIT_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  if (!(desc->rms_eps >= 0.f) || !std::isfinite(desc->rms_eps))
+    return fail(MMDIT_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (desc->token_budget < 0) return fail(MMDIT_ERR_INVALID_ARG, "token_budget must be >= 0");
+
+  std::vector<int64_t> L(S);
+  int64_t N = 0, max_len = 0, max_side = 0;
+  for (int i = 0; i < S; ++i) {
+    const int32_t t = desc->text_len[i], h = desc->grid_h[i], w = desc->grid_w[i];
+    if (t < 0 || h < 0 || w < 0)
+      return fail(MMDIT_ERR_INVALID_ARG, "sample %d: negative text_len or grid size", i);
+    if ((h == 0) != (w == 0))
+      return fail(MMDIT_ERR_INVALID_ARG, "sample %d: grid_h and grid_w must both be 0 or both > 0", i);
+    if (h >= kMaxGridSide || w >= kMaxGridSide)
+      return fail(MMDIT_ERR_INVALID_ARG, "sample %d: grid side must be < %d", i, kMaxGridSide);
+    L[i] = (int64_t)t + (int64_t)h * (int64_t)w;
+    if (L[i] < 1) return fail(MMDIT_ERR_INVALID_ARG, "sample %d has no tokens", i);
+    N += L[i];
+    if (N > kMaxTokens) return fail(MMDIT_ERR_INVALID_ARG, "total tokens exceed %lld", (long long)kMaxTokens);
+    max_len = std::max(max_len, L[i]);
+    max_side = std::max<int64_t>(max_side, std::max(h, w));
+  }
+  if (desc->token_budget > 0 && N > desc->token_budget)
+    return fail(MMDIT_ERR_BUDGET, "pack has %lld tokens, budget is %lld", (long long)N,
+                (long long)desc->token_budget);
+  const int64_t H = desc->num_heads, d = desc->head_dim;
+  if (N * H * d > kMaxElements)
+    return fail(MMDIT_ERR_INVALID_ARG, "N*H*d exceeds %lld", (long long)kMaxElements);
+
+  const int qt = fwd_tile(desc->dtype, (int)d), kt = bwd_tile(desc->dtype, (int)d);
+  std::vector<int64_t> cu(S + 1, 0);
+  for (int i = 0; i < S; ++i) cu[i + 1] = cu[i] + L[i];
+
+  // Longest segment first; ties by sample, then by tile.
+  std::vector<int> order(S);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return L[a] > L[b]; });
+  auto count_items = [&](int tile) {
+    int64_t n = 0;
+    for (int i = 0; i < S; ++i) n += (L[i] + tile - 1) / tile;
+    return n;
+  };
+  const int64_t n_fwd = count_items(qt), n_bwd = count_items(kt);
+  const int rope_rows = (int)std::max<int64_t>(1, max_side);
+
+  mmdit_plan p;
+  std::memset(&p, 0, sizeof(p));
+  p.num_samples = S;
+  p.total_tokens = (int32_t)N;
+  p.max_seqlen = (int32_t)max_len;
+  p.num_heads = (int32_t)H;
+  p.head_dim = (int32_t)d;
+  p.dtype = desc->dtype;
+  p.q_tile = qt;
+  p.kv_tile = kt;
+  p.num_fwd_items = (int32_t)n_fwd;
+  p.num_bwd_items = (int32_t)n_bwd;
+  p.rope_rows = rope_rows;
+  p.rope_theta = desc->rope_theta;
+  p.rms_eps = desc->rms_eps;
+  uint64_t off = align_up(kBlobHeaderBytes, 256);
+  p.off_cu_seqlens = off;
+  off = align_up(off + 4ull * (S + 1), 256);
+  p.off_tok_meta = off;
+  off = align_up(off + 4ull * N, 256);
+  p.off_fwd_items = off;
+  off = align_up(off + 16ull * n_fwd, 256);
+  p.off_bwd_items = off;
+  off = align_up(off + 16ull * n_bwd, 256);
+  p.off_rope = off;
+  off = align_up(off + 8ull * rope_rows * (d / 4), 256);
+  p.blob_bytes = off;
+
+  const uint64_t elt = desc->dtype == MMDIT_BF16 ? 2 : 4;
+  const uint64_t nhd = (uint64_t)N * H * d;
+  p.fwd_workspace_bytes = 2 * align_up(nhd * elt, 256);
+  p.bwd_workspace_bytes = 2 * align_up(nhd * 4, 256) + align_up(4ull * H * N, 256) +
+                          align_up(bwd_partial_blocks(N) * 4ull * d * 4, 256);
+  p.fingerprint = plan_fingerprint(p);
+  *plan = p;
+
+  if (!host_blob) return MMDIT_OK;  // size query
+  if (host_blob_bytes < p.blob_bytes)
+    return fail(MMDIT_ERR_BUFFER_TOO_SMALL, "host blob needs %llu bytes, got %llu",
+                (unsigned long long)p.blob_bytes, (unsigned long long)host_blob_bytes);
+
+  unsigned char *blob = static_cast<unsigned char *>(host_blob);
+  std::memset(blob, 0, p.blob_bytes);
+  BlobHeader hdr;
+  std::memset(&hdr, 0, sizeof(hdr));
+  hdr.magic = kBlobMagic;
+  hdr.version = MMDIT_ABI_VERSION;
+  hdr.num_samples = S;
+  hdr.total_tokens = (int32_t)N;
+  hdr.fingerprint = p.fingerprint;
+  std::memcpy(blob, &hdr, sizeof(hdr));
+
+  int32_t *cu32 = reinterpret_cast<int32_t *>(blob + p.off_cu_seqlens);
+  for (int i = 0; i <= S; ++i) cu32[i] = (int32_t)cu[i];
+
+  int32_t *meta = reinterpret_cast<int32_t *>(blob + p.off_tok_meta);
+  for (int i = 0; i < S; ++i) {
+    const int64_t base = cu[i] + desc->text_len[i];
+    for (int64_t t = cu[i]; t < base; ++t) meta[t] = 0;
+    const int32_t h = desc->grid_h[i], w = desc->grid_w[i];
+    for (int32_t r = 0; r < h; ++r)
+      for (int32_t c = 0; c < w; ++c)
+        meta[base + (int64_t)r * w + c] = (int32_t)(0x80000000u | ((uint32_t)r << 16) | (uint32_t)c);
+  }
+
+  auto fill_items = [&](int32_t *it, int tile) {
+    int64_t k = 0;
+    for (int s : order)
+      for (int64_t t0 = cu[s]; t0 < cu[s + 1]; t0 += tile) {
+        it[4 * k + 0] = (int32_t)cu[s];
+        it[4 * k + 1] = (int32_t)cu[s + 1];
+        it[4 * k + 2] = (int32_t)t0;
+        it[4 * k + 3] = s;
+        ++k;
+      }
+  };
+  fill_items(reinterpret_cast<int32_t *>(blob + p.off_fwd_items), qt);
+  fill_items(reinterpret_cast<int32_t *>(blob + p.off_bwd_items), kt);
+
+  // RoPE table: angle pos * theta^(-4j/d), j < d/4, in double, rounded once.
+  float *rope = reinterpret_cast<float *>(blob + p.off_rope);
+  const int q4 = (int)(d / 4);
+  for (int pos = 0; pos < rope_rows; ++pos)
+    for (int j = 0; j < q4; ++j) {
+      const double om = std::pow((double)desc->rope_theta, -4.0 * j / (double)d);
+      const double a = (double)pos * om;
+      rope[2 * (pos * q4 + j) + 0] = (float)std::cos(a);
+      rope[2 * (pos * q4 + j) + 1] = (float)std::sin(a);
+    }
+  return MMDIT_OK;
+}
+
+}  // namespace mmdit

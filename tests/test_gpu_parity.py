@@ -1,0 +1,112 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs. Marked ``gpu``: needs an MI355X and the built library."""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from parity import check, prologue_bwd_from, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import packed_attention_nr_amd as pam
+    pam.lib()  # must load: no fallback
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _compare(inp, gpu, ref, heads=None, backward=True, extra=()):
+    """Check every output of the oracle against the GPU's (on `heads`)."""
+    hs = slice(None) if heads is None else list(heads)
+    fails = []
+    keys = ["q_hat", "k_hat", "o", "rstd_q", "rstd_k"] + list(extra)
+    if backward and inp.dout is not None:
+        keys += ["dq_hat", "dk_hat", "dv", "dq", "dk"]
+        if heads is None:
+            keys += ["dgains"]
+    for k in keys:
+        g = gpu[k] if k == "dgains" else gpu[k][:, hs]
+        ok, msg = check(k, g, ref[k], inp.dtype, l2_only=(k == "dgains"), failures=fails)
+        _say("   " + msg)
+    # lse: natural-log logsumexp, absolute error (bf16) / normwise (fp32)
+    e = np.max(np.abs(gpu["lse"][:, hs] - ref["lse"]))
+    _say(f"   lse: max_abs={e:.3e}")
+    if e > (2e-2 if inp.dtype == "bf16" else 1e-5 * np.max(np.abs(ref["lse"]))):
+        fails.append(f"lse max_abs {e:.3e}")
+    assert not fails, fails
+
+
+# ---------------------------------------------------------------------------
+# small packs: every output, all heads
+# ---------------------------------------------------------------------------
+EDGE_PACKS = {
+    "one_token_samples": dict(text=[1, 0, 1], grids=[(0, 0), (1, 1), (0, 0)]),
+    "text_only_and_image_only": dict(text=[37, 0], grids=[(0, 0), (9, 7)]),
+    "exact_tiles": dict(text=[64, 0], grids=[(8, 8), (16, 8)]),
+    "ragged_multi_tile": dict(text=[45, 3, 130], grids=[(13, 11), (2, 5), (7, 19)]),
+    "wide_4to1": dict(text=[20], grids=[(8, 32)]),
+    "tile_plus_one": dict(text=[1], grids=[(16, 8)]),
+}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", sorted(EDGE_PACKS))
+def test_edge_packs(case, d, dtype):
+    spec = EDGE_PACKS[case]
+    inp = workloads.random_pack(sorted(EDGE_PACKS).index(case), heads=3, head_dim=d, dtype=dtype,
+                                text=spec["text"], grids=spec["grids"])
+    _say(f"edge pack {case} d={d} {dtype} N={inp.num_tokens}")
+    _compare(inp, run_gpu(inp), run_oracle(inp))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seed", range(6))
+def test_random_packs(seed, dtype):
+    inp = workloads.random_pack(100 + seed, max_samples=6, max_text=300, max_side=24,
+                                heads=2, head_dim=128 if seed % 2 else 64, dtype=dtype)
+    _say(f"random pack seed={seed} {dtype} d={inp.head_dim} N={inp.num_tokens} "
+         f"L={inp.seqlens().tolist()}")
+    _compare(inp, run_gpu(inp), run_oracle(inp))
+
+
+def test_tiny_fp32_workload():
+    inp = workloads.draw("tiny_fp32")
+    _say(f"tiny_fp32 N={inp.num_tokens}")
+    _compare(inp, run_gpu(inp, backward=False), run_oracle(inp, backward=False))
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: complete outputs for a subset of heads, and the
+# prologue backward checked on all heads from the GPU's own dQ-hat / dK-hat
+# ---------------------------------------------------------------------------
+FULL = [("gen1024", [0, 11, 23]), ("mixed6", [0, 13]), ("gen2048", [5]), ("small64", [0, 23])]
+
+
+@pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
+def test_full_workload(name, heads):
+    w = workloads.get(name)
+    inp = workloads.draw(name)
+    _say(f"{name}: N={inp.num_tokens} H={inp.heads} heads checked={heads}")
+    gpu = run_gpu(inp, backward=w.backward)
+    ref = run_oracle(inp, heads=heads, backward=w.backward)
+    _compare(inp, gpu, ref, heads=heads, backward=w.backward)
+    if w.backward:
+        pb = prologue_bwd_from(inp, gpu["dq_hat"], gpu["dk_hat"])
+        fails = []
+        for k in ("dq", "dk", "dgains"):
+            _, msg = check(k + " (from GPU dQ/dK-hat)", gpu[k], pb[k], inp.dtype,
+                           l2_only=(k == "dgains"), failures=fails)
+            _say("   " + msg)
+        assert not fails, fails

@@ -1,0 +1,226 @@
+"""CPU tests of the C ABI: symbols, the host pack plan (checked against the
+oracle's independent layout), and argument validation (invalid calls must
+return their status code before anything is launched)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pam = pytest.importorskip("packed_attention_nr_amd")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    try:
+        return pam.lib()
+    except ImportError as e:
+        pytest.fail(f"libmmdit.so must be built before the tests: {e}")
+
+
+def test_exports_every_header_symbol(L):
+    hdr = open(os.path.join(ROOT, "include", "mmdit.h")).read()
+    names = set(re.findall(r"\b(mmdit_[a-z_]+)\s*\(", hdr))
+    assert {"mmdit_pack_plan", "mmdit_attn_fwd", "mmdit_attn_bwd"} <= names
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert pam.mmdit_abi_version() == 1
+    assert pam.mmdit_status_str(0) == "ok"
+
+
+def _blob_section(blob, off, n, dtype):
+    return np.frombuffer(blob[off:off + n * np.dtype(dtype).itemsize].tobytes(), dtype=dtype)
+
+
+def _check_plan(inp, dtype_code):
+    H, d = inp.heads, inp.head_dim
+    plan, blob = pam.mmdit_pack_plan(inp.text_len, inp.grid_h, inp.grid_w, H, d, dtype_code)
+    lay = oracle.layout(inp.text_len, inp.grid_h, inp.grid_w)
+    N, S = lay.num_tokens, len(inp.text_len)
+    assert plan.total_tokens == N and plan.num_samples == S and plan.num_heads == H
+    assert plan.max_seqlen == int(np.diff(lay.cu_seqlens).max())
+    cu = _blob_section(blob, plan.off_cu_seqlens, S + 1, np.int32)
+    assert np.array_equal(cu, lay.cu_seqlens)
+    meta = _blob_section(blob, plan.off_tok_meta, N, np.int32)
+    um = meta.view(np.uint32)
+    assert np.array_equal((um >> 31).astype(bool), lay.is_image)
+    assert np.array_equal(((um >> 16) & 0x7FFF).astype(np.int64), lay.row)
+    assert np.array_equal((um & 0xFFFF).astype(np.int64), lay.col)
+    # work lists: every tile of every sample once, longest segment first
+    for n_items, off, tile in ((plan.num_fwd_items, plan.off_fwd_items, plan.q_tile),
+                               (plan.num_bwd_items, plan.off_bwd_items, plan.kv_tile)):
+        it = _blob_section(blob, off, 4 * n_items, np.int32).reshape(-1, 4)
+        expect = set()
+        for s in range(S):
+            for t0 in range(cu[s], cu[s + 1], tile):
+                expect.add((cu[s], cu[s + 1], t0, s))
+        assert set(map(tuple, it.tolist())) == expect and len(it) == len(expect)
+        lens = it[:, 1] - it[:, 0]
+        assert np.all(np.diff(lens) <= 0)
+    # RoPE table: cos/sin of pos * theta^(-4j/d), rounded once to fp32
+    rope = _blob_section(blob, plan.off_rope, plan.rope_rows * (d // 4) * 2, np.float32)
+    rope = rope.reshape(plan.rope_rows, d // 4, 2)
+    assert plan.rope_rows == max(1, int(max(inp.grid_h.max(), inp.grid_w.max())))
+    pos = np.arange(plan.rope_rows)[:, None].astype(np.float64)
+    ang = pos * oracle.rope_frequencies(d)[None, :]
+    assert np.array_equal(rope[..., 0], np.cos(ang).astype(np.float32))
+    assert np.array_equal(rope[..., 1], np.sin(ang).astype(np.float32))
+    return plan
+
+
+@pytest.mark.parametrize("name", workloads.ORDER)
+def test_plan_matches_oracle_layout_on_workloads(L, name):
+    w = workloads.get(name)
+    rng = np.random.default_rng(0)
+    if w.text is None:
+        text = rng.integers(w.text_range[0], w.text_range[1] + 1, len(w.grids))
+    else:
+        text = np.array(w.text)
+    inp = workloads.Inputs(np.asarray(text, np.int32), np.array([g[0] for g in w.grids], np.int32),
+                           np.array([g[1] for g in w.grids], np.int32), None, None, None, None,
+                           None, w.heads, w.head_dim, w.dtype)
+    plan = _check_plan(inp, 1 if w.dtype == "bf16" else 0)
+    expect_n = {"tiny_fp32": 440, "gen1024": 4608, "mixed6": 20436, "gen2048": 16896, "small64": 74894}
+    assert plan.total_tokens == expect_n[name]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_matches_oracle_layout_random(L, seed):
+    inp = workloads.random_pack(seed, max_samples=9, max_text=300, max_side=40,
+                                heads=3, head_dim=64, backward=False)
+    _check_plan(inp, 0)
+
+
+def _desc_call(text, gh, gw, H=2, d=64, dtype=1, theta=1e4, eps=1e-6, budget=0, blob_bytes=None):
+    t = np.ascontiguousarray(text, np.int32)
+    h = np.ascontiguousarray(gh, np.int32)
+    w = np.ascontiguousarray(gw, np.int32)
+    P = C.POINTER(C.c_int32)
+    desc = pam.PackDesc(len(t), t.ctypes.data_as(P), h.ctypes.data_as(P), w.ctypes.data_as(P),
+                        H, d, dtype, theta, eps, budget)
+    plan = pam.Plan()
+    if blob_bytes is None:
+        return pam.lib().mmdit_pack_plan(C.byref(desc), C.byref(plan), None, 0), plan
+    buf = np.zeros(max(blob_bytes, 1), np.uint8)
+    return pam.lib().mmdit_pack_plan(C.byref(desc), C.byref(plan), buf.ctypes.data, blob_bytes), plan
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(text=[3], gh=[2], gw=[0]), 1),                 # grid h without w
+    (dict(text=[-1], gh=[2], gw=[2]), 1),                # negative text
+    (dict(text=[0], gh=[0], gw=[0]), 1),                 # empty sample
+    (dict(text=[3], gh=[40000], gw=[1]), 1),             # grid side too large
+    (dict(text=[3], gh=[2], gw=[2], H=0), 1),            # no heads
+    (dict(text=[3], gh=[2], gw=[2], d=96), 2),           # unsupported head_dim
+    (dict(text=[3], gh=[2], gw=[2], d=66), 1),           # not a multiple of 4
+    (dict(text=[3], gh=[2], gw=[2], dtype=7), 1),        # bad dtype
+    (dict(text=[3], gh=[2], gw=[2], theta=0.0), 1),      # bad theta
+    (dict(text=[3], gh=[2], gw=[2], eps=-1.0), 1),       # bad eps
+    (dict(text=[3], gh=[2], gw=[2], eps=float("nan")), 1),
+    (dict(text=[30, 5], gh=[4, 1], gw=[4, 1], budget=40), 4),   # over budget (52 tokens)
+])
+def test_plan_rejects_invalid_descriptors(L, case, code):
+    st, _ = _desc_call(**case)
+    assert st == code, pam.mmdit_last_error()
+    assert pam.mmdit_last_error()
+
+
+def test_plan_budget_and_blob_size(L):
+    st, plan = _desc_call([30, 5], [4, 1], [4, 1], budget=52)
+    assert st == 0 and plan.total_tokens == 52
+    st, _ = _desc_call([30, 5], [4, 1], [4, 1], blob_bytes=int(plan.blob_bytes) - 1)
+    assert st == 3
+    st, plan2 = _desc_call([30, 5], [4, 1], [4, 1], blob_bytes=int(plan.blob_bytes))
+    assert st == 0 and plan2.fingerprint == plan.fingerprint
+
+
+# --------------------------------------------------------------------------
+# argument validation of fwd / bwd: fake (aligned, never dereferenced) device
+# pointers; every call below must fail on the host before any launch.
+# --------------------------------------------------------------------------
+BASE = 1 << 40
+SZ = 1 << 30
+
+
+def _p(i):
+    return BASE + i * SZ
+
+
+@pytest.fixture(scope="module")
+def small_plan(L):
+    plan, blob = pam.mmdit_pack_plan([5, 3], [2, 3], [3, 2], 2, 64, 1)
+    return plan
+
+
+def _fwd(plan, **kw):
+    """Call mmdit_attn_fwd with fake pointers (ints); kw overrides fields."""
+    args = dict(q=_p(1), k=_p(2), v=_p(3), q_stride=128, k_stride=128, v_stride=128,
+                gains=_p(4), o=_p(5), lse=_p(6), q_hat=_p(7), k_hat=_p(8), rstd=_p(9),
+                stages=0, blob=_p(0), ws=None, ws_bytes=0, plan=plan)
+    args.update(kw)
+    a = pam.FwdArgs(args["q"], args["k"], args["v"], args["q_stride"], args["k_stride"],
+                    args["v_stride"], args["gains"], args["o"], args["lse"], args["q_hat"],
+                    args["k_hat"], args["rstd"], args["stages"])
+    return pam.lib().mmdit_attn_fwd(C.byref(args["plan"]), args["blob"], C.byref(a),
+                                    args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1),
+    (dict(q=_p(1) + 8), 1),               # misaligned
+    (dict(q_stride=64), 1),               # stride < H*d
+    (dict(k_stride=132), 1),              # not a multiple of 8
+    (dict(gains=None), 1),
+    (dict(o=None), 1),
+    (dict(k_hat=None), 1),                # only one of q_hat / k_hat
+    (dict(o=_p(3) + 256), 1),             # output overlaps v
+    (dict(lse=_p(5) + 64), 1),            # output overlaps output
+    (dict(stages=8), 1),
+    (dict(blob=None), 1),
+    (dict(q_hat=None, k_hat=None), 1),    # needs a workspace then
+    (dict(q_hat=None, k_hat=None, ws=_p(10), ws_bytes=16), 3),
+    (dict(q_hat=None, k_hat=None, ws=_p(10), ws_bytes=1 << 20, stages=1), 1),
+])
+def test_fwd_rejects_invalid_arguments(small_plan, kw, code):
+    assert _fwd(small_plan, **kw) == code, pam.mmdit_last_error()
+
+
+def test_fwd_rejects_foreign_plan(small_plan):
+    bad = pam.Plan.from_buffer_copy(bytes(small_plan))
+    bad.total_tokens += 1
+    assert _fwd(bad) == 1
+    assert "fingerprint" in pam.mmdit_last_error()
+
+
+def _bwd(plan, ws_bytes=None, **kw):
+    names = ("q", "k", "v", "q_hat", "k_hat", "o", "dout")
+    args = {n: _p(i + 1) for i, n in enumerate(names)}
+    args.update(gains=_p(8), lse=_p(9), rstd=_p(10), dq=_p(11), dk=_p(12), dv=_p(13), dgains=_p(14))
+    args.update(kw)
+    a = pam.BwdArgs(*(args[n] for n in names), 128, 128, 128, args.get("dout_stride", 128),
+                    args["gains"], args["lse"], args["rstd"], args["dq"], args["dk"], args["dv"],
+                    args["dgains"], args.get("stages", 0))
+    ws = args.get("ws", _p(15))
+    wsb = int(plan.bwd_workspace_bytes) if ws_bytes is None else ws_bytes
+    return pam.lib().mmdit_attn_bwd(C.byref(plan), _p(0), C.byref(a), ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=None), 1),
+    (dict(lse=None), 1),
+    (dict(dq=None), 1),
+    (dict(dq=_p(12) + 16), 1),            # dq overlaps dk
+    (dict(dv=_p(3)), 1),                  # dv overlaps v
+    (dict(dout_stride=64), 1),
+    (dict(ws=None), 1),
+    (dict(stages=16), 1),
+    (dict(ws_bytes=64), 3),
+])
+def test_bwd_rejects_invalid_arguments(small_plan, kw, code):
+    ws_bytes = kw.pop("ws_bytes", None)
+    assert _bwd(small_plan, ws_bytes=ws_bytes, **kw) == code, pam.mmdit_last_error()
