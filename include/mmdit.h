@@ -115,8 +115,8 @@ mmdit_status mmdit_pack_plan(const mmdit_pack_desc *desc, mmdit_plan *plan,
  * reads the caller's q_hat / k_hat). */
 #define MMDIT_STAGE_PROLOGUE      1u  /* fwd: RMSNorm + RoPE of Q and K -> q_hat, k_hat */
 #define MMDIT_STAGE_ATTENTION     2u  /* fwd: var-len attention -> o, lse */
-#define MMDIT_STAGE_BWD_PRE       1u  /* bwd: D = rowsum(dO * O), clear dQ-hat accumulator */
-#define MMDIT_STAGE_BWD_ATTENTION 2u  /* bwd: dQ-hat, dK-hat (fp32 workspace), dV */
+#define MMDIT_STAGE_BWD_DQ        1u  /* bwd: D = rowsum(dO * O) and dQ-hat (fp32 workspace) */
+#define MMDIT_STAGE_BWD_DKDV      2u  /* bwd: dK-hat (fp32 workspace) and dV; reads D */
 #define MMDIT_STAGE_BWD_PROLOGUE  4u  /* bwd: inverse RoPE + RMSNorm backward -> dq, dk, dgains */
 
 typedef struct {
@@ -154,10 +154,10 @@ typedef struct {
 } mmdit_bwd_args;
 
 /* Backward of mmdit_attn_fwd for the loss sum(dout * o). workspace_bytes >=
- * plan->bwd_workspace_bytes. Workspace layout after the call (fp32): dQ-hat
- * [N][H][d] at offset 0, dK-hat [N][H][d] right after it, then D [H][N].
- * dq (and so dgains) may differ in the last bits from run to run: dQ-hat is
- * accumulated with fp32 atomics. */
+ * plan->bwd_workspace_bytes. Workspace layout after the call (fp32, each part
+ * 256-byte aligned): dQ-hat [N][H][d] at offset 0, dK-hat [N][H][d] after it,
+ * then D [H][N], then the gain-gradient partials. Deterministic: the same
+ * inputs give bitwise the same outputs (no atomics; fixed-order reductions). */
 mmdit_status mmdit_attn_bwd(const mmdit_plan *plan, const void *plan_blob_dev,
                             const mmdit_bwd_args *args, void *workspace,
                             uint64_t workspace_bytes, void *hip_stream);

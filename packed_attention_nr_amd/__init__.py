@@ -27,9 +27,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmmdit.so
 
 MMDIT_F32, MMDIT_BF16 = 0, 1
 STAGE_PROLOGUE, STAGE_ATTENTION = 1, 2
-STAGE_BWD_PRE, STAGE_BWD_ATTENTION, STAGE_BWD_PROLOGUE = 1, 2, 4
+STAGE_BWD_DQ, STAGE_BWD_DKDV, STAGE_BWD_PROLOGUE = 1, 2, 4
 FWD_STAGES = {"prologue": STAGE_PROLOGUE, "attention": STAGE_ATTENTION}
-BWD_STAGES = {"pre": STAGE_BWD_PRE, "attention": STAGE_BWD_ATTENTION, "prologue": STAGE_BWD_PROLOGUE}
+BWD_STAGES = {"dq": STAGE_BWD_DQ, "dkdv": STAGE_BWD_DKDV, "prologue": STAGE_BWD_PROLOGUE}
 
 
 class PackDesc(C.Structure):

@@ -178,10 +178,10 @@ static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmd
   mmdit_status st = check_plan(plan, blob);
   if (st) return st;
   if (!a) return fail(MMDIT_ERR_INVALID_ARG, "args must not be NULL");
-  const uint32_t all = MMDIT_STAGE_BWD_PRE | MMDIT_STAGE_BWD_ATTENTION | MMDIT_STAGE_BWD_PROLOGUE;
+  const uint32_t all = MMDIT_STAGE_BWD_DQ | MMDIT_STAGE_BWD_DKDV | MMDIT_STAGE_BWD_PROLOGUE;
   const uint32_t stages = a->stages ? a->stages : all;
   if (stages & ~all) return fail(MMDIT_ERR_INVALID_ARG, "unknown backward stage bits 0x%x", stages);
-  const bool pre = stages & MMDIT_STAGE_BWD_PRE, att = stages & MMDIT_STAGE_BWD_ATTENTION,
+  const bool sdq = stages & MMDIT_STAGE_BWD_DQ, skv = stages & MMDIT_STAGE_BWD_DKDV,
              pro = stages & MMDIT_STAGE_BWD_PROLOGUE;
   const int64_t N = plan->total_tokens, H = plan->num_heads, d = plan->head_dim, HD = H * d;
   const int elt = plan->dtype == MMDIT_BF16 ? 2 : 4;
@@ -200,23 +200,23 @@ static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmd
   std::vector<Span> spans;
   spans.push_back(Span{"workspace", reinterpret_cast<uintptr_t>(ws),
                        reinterpret_cast<uintptr_t>(ws) + plan->bwd_workspace_bytes, true});
-  if (pre) {
-    if ((st = check_ptr("o", a->o)) || (st = check_tensor("dout", a->dout, a->dout_stride, HD))) return st;
+  if (sdq) {
+    if ((st = check_ptr("o", a->o))) return st;
+    spans.push_back(span("o", a->o, N, HD, HD, elt, false));
   }
-  if (pre) spans.push_back(span("o", a->o, N, HD, HD, elt, false));
-  if (pre || att) {
-    if ((st = check_tensor("dout", a->dout, a->dout_stride, HD))) return st;
-    spans.push_back(span("dout", a->dout, N, a->dout_stride, HD, elt, false));
-  }
-  if (att) {
+  if (sdq || skv) {
     if ((st = check_ptr("q_hat", a->q_hat)) || (st = check_ptr("k_hat", a->k_hat)) ||
-        (st = check_tensor("v", a->v, a->v_stride, HD)) || (st = check_ptr("lse", a->lse)) ||
-        (st = check_ptr("dv", a->dv)))
+        (st = check_tensor("v", a->v, a->v_stride, HD)) ||
+        (st = check_tensor("dout", a->dout, a->dout_stride, HD)) || (st = check_ptr("lse", a->lse)))
       return st;
     spans.push_back(span("q_hat", a->q_hat, N, HD, HD, elt, false));
     spans.push_back(span("k_hat", a->k_hat, N, HD, HD, elt, false));
     spans.push_back(span("v", a->v, N, a->v_stride, HD, elt, false));
+    spans.push_back(span("dout", a->dout, N, a->dout_stride, HD, elt, false));
     spans.push_back(span("lse", a->lse, H, N, N, 4, false));
+  }
+  if (skv) {
+    if ((st = check_ptr("dv", a->dv))) return st;
     spans.push_back(span("dv", a->dv, N, HD, HD, elt, true));
   }
   if (pro) {
@@ -242,16 +242,16 @@ static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmd
   const PlanDev pd = plan_dev(*plan, blob);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float scale = (float)(1.0 / std::sqrt((double)d));
-  if (pre) {
-    BwdPreArgs ba{a->o, a->dout, a->dout_stride, delta, dq_acc};
-    hipError_t e = launch_bwd_pre(plan->dtype, pd, ba, s);
-    if (e != hipSuccess) return hip_fail("backward preprocess", e);
+  AttnBwdArgs ba{a->q_hat, a->k_hat, a->v, a->dout, a->o, a->v_stride, a->dout_stride, a->lse,
+                 delta, dq_acc, dk_acc, a->dv, (float)(1.4426950408889634 / std::sqrt((double)d)),
+                 scale};
+  if (sdq) {
+    hipError_t e = launch_attn_bwd(plan->dtype, pd, ba, 0, s);
+    if (e != hipSuccess) return hip_fail("attention backward (dQ)", e);
   }
-  if (att) {
-    AttnBwdArgs ba{a->q_hat, a->k_hat, a->v, a->dout, a->v_stride, a->dout_stride, a->lse, delta,
-                   dq_acc, dk_acc, a->dv, (float)(1.4426950408889634 / std::sqrt((double)d)), scale};
-    hipError_t e = launch_attn_bwd(plan->dtype, pd, ba, s);
-    if (e != hipSuccess) return hip_fail("attention backward", e);
+  if (skv) {
+    hipError_t e = launch_attn_bwd(plan->dtype, pd, ba, 1, s);
+    if (e != hipSuccess) return hip_fail("attention backward (dK, dV)", e);
   }
   if (pro) {
     PrologueBwdArgs pa{a->q, a->k, a->q_stride, a->k_stride, a->gains, a->rstd, dq_acc, dk_acc,

@@ -8,49 +8,186 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O),
 //   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d).
 //
-// Design for CDNA4:
-//  * one workgroup = 4 waves = one 128-key tile of one sample and one head
-//    (plan's longest-first work list); each wave owns 32 keys and keeps its
-//    K and V rows in registers as MFMA B operands and its dK, dV accumulators
-//    in registers for the whole item;
-//  * the loop runs over the sample's queries, 64 at a time, with the Q-hat and
-//    dO tiles double-buffered in LDS; S = Q K^T and dP = dO V^T come out with
-//    one key per lane, so P and dS feed dV += P^T dO and dK += dS^T Q as A
-//    operands straight from registers; the Q/dO operands of those products are
-//    read transposed from LDS with ds_read_b64_tr_b16;
-//  * dS (bf16) is written to LDS as dS^T and the 64 x d slice of dQ for all
-//    128 keys is formed by the 4 waves together, then added to an fp32 dQ
-//    accumulator in HBM with atomics (one add per element per key tile);
-//  * masking only for keys past the segment end and queries past it in the
-//    last query tile.
+// Two kernels, neither using atomics:
+//  * dQ kernel (query-tile items, like the forward): each wave owns 32
+//    queries and forms S^T = K Q^T and dP^T = V dO^T with one query per lane,
+//    so P^T and dS^T are per-lane and dS^T feeds dQ^T += K^T dS^T as the B
+//    operand straight from registers; K^T fragments are read transposed from
+//    LDS (ds_read_b64_tr_b16). It also computes and stores D for its queries.
+//  * dK/dV kernel (key-tile items): each wave owns 32 keys with K and V rows
+//    held in registers, loops over the sample's queries 64 at a time, forms
+//    S = Q K^T and dP = dO V^T with one key per lane, and accumulates
+//    dV^T += dO^T P and dK^T += Q^T dS with P and dS as B operands from
+//    registers and dO^T / Q^T read transposed from LDS.
+// dQ is recomputed rather than accumulated across key tiles: device-wide
+// fp32 atomics from eight XCDs cost far more than the extra S and dP products.
 #include "device.h"
 #include "internal.h"
 
 namespace mmdit {
 
 namespace bwd {
-constexpr int BN = 128;   // keys per workgroup (= kBwdTile)
-constexpr int BMQ = 64;   // queries per iteration
+constexpr int QT = 128;   // queries per dQ workgroup (= kFwdTile)
+constexpr int KT = 128;   // keys per dK/dV workgroup (= kBwdTile)
+constexpr int BN = 64;    // keys per dQ iteration
+constexpr int BMQ = 64;   // queries per dK/dV iteration
 constexpr int PAD = 8;    // LDS row padding (elements)
+constexpr float kLog2e = 1.4426950408889634f;
 }  // namespace bwd
 
-static_assert(bwd::BN == kBwdTile, "backward tile must match the plan");
+static_assert(bwd::QT == kFwdTile && bwd::KT == kBwdTile, "backward tiles must match the plan");
 
+// ---------------------------------------------------------------------------
+// dQ-hat (and D) for one 128-query tile of one sample and head.
+// ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_bf16_kernel(PlanDev p, AttnBwdArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(PlanDev p, AttnBwdArgs a) {
+  using namespace bwd;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int LD = D + PAD;
+  constexpr int CHUNKS = BN * D / 8 / 256;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * LD];  // [buf][K,V]
+
+  const int H = p.num_heads;
+  const int N = p.total_tokens;
+  const int item = blockIdx.x / H, h = blockIdx.x % H;
+  const int4 it = p.fwd_items[item];
+  const int seg0 = it.x, seg1 = it.y, q0 = it.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lq = lane & 31, g = lane >> 5;
+  const int64_t HD = (int64_t)H * D;
+  const bf16 *qh = static_cast<const bf16 *>(a.q_hat);
+  const bf16 *kh = static_cast<const bf16 *>(a.k_hat);
+  const bf16 *vv = static_cast<const bf16 *>(a.v);
+  const bf16 *go = static_cast<const bf16 *>(a.dout);
+  const bf16 *oo = static_cast<const bf16 *>(a.o);
+  const float c2 = a.scale_log2;
+
+  // This lane's query: Q-hat and dO rows as B operands (d = 16s + 8g + 0..7).
+  const int qi = q0 + wave * 32 + lq;
+  const int qc = min(qi, seg1 - 1);
+  bf16x8 qf[KS], gf[KS];
+  float dlt = 0.f;
+  {
+    const bf16 *qs = qh + (int64_t)qc * HD + h * D + 8 * g;
+    const bf16 *gs = go + (int64_t)qc * a.dout_stride + h * D + 8 * g;
+    const bf16 *os = oo + (int64_t)qc * HD + h * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qf[s] = as_bf16x8(ld16(qs + 16 * s));
+      gf[s] = as_bf16x8(ld16(gs + 16 * s));
+      const bf16x8 of = as_bf16x8(ld16(os + 16 * s));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dlt = fmaf((float)gf[s][j], (float)of[j], dlt);
+    }
+    dlt = half_sum(dlt);
+  }
+  if (g == 0 && qi < seg1) a.delta[(int64_t)h * N + qi] = dlt;
+  const float lse2 = a.lse[(int64_t)h * N + qc] * kLog2e;
+
+  uint4 kreg[CHUNKS], vreg[CHUNKS];
+  auto load_tile = [&](int kb0) {
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+      const int idx = tid + 256 * c;
+      const int r = idx / (D / 8), c8 = idx % (D / 8);
+      const int key = min(kb0 + r, seg1 - 1);
+      kreg[c] = ld16(kh + (int64_t)key * HD + h * D + 8 * c8);
+      vreg[c] = ld16(vv + (int64_t)key * a.v_stride + h * D + 8 * c8);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+      const int idx = tid + 256 * c;
+      const int r = idx / (D / 8), c8 = idx % (D / 8);
+      st16(&smem[buf][0][r * LD + 8 * c8], kreg[c]);
+      st16(&smem[buf][1][r * LD + 8 * c8], vreg[c]);
+    }
+  };
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[b][i] = 0.f;
+
+  const int ntiles = (seg1 - seg0 + BN - 1) / BN;
+  load_tile(seg0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    const int kb0 = seg0 + j * BN;
+    if (j + 1 < ntiles) load_tile(kb0 + BN);
+    const bf16 *Ks = smem[buf][0];
+    const bf16 *Vs = smem[buf][1];
+    bf16x8 dsf[BN / 16];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kf = as_bf16x8(ld16(&Ks[(kb * 32 + lq) * LD + 16 * ks + 8 * g]));
+        const bf16x8 vf = as_bf16x8(ld16(&Vs[(kb * 32 + lq) * LD + 16 * ks + 8 * g]));
+        s = mfma32(kf, qf[ks], s);
+        dp = mfma32(vf, gf[ks], dp);
+      }
+      const bool tail = kb0 + kb * 32 + 32 > seg1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse2));
+        if (tail && kb0 + kb * 32 + acc_row(i, g) >= seg1) pv = 0.f;
+        s[i] = pv * (dp[i] - dlt);
+      }
+      dsf[2 * kb] = acc_to_bf16(s, 0);
+      dsf[2 * kb + 1] = acc_to_bf16(s, 8);
+    }
+    // dQ^T += K^T dS^T (keys as the k dimension).
+#pragma unroll
+    for (int t = 0; t < BN / 16; ++t)
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const bf16x8 kt = lds_read_tr(Ks, LD, t * 16, b * 32, lane);
+        dq[b] = mfma32(kt, dsf[t], dq[b]);
+      }
+    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dQ-hat row of this lane's query: register i of block b is d = 32b + acc_row(i, g).
+  if (qi < seg1) {
+    float *dst = a.dq_acc + (int64_t)qi * HD + h * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4 *>(dst + b * 32 + 8 * r4 + 4 * g) =
+            make_float4(dq[b][4 * r4] * a.scale, dq[b][4 * r4 + 1] * a.scale,
+                        dq[b][4 * r4 + 2] * a.scale, dq[b][4 * r4 + 3] * a.scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK-hat and dV for one 128-key tile of one sample and head.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(PlanDev p, AttnBwdArgs a) {
   using namespace bwd;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int QB = BMQ / 32;
   constexpr int LD = D + PAD;
-  constexpr int LDT = BMQ + PAD;
-  constexpr int QCH = BMQ * D / 8 / 256;    // 16-byte chunks per thread per Q (or dO) tile
-  constexpr int KCH = BN * D / 8 / 256;     // ... per K tile
-  constexpr int DQ_BLOCKS = QB * DB / 4;    // dQ output blocks per wave
-  __shared__ __attribute__((aligned(16))) bf16 k_s[BN * LD];
+  constexpr int QCH = BMQ * D / 8 / 256;
   __shared__ __attribute__((aligned(16))) bf16 q_s[2][BMQ * LD];
   __shared__ __attribute__((aligned(16))) bf16 g_s[2][BMQ * LD];
-  __shared__ __attribute__((aligned(16))) bf16 dst_s[BN * LDT];
   __shared__ float lse_s[2][BMQ], dlt_s[2][BMQ];
 
   const int H = p.num_heads;
@@ -65,10 +202,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_bf16_kernel(PlanDev p, AttnBw
   const bf16 *kh = static_cast<const bf16 *>(a.k_hat);
   const bf16 *vv = static_cast<const bf16 *>(a.v);
   const bf16 *go = static_cast<const bf16 *>(a.dout);
-  constexpr float kLog2e = 1.4426950408889634f;
   const float c2 = a.scale_log2;
 
-  // This lane's key (B operand row of S and dP).
+  // This lane's key: K-hat and V rows as B operands.
   const int kr = k0 + wave * 32 + lq;
   const bool key_ok = kr < seg1;
   const int kc = min(kr, seg1 - 1);
@@ -81,14 +217,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_bf16_kernel(PlanDev p, AttnBw
       kf[s] = as_bf16x8(ld16(ks + 16 * s));
       vf[s] = as_bf16x8(ld16(vs + 16 * s));
     }
-  }
-  // Whole K tile into LDS for dQ = dS K.
-#pragma unroll
-  for (int c = 0; c < KCH; ++c) {
-    const int idx = tid + 256 * c;
-    const int r = idx / (D / 8), c8 = idx % (D / 8);
-    const int key = min(k0 + r, seg1 - 1);
-    st16(&k_s[r * LD + 8 * c8], ld16(kh + (int64_t)key * HD + h * D + 8 * c8));
   }
 
   uint4 qreg[QCH], greg[QCH];
@@ -103,9 +231,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_bf16_kernel(PlanDev p, AttnBw
       greg[c] = ld16(go + (int64_t)qq * a.dout_stride + h * D + 8 * c8);
     }
     if (tid < BMQ) {
-      const int qq = min(qb0 + tid, seg1 - 1);
-      lreg = a.lse[(int64_t)h * N + qq] * kLog2e;
-      dreg = a.delta[(int64_t)h * N + qq];
+      const int qq = qb0 + tid;
+      const bool ok = qq < seg1;
+      const int qcl = min(qq, seg1 - 1);
+      // Queries past the segment end get lse = +inf, so their P is exactly 0.
+      lreg = ok ? a.lse[(int64_t)h * N + qcl] * kLog2e : INFINITY;
+      dreg = a.delta[(int64_t)h * N + qcl];
     }
   };
   auto store_q = [&](int buf) {
@@ -143,7 +274,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_bf16_kernel(PlanDev p, AttnBw
     const bf16 *Qs = q_s[buf];
     const bf16 *Gs = g_s[buf];
 
-    bf16x8 pa[BMQ / 16], da[BMQ / 16];   // P^T and dS^T as A operands (16 queries each)
+    bf16x8 pb[BMQ / 16], db[BMQ / 16];   // P and dS as B operands (16 queries each)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       f32x16 s, dp;
@@ -154,99 +285,81 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_bf16_kernel(PlanDev p, AttnBw
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 qa = as_bf16x8(ld16(&Qs[(qb * 32 + lq) * LD + 16 * ks + 8 * g]));
-        bf16x8 ga = as_bf16x8(ld16(&Gs[(qb * 32 + lq) * LD + 16 * ks + 8 * g]));
+        const bf16x8 qa = as_bf16x8(ld16(&Qs[(qb * 32 + lq) * LD + 16 * ks + 8 * g]));
+        const bf16x8 ga = as_bf16x8(ld16(&Gs[(qb * 32 + lq) * LD + 16 * ks + 8 * g]));
         s = mfma32(qa, kf[ks], s);
         dp = mfma32(ga, vf[ks], dp);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int ql = qb * 32 + acc_row(i, g);
-        const bool ok = key_ok && (qb0 + ql < seg1);
-        const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse_s[buf][ql])) : 0.f;
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse_s[buf][ql]));
+        pv = key_ok ? pv : 0.f;
         s[i] = pv;
         dp[i] = pv * (dp[i] - dlt_s[buf][ql]);
       }
-      pa[2 * qb] = acc_to_bf16(s, 0);
-      pa[2 * qb + 1] = acc_to_bf16(s, 8);
-      da[2 * qb] = acc_to_bf16(dp, 0);
-      da[2 * qb + 1] = acc_to_bf16(dp, 8);
-      // dS^T rows of this wave's keys, 4 consecutive queries per store.
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 v4;
-        v4[0] = da[2 * qb + (r4 >> 1)][4 * (r4 & 1) + 0];
-        v4[1] = da[2 * qb + (r4 >> 1)][4 * (r4 & 1) + 1];
-        v4[2] = da[2 * qb + (r4 >> 1)][4 * (r4 & 1) + 2];
-        v4[3] = da[2 * qb + (r4 >> 1)][4 * (r4 & 1) + 3];
-        *reinterpret_cast<bf16x4 *>(&dst_s[(wave * 32 + lq) * LDT + qb * 32 + 8 * r4 + 4 * g]) = v4;
-      }
+      pb[2 * qb] = acc_to_bf16(s, 0);
+      pb[2 * qb + 1] = acc_to_bf16(s, 8);
+      db[2 * qb] = acc_to_bf16(dp, 0);
+      db[2 * qb + 1] = acc_to_bf16(dp, 8);
     }
-    // dV += P^T dO, dK += dS^T Q (queries as the k dimension).
+    // dV^T += dO^T P, dK^T += Q^T dS (queries as the k dimension).
 #pragma unroll
     for (int t = 0; t < BMQ / 16; ++t)
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
-        bf16x8 gb = lds_read_tr(Gs, LD, t * 16, b * 32, lane);
-        dv[b] = mfma32(pa[t], gb, dv[b]);
-        bf16x8 qbf = lds_read_tr(Qs, LD, t * 16, b * 32, lane);
-        dk[b] = mfma32(da[t], qbf, dk[b]);
+        const bf16x8 gt = lds_read_tr(Gs, LD, t * 16, b * 32, lane);
+        dv[b] = mfma32(gt, pb[t], dv[b]);
+        const bf16x8 qt = lds_read_tr(Qs, LD, t * 16, b * 32, lane);
+        dk[b] = mfma32(qt, db[t], dk[b]);
       }
-    __syncthreads();
-
-    // dQ[64 x D] = dS[64 x 128] K[128 x D]: DQ_BLOCKS 32x32 blocks per wave.
-#pragma unroll
-    for (int ob = 0; ob < DQ_BLOCKS; ++ob) {
-      const int blk = wave * DQ_BLOCKS + ob;
-      const int qb = blk / DB, b = blk % DB;
-      f32x16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int t = 0; t < BN / 16; ++t) {
-        bf16x8 sa = lds_read_tr(dst_s, LDT, t * 16, qb * 32, lane);
-        bf16x8 kb = lds_read_tr(k_s, LD, t * 16, b * 32, lane);
-        acc = mfma32(sa, kb, acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qg = qb0 + qb * 32 + acc_row(i, g);
-        if (qg < seg1)
-          unsafeAtomicAdd(a.dq_acc + (int64_t)qg * HD + h * D + b * 32 + lq, acc[i] * a.scale);
-      }
-    }
     if (itq + 1 < nit) store_q(buf ^ 1);
     __syncthreads();
   }
 
-  // dV (bf16) and dK-hat (fp32, scaled) for the keys inside the segment.
-  // Accumulator register i of block b holds key acc_row(i, g), d = 32b + lq.
+  // Rows of this lane's key: register i of block b is d = 32b + acc_row(i, g).
+  if (key_ok) {
+    const int64_t off = (int64_t)kr * HD + h * D;
+    bf16 *dvp = static_cast<bf16 *>(a.dv) + off;
+    float *dkp = a.dk_acc + off;
 #pragma unroll
-  for (int b = 0; b < DB; ++b)
+    for (int b = 0; b < DB; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = k0 + wave * 32 + acc_row(i, g);
-      if (key < seg1) {
-        const int64_t off = (int64_t)key * HD + h * D + b * 32 + lq;
-        static_cast<bf16 *>(a.dv)[off] = (bf16)dv[b][i];
-        a.dk_acc[off] = dk[b][i] * a.scale;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int e = b * 32 + 8 * r4 + 4 * g;
+        bf16x4 v4;
+        const bf16x2 t0 = pack2(dv[b][4 * r4], dv[b][4 * r4 + 1]);
+        const bf16x2 t1 = pack2(dv[b][4 * r4 + 2], dv[b][4 * r4 + 3]);
+        v4[0] = t0[0]; v4[1] = t0[1]; v4[2] = t1[0]; v4[3] = t1[1];
+        *reinterpret_cast<bf16x4 *>(dvp + e) = v4;
+        *reinterpret_cast<float4 *>(dkp + e) =
+            make_float4(dk[b][4 * r4] * a.scale, dk[b][4 * r4 + 1] * a.scale,
+                        dk[b][4 * r4 + 2] * a.scale, dk[b][4 * r4 + 3] * a.scale);
       }
-    }
+  }
 }
 
-hipError_t launch_attn_bwd_f32(const PlanDev &p, const AttnBwdArgs &a, hipStream_t stream);
+hipError_t launch_attn_bwd_f32(const PlanDev &p, const AttnBwdArgs &a, int which, hipStream_t stream);
 
 template <int D>
-static hipError_t attn_bwd_bf16(const PlanDev &p, const AttnBwdArgs &a, hipStream_t s) {
+static hipError_t bwd_dq(const PlanDev &p, const AttnBwdArgs &a, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.num_fwd_items * p.num_heads;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, s, p, a);
+  return hipGetLastError();
+}
+template <int D>
+static hipError_t bwd_dkdv(const PlanDev &p, const AttnBwdArgs &a, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_bwd_items * p.num_heads;
-  hipLaunchKernelGGL(attn_bwd_bf16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, s, p, a);
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, s, p, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd(int dtype, const PlanDev &p, const AttnBwdArgs &a, hipStream_t stream) {
-  if (dtype == MMDIT_F32) return launch_attn_bwd_f32(p, a, stream);
-  if (p.head_dim == 64) return attn_bwd_bf16<64>(p, a, stream);
-  if (p.head_dim == 128) return attn_bwd_bf16<128>(p, a, stream);
+// which = 0: dQ-hat and D; which = 1: dK-hat and dV (reads D).
+hipError_t launch_attn_bwd(int dtype, const PlanDev &p, const AttnBwdArgs &a, int which,
+                           hipStream_t stream) {
+  if (dtype == MMDIT_F32) return launch_attn_bwd_f32(p, a, which, stream);
+  if (p.head_dim == 64) return which == 0 ? bwd_dq<64>(p, a, stream) : bwd_dkdv<64>(p, a, stream);
+  if (p.head_dim == 128) return which == 0 ? bwd_dq<128>(p, a, stream) : bwd_dkdv<128>(p, a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -228,10 +228,14 @@ static hipError_t fwd_f32(const PlanDev &p, const AttnFwdArgs &a, hipStream_t s)
 }
 
 template <int D>
-static hipError_t bwd_f32(const PlanDev &p, const AttnBwdArgs &a, hipStream_t s) {
-  const int64_t kv_blocks = (int64_t)p.num_bwd_items * p.num_heads;
-  hipLaunchKernelGGL(attn_bwd_kv_f32_kernel<D>, dim3((unsigned)kv_blocks), dim3(f32k::NT), 0, s, p, a);
-  hipError_t e = hipGetLastError();
+static hipError_t bwd_f32(const PlanDev &p, const AttnBwdArgs &a, int which, hipStream_t s) {
+  if (which == 1) {
+    const int64_t kv_blocks = (int64_t)p.num_bwd_items * p.num_heads;
+    hipLaunchKernelGGL(attn_bwd_kv_f32_kernel<D>, dim3((unsigned)kv_blocks), dim3(f32k::NT), 0, s, p, a);
+    return hipGetLastError();
+  }
+  BwdPreArgs pre{a.o, a.dout, a.dout_stride, a.delta, a.dq_acc};
+  hipError_t e = launch_bwd_pre(MMDIT_F32, p, pre, s);
   if (e != hipSuccess) return e;
   const int64_t q_blocks = (int64_t)p.num_fwd_items * p.num_heads;
   hipLaunchKernelGGL(attn_bwd_q_f32_kernel<D>, dim3((unsigned)q_blocks), dim3(f32k::NT), 0, s, p, a);
@@ -244,9 +248,9 @@ hipError_t launch_attn_fwd_f32(const PlanDev &p, const AttnFwdArgs &a, hipStream
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_bwd_f32(const PlanDev &p, const AttnBwdArgs &a, hipStream_t stream) {
-  if (p.head_dim == 64) return bwd_f32<64>(p, a, stream);
-  if (p.head_dim == 128) return bwd_f32<128>(p, a, stream);
+hipError_t launch_attn_bwd_f32(const PlanDev &p, const AttnBwdArgs &a, int which, hipStream_t stream) {
+  if (p.head_dim == 64) return bwd_f32<64>(p, a, which, stream);
+  if (p.head_dim == 128) return bwd_f32<128>(p, a, which, stream);
   return hipErrorInvalidValue;
 }
 

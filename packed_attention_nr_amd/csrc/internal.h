@@ -83,11 +83,12 @@ struct BwdPreArgs {
 };
 
 struct AttnBwdArgs {
-  const void *q_hat, *k_hat, *v, *dout;
+  const void *q_hat, *k_hat, *v, *dout, *o;
   int64_t v_stride, dout_stride;
-  const float *lse, *delta;    // [H][N]
-  float *dq_acc;               // [N][H][d] fp32, atomically accumulated (pre-scaled)
-  float *dk_acc;               // [N][H][d] fp32
+  const float *lse;            // [H][N]
+  float *delta;                // [H][N]: written by the dQ pass, read by the dK/dV pass
+  float *dq_acc;               // [N][H][d] fp32 dQ-hat (scaled by 1/sqrt(d))
+  float *dk_acc;               // [N][H][d] fp32 dK-hat (scaled by 1/sqrt(d))
   void *dv;                    // [N][H][d] dtype
   float scale_log2;            // log2(e) / sqrt(d)
   float scale;                 // 1 / sqrt(d)
@@ -110,7 +111,9 @@ hipError_t launch_prologue_fwd(int dtype, const PlanDev &p, const PrologueFwdArg
                                hipStream_t stream);
 hipError_t launch_attn_fwd(int dtype, const PlanDev &p, const AttnFwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd_pre(int dtype, const PlanDev &p, const BwdPreArgs &a, hipStream_t stream);
-hipError_t launch_attn_bwd(int dtype, const PlanDev &p, const AttnBwdArgs &a, hipStream_t stream);
+// which = 0: dQ-hat and D; which = 1: dK-hat and dV (needs D).
+hipError_t launch_attn_bwd(int dtype, const PlanDev &p, const AttnBwdArgs &a, int which,
+                           hipStream_t stream);
 hipError_t launch_prologue_bwd(int dtype, const PlanDev &p, const PrologueBwdArgs &a,
                                hipStream_t stream);
 
