@@ -31,7 +31,11 @@ constexpr int QT = 128;   // queries per dQ workgroup (= kFwdTile)
 constexpr int KT = 128;   // keys per dK/dV workgroup (= kBwdTile)
 constexpr int BN = 64;    // keys per dQ iteration
 constexpr int BMQ = 64;   // queries per dK/dV iteration
-constexpr int PAD = 8;    // LDS row padding (elements)
+// LDS row strides (elements past d), by measured gfx950 LDS throughput: tiles
+// read only 16 B per lane down consecutive rows use a 272-byte stride; tiles
+// also read with ds_read_b64_tr_b16 use 304 bytes, fast for both patterns.
+constexpr int PAD_ROWS = 8;
+constexpr int PAD_BOTH = 24;
 constexpr float kLog2e = 1.4426950408889634f;
 }  // namespace bwd
 
@@ -45,9 +49,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(PlanDev p, AttnBwdA
   using namespace bwd;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int LD = D + PAD;
+  constexpr int LDK = D + PAD_BOTH;   // K: row reads and transposed reads
+  constexpr int LDV = D + PAD_ROWS;   // V: row reads only
   constexpr int CHUNKS = BN * D / 8 / 256;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * LD];  // [buf][K,V]
+  __shared__ __attribute__((aligned(16))) bf16 k_s[2][BN * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 v_s[2][BN * LDV];
 
   const int H = p.num_heads;
   const int N = p.total_tokens;
@@ -86,24 +92,36 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(PlanDev p, AttnBwdA
   if (g == 0 && qi < seg1) a.delta[(int64_t)h * N + qi] = dlt;
   const float lse2 = a.lse[(int64_t)h * N + qc] * kLog2e;
 
+  // K/V tile staging (see the forward kernel): rows clamped only in the
+  // segment's last tile.
+  constexpr int RSTEP = 256 / (D / 8);
+  const int r0 = tid / (D / 8), c8 = tid % (D / 8);
+  const bf16 *kbase = kh + (int64_t)r0 * HD + h * D + 8 * c8;
+  const bf16 *vbase = vv + (int64_t)r0 * a.v_stride + h * D + 8 * c8;
   uint4 kreg[CHUNKS], vreg[CHUNKS];
   auto load_tile = [&](int kb0) {
+    if (kb0 + BN <= seg1) {
+      const bf16 *kp = kbase + (int64_t)kb0 * HD;
+      const bf16 *vp = vbase + (int64_t)kb0 * a.v_stride;
 #pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-      const int idx = tid + 256 * c;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      const int key = min(kb0 + r, seg1 - 1);
-      kreg[c] = ld16(kh + (int64_t)key * HD + h * D + 8 * c8);
-      vreg[c] = ld16(vv + (int64_t)key * a.v_stride + h * D + 8 * c8);
+      for (int c = 0; c < CHUNKS; ++c) {
+        kreg[c] = ld16(kp + (int64_t)(RSTEP * c) * HD);
+        vreg[c] = ld16(vp + (int64_t)(RSTEP * c) * a.v_stride);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CHUNKS; ++c) {
+        const int key = min(kb0 + r0 + RSTEP * c, seg1 - 1);
+        kreg[c] = ld16(kh + (int64_t)key * HD + h * D + 8 * c8);
+        vreg[c] = ld16(vv + (int64_t)key * a.v_stride + h * D + 8 * c8);
+      }
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
-      const int idx = tid + 256 * c;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      st16(&smem[buf][0][r * LD + 8 * c8], kreg[c]);
-      st16(&smem[buf][1][r * LD + 8 * c8], vreg[c]);
+      st16(&k_s[buf][(r0 + RSTEP * c) * LDK + 8 * c8], kreg[c]);
+      st16(&v_s[buf][(r0 + RSTEP * c) * LDV + 8 * c8], vreg[c]);
     }
   };
 
@@ -122,8 +140,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(PlanDev p, AttnBwdA
     const int buf = j & 1;
     const int kb0 = seg0 + j * BN;
     if (j + 1 < ntiles) load_tile(kb0 + BN);
-    const bf16 *Ks = smem[buf][0];
-    const bf16 *Vs = smem[buf][1];
+    const bf16 *Ks = k_s[buf];
+    const bf16 *Vs = v_s[buf];
     bf16x8 dsf[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
@@ -135,16 +153,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(PlanDev p, AttnBwdA
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = as_bf16x8(ld16(&Ks[(kb * 32 + lq) * LD + 16 * ks + 8 * g]));
-        const bf16x8 vf = as_bf16x8(ld16(&Vs[(kb * 32 + lq) * LD + 16 * ks + 8 * g]));
+        const bf16x8 kf = as_bf16x8(ld16(&Ks[(kb * 32 + lq) * LDK + 16 * ks + 8 * g]));
+        const bf16x8 vf = as_bf16x8(ld16(&Vs[(kb * 32 + lq) * LDV + 16 * ks + 8 * g]));
         s = mfma32(kf, qf[ks], s);
         dp = mfma32(vf, gf[ks], dp);
       }
-      const bool tail = kb0 + kb * 32 + 32 > seg1;
+      // Keys past the segment end (last tile only): score -inf, so P = dS = 0.
+      if (kb0 + kb * 32 + 32 > seg1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb0 + kb * 32 + acc_row(i, g) >= seg1) s[i] = -INFINITY;
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse2));
-        if (tail && kb0 + kb * 32 + acc_row(i, g) >= seg1) pv = 0.f;
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse2));
         s[i] = pv * (dp[i] - dlt);
       }
       dsf[2 * kb] = acc_to_bf16(s, 0);
@@ -155,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(PlanDev p, AttnBwdA
     for (int t = 0; t < BN / 16; ++t)
 #pragma unroll
       for (int b = 0; b < DB; ++b) {
-        const bf16x8 kt = lds_read_tr(Ks, LD, t * 16, b * 32, lane);
+        const bf16x8 kt = lds_read_tr(Ks, LDK, t * 16, b * 32, lane);
         dq[b] = mfma32(kt, dsf[t], dq[b]);
       }
     if (j + 1 < ntiles) store_tile(buf ^ 1);
@@ -184,7 +206,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(PlanDev p, AttnBw
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int QB = BMQ / 32;
-  constexpr int LD = D + PAD;
+  constexpr int LD = D + PAD_BOTH;    // Q-hat and dO: row reads and transposed reads
   constexpr int QCH = BMQ * D / 8 / 256;
   __shared__ __attribute__((aligned(16))) bf16 q_s[2][BMQ * LD];
   __shared__ __attribute__((aligned(16))) bf16 g_s[2][BMQ * LD];
@@ -219,16 +241,30 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(PlanDev p, AttnBw
     }
   }
 
+  // Q-hat / dO tile staging: thread tid moves chunk c8 of rows r0 + RSTEP*c;
+  // rows clamped into the segment only in its last tile.
+  constexpr int RSTEP = 256 / (D / 8);
+  const int r0 = tid / (D / 8), c8 = tid % (D / 8);
+  const bf16 *qbase = qh + (int64_t)r0 * HD + h * D + 8 * c8;
+  const bf16 *gbase = go + (int64_t)r0 * a.dout_stride + h * D + 8 * c8;
   uint4 qreg[QCH], greg[QCH];
   float lreg = 0.f, dreg = 0.f;
   auto load_q = [&](int qb0) {
+    if (qb0 + BMQ <= seg1) {
+      const bf16 *qp = qbase + (int64_t)qb0 * HD;
+      const bf16 *gp = gbase + (int64_t)qb0 * a.dout_stride;
 #pragma unroll
-    for (int c = 0; c < QCH; ++c) {
-      const int idx = tid + 256 * c;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      const int qq = min(qb0 + r, seg1 - 1);
-      qreg[c] = ld16(qh + (int64_t)qq * HD + h * D + 8 * c8);
-      greg[c] = ld16(go + (int64_t)qq * a.dout_stride + h * D + 8 * c8);
+      for (int c = 0; c < QCH; ++c) {
+        qreg[c] = ld16(qp + (int64_t)(RSTEP * c) * HD);
+        greg[c] = ld16(gp + (int64_t)(RSTEP * c) * a.dout_stride);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < QCH; ++c) {
+        const int qq = min(qb0 + r0 + RSTEP * c, seg1 - 1);
+        qreg[c] = ld16(qh + (int64_t)qq * HD + h * D + 8 * c8);
+        greg[c] = ld16(go + (int64_t)qq * a.dout_stride + h * D + 8 * c8);
+      }
     }
     if (tid < BMQ) {
       const int qq = qb0 + tid;
@@ -242,10 +278,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(PlanDev p, AttnBw
   auto store_q = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < QCH; ++c) {
-      const int idx = tid + 256 * c;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      st16(&q_s[buf][r * LD + 8 * c8], qreg[c]);
-      st16(&g_s[buf][r * LD + 8 * c8], greg[c]);
+      st16(&q_s[buf][(r0 + RSTEP * c) * LD + 8 * c8], qreg[c]);
+      st16(&g_s[buf][(r0 + RSTEP * c) * LD + 8 * c8], greg[c]);
     }
     if (tid < BMQ) {
       lse_s[buf][tid] = lreg;
@@ -293,8 +327,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(PlanDev p, AttnBw
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int ql = qb * 32 + acc_row(i, g);
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse_s[buf][ql]));
-        pv = key_ok ? pv : 0.f;
+        // Keys past the segment end only feed their own dK/dV rows, which are
+        // never stored: no mask needed here.
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse_s[buf][ql]));
         s[i] = pv;
         dp[i] = pv * (dp[i] - dlt_s[buf][ql]);
       }
