@@ -89,9 +89,10 @@ def layout(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int]
     Sample i occupies tokens cu[i] .. cu[i+1]-1 where cu[i+1] = cu[i] + T_i + h_i*w_i:
     first its T_i text tokens, then its h_i x w_i latent grid flattened row-major,
     the grid token at (r, c) being token cu[i] + T_i + r*w_i + c.
-    (picx.dev, "Native-Resolution MMDiT (NR-MMDiT)": images flattened into
-    variable-length token sequences, packed with text, per-sample cumulative
-    offsets; transcript [00:03:16]: a single contiguous batch.)
+    (picx.dev, "Native-Resolution MMDiT (NR-MMDiT)": each image becomes a
+    variable-length token sequence by flattening and is packed together with
+    its text under cumulative offsets; transcript [00:03:16]: all samples share
+    one contiguous batch.)
     """
     T = np.asarray(text_len, dtype=np.int64)
     h = np.asarray(grid_h, dtype=np.int64)
