@@ -90,14 +90,22 @@ typedef struct {
  *   fwd_items   int32 [num_fwd_items][4] = {seg_start, seg_end, tile_start, sample}
  *               one per q_tile-row query tile, longest segment first
  *   bwd_items   int32 [num_bwd_items][4], same for kv_tile-row key tiles
+ *   fwd_blocks  int32 [num_fwd_blocks][2] = {item, head} per workgroup of the
+ *               query-tile kernels, or {-1, -1} (idle). All tiles of one
+ *               (sample, head) form a chunk; chunks are dealt round-robin to
+ *               the GPU's 8 XCDs in longest-first order so that each sample's
+ *               K/V stay in one XCD's L2 (workgroup b runs on XCD b % 8).
+ *   bwd_blocks  int32 [num_bwd_blocks][2], the same for the key-tile kernel
  *   rope        fp32  [rope_rows][d/4][2] = {cos, sin}(pos * theta^(-4j/d)),
  *               computed in double precision and rounded once. */
 typedef struct {
   int32_t num_samples, total_tokens, max_seqlen, num_heads, head_dim, dtype;
   int32_t q_tile, kv_tile, num_fwd_items, num_bwd_items, rope_rows, reserved;
+  int32_t num_fwd_blocks, num_bwd_blocks;
   float rope_theta, rms_eps;
   uint64_t blob_bytes;
   uint64_t off_cu_seqlens, off_tok_meta, off_fwd_items, off_bwd_items, off_rope;
+  uint64_t off_fwd_blocks, off_bwd_blocks;
   uint64_t fwd_workspace_bytes;  /* needed by mmdit_attn_fwd when q_hat/k_hat are NULL */
   uint64_t bwd_workspace_bytes;  /* needed by mmdit_attn_bwd */
   uint64_t fingerprint;          /* hash of every field above; checked on each call */

@@ -42,10 +42,12 @@ class PackDesc(C.Structure):
 class Plan(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "num_samples", "total_tokens", "max_seqlen", "num_heads", "head_dim", "dtype",
-        "q_tile", "kv_tile", "num_fwd_items", "num_bwd_items", "rope_rows", "reserved")] + [
+        "q_tile", "kv_tile", "num_fwd_items", "num_bwd_items", "rope_rows", "reserved",
+        "num_fwd_blocks", "num_bwd_blocks")] + [
         ("rope_theta", C.c_float), ("rms_eps", C.c_float)] + [(n, C.c_uint64) for n in (
         "blob_bytes", "off_cu_seqlens", "off_tok_meta", "off_fwd_items", "off_bwd_items",
-        "off_rope", "fwd_workspace_bytes", "bwd_workspace_bytes", "fingerprint")]
+        "off_rope", "off_fwd_blocks", "off_bwd_blocks", "fwd_workspace_bytes",
+        "bwd_workspace_bytes", "fingerprint")]
 
 
 class FwdArgs(C.Structure):

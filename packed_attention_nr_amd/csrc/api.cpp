@@ -85,6 +85,8 @@ static PlanDev plan_dev(const mmdit_plan &p, const void *blob) {
   d.tok_meta = reinterpret_cast<const int32_t *>(b + p.off_tok_meta);
   d.fwd_items = reinterpret_cast<const int4 *>(b + p.off_fwd_items);
   d.bwd_items = reinterpret_cast<const int4 *>(b + p.off_bwd_items);
+  d.fwd_blocks = reinterpret_cast<const int2 *>(b + p.off_fwd_blocks);
+  d.bwd_blocks = reinterpret_cast<const int2 *>(b + p.off_bwd_blocks);
   d.rope = reinterpret_cast<const float2 *>(b + p.off_rope);
   d.num_samples = p.num_samples;
   d.total_tokens = p.total_tokens;
@@ -92,6 +94,8 @@ static PlanDev plan_dev(const mmdit_plan &p, const void *blob) {
   d.head_dim = p.head_dim;
   d.num_fwd_items = p.num_fwd_items;
   d.num_bwd_items = p.num_bwd_items;
+  d.num_fwd_blocks = p.num_fwd_blocks;
+  d.num_bwd_blocks = p.num_bwd_blocks;
   d.rope_rows = p.rope_rows;
   d.rms_eps = p.rms_eps;
   return d;

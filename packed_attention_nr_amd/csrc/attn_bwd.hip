@@ -27,7 +27,8 @@
 namespace mmdit {
 
 namespace bwd {
-constexpr int QT = 128;   // queries per dQ workgroup (= kFwdTile)
+constexpr int NWQ = 8;    // waves of a dQ workgroup
+constexpr int QT = 32 * NWQ;  // queries per dQ workgroup (= kFwdTileBf16)
 constexpr int KT = 128;   // keys per dK/dV workgroup (= kBwdTile)
 constexpr int BN = 64;    // keys per dQ iteration
 constexpr int BMQ = 64;   // queries per dK/dV iteration
@@ -39,26 +40,29 @@ constexpr int PAD_BOTH = 24;
 constexpr float kLog2e = 1.4426950408889634f;
 }  // namespace bwd
 
-static_assert(bwd::QT == kFwdTile && bwd::KT == kBwdTile, "backward tiles must match the plan");
+static_assert(bwd::QT == kFwdTileBf16 && bwd::KT == kBwdTile, "backward tiles must match the plan");
 
 // ---------------------------------------------------------------------------
-// dQ-hat (and D) for one 128-query tile of one sample and head.
+// dQ-hat (and D) for one 256-query tile of one sample and head.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(PlanDev p, AttnBwdArgs a) {
+__global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p, AttnBwdArgs a) {
   using namespace bwd;
+  constexpr int NT = 64 * NWQ;        // threads
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int LDK = D + PAD_BOTH;   // K: row reads and transposed reads
   constexpr int LDV = D + PAD_ROWS;   // V: row reads only
-  constexpr int CHUNKS = BN * D / 8 / 256;
+  constexpr int CHUNKS = BN * D / 8 / NT;
   __shared__ __attribute__((aligned(16))) bf16 k_s[2][BN * LDK];
   __shared__ __attribute__((aligned(16))) bf16 v_s[2][BN * LDV];
 
   const int H = p.num_heads;
   const int N = p.total_tokens;
-  const int item = blockIdx.x / H, h = blockIdx.x % H;
-  const int4 it = p.fwd_items[item];
+  const int2 wb = p.fwd_blocks[blockIdx.x];
+  if (wb.x < 0) return;  // idle slot of the block map (whole workgroup)
+  const int h = wb.y;
+  const int4 it = p.fwd_items[wb.x];
   const int seg0 = it.x, seg1 = it.y, q0 = it.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, g = lane >> 5;
@@ -92,9 +96,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(PlanDev p, AttnBwdA
   if (g == 0 && qi < seg1) a.delta[(int64_t)h * N + qi] = dlt;
   const float lse2 = a.lse[(int64_t)h * N + qc] * kLog2e;
 
-  // K/V tile staging (see the forward kernel): rows clamped only in the
-  // segment's last tile.
-  constexpr int RSTEP = 256 / (D / 8);
+  // K/V tile staging: thread tid moves 16-byte chunk c8 of rows r0 + RSTEP*c;
+  // rows clamped only in the segment's last tile.
+  constexpr int RSTEP = NT / (D / 8);
   const int r0 = tid / (D / 8), c8 = tid % (D / 8);
   const bf16 *kbase = kh + (int64_t)r0 * HD + h * D + 8 * c8;
   const bf16 *vbase = vv + (int64_t)r0 * a.v_stride + h * D + 8 * c8;
@@ -214,8 +218,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(PlanDev p, AttnBw
 
   const int H = p.num_heads;
   const int N = p.total_tokens;
-  const int item = blockIdx.x / H, h = blockIdx.x % H;
-  const int4 it = p.bwd_items[item];
+  const int2 wb = p.bwd_blocks[blockIdx.x];
+  if (wb.x < 0) return;  // idle slot of the block map (whole workgroup)
+  const int h = wb.y;
+  const int4 it = p.bwd_items[wb.x];
   const int seg0 = it.x, seg1 = it.y, k0 = it.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, g = lane >> 5;
@@ -378,14 +384,12 @@ hipError_t launch_attn_bwd_f32(const PlanDev &p, const AttnBwdArgs &a, int which
 
 template <int D>
 static hipError_t bwd_dq(const PlanDev &p, const AttnBwdArgs &a, hipStream_t s) {
-  const int64_t blocks = (int64_t)p.num_fwd_items * p.num_heads;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, s, p, a);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3((unsigned)p.num_fwd_blocks), dim3(64 * bwd::NWQ), 0, s, p, a);
   return hipGetLastError();
 }
 template <int D>
 static hipError_t bwd_dkdv(const PlanDev &p, const AttnBwdArgs &a, hipStream_t s) {
-  const int64_t blocks = (int64_t)p.num_bwd_items * p.num_heads;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, s, p, a);
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)p.num_bwd_blocks), dim3(256), 0, s, p, a);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ constexpr int NT = ROWS * TPR;   // threads per workgroup
 constexpr int ST = 32;           // staged rows per step
 constexpr float kLog2e = 1.4426950408889634f;
 }  // namespace f32k
-static_assert(f32k::ROWS == kFwdTile && f32k::ROWS == kBwdTile, "fp32 kernels use the plan tiles");
+static_assert(f32k::ROWS == kFwdTileF32 && f32k::ROWS == kBwdTile, "fp32 kernels use the plan tiles");
 
 template <int D>
 __global__ __launch_bounds__(512) void attn_fwd_f32_kernel(PlanDev p, AttnFwdArgs a) {
@@ -29,8 +29,10 @@ __global__ __launch_bounds__(512) void attn_fwd_f32_kernel(PlanDev p, AttnFwdArg
   constexpr int DC = D / TPR;
   __shared__ float ks[ST][D], vs[ST][D];
   const int H = p.num_heads;
-  const int4 it = p.fwd_items[blockIdx.x / H];
-  const int h = blockIdx.x % H;
+  const int2 wb = p.fwd_blocks[blockIdx.x];
+  if (wb.x < 0) return;  // idle slot of the block map (whole workgroup)
+  const int4 it = p.fwd_items[wb.x];
+  const int h = wb.y;
   const int seg0 = it.x, seg1 = it.y;
   const int qi = it.z + threadIdx.x / TPR;
   const int e0 = (threadIdx.x % TPR) * DC;
@@ -93,8 +95,10 @@ __global__ __launch_bounds__(512) void attn_bwd_kv_f32_kernel(PlanDev p, AttnBwd
   __shared__ float qs[ST][D], gs[ST][D], ls[ST], ds_[ST];
   const int H = p.num_heads;
   const int N = p.total_tokens;
-  const int4 it = p.bwd_items[blockIdx.x / H];
-  const int h = blockIdx.x % H;
+  const int2 wb = p.bwd_blocks[blockIdx.x];
+  if (wb.x < 0) return;  // idle slot of the block map (whole workgroup)
+  const int4 it = p.bwd_items[wb.x];
+  const int h = wb.y;
   const int seg0 = it.x, seg1 = it.y;
   const int ki = it.z + threadIdx.x / TPR;
   const int e0 = (threadIdx.x % TPR) * DC;
@@ -166,8 +170,10 @@ __global__ __launch_bounds__(512) void attn_bwd_q_f32_kernel(PlanDev p, AttnBwdA
   __shared__ float ks[ST][D], vs[ST][D];
   const int H = p.num_heads;
   const int N = p.total_tokens;
-  const int4 it = p.fwd_items[blockIdx.x / H];
-  const int h = blockIdx.x % H;
+  const int2 wb = p.fwd_blocks[blockIdx.x];
+  if (wb.x < 0) return;  // idle slot of the block map (whole workgroup)
+  const int4 it = p.fwd_items[wb.x];
+  const int h = wb.y;
   const int seg0 = it.x, seg1 = it.y;
   const int qi = it.z + threadIdx.x / TPR;
   const int e0 = (threadIdx.x % TPR) * DC;
@@ -222,23 +228,20 @@ __global__ __launch_bounds__(512) void attn_bwd_q_f32_kernel(PlanDev p, AttnBwdA
 
 template <int D>
 static hipError_t fwd_f32(const PlanDev &p, const AttnFwdArgs &a, hipStream_t s) {
-  const int64_t blocks = (int64_t)p.num_fwd_items * p.num_heads;
-  hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)blocks), dim3(f32k::NT), 0, s, p, a);
+  hipLaunchKernelGGL(attn_fwd_f32_kernel<D>, dim3((unsigned)p.num_fwd_blocks), dim3(f32k::NT), 0, s, p, a);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t bwd_f32(const PlanDev &p, const AttnBwdArgs &a, int which, hipStream_t s) {
   if (which == 1) {
-    const int64_t kv_blocks = (int64_t)p.num_bwd_items * p.num_heads;
-    hipLaunchKernelGGL(attn_bwd_kv_f32_kernel<D>, dim3((unsigned)kv_blocks), dim3(f32k::NT), 0, s, p, a);
+    hipLaunchKernelGGL(attn_bwd_kv_f32_kernel<D>, dim3((unsigned)p.num_bwd_blocks), dim3(f32k::NT), 0, s, p, a);
     return hipGetLastError();
   }
   BwdPreArgs pre{a.o, a.dout, a.dout_stride, a.delta, a.dq_acc};
   hipError_t e = launch_bwd_pre(MMDIT_F32, p, pre, s);
   if (e != hipSuccess) return e;
-  const int64_t q_blocks = (int64_t)p.num_fwd_items * p.num_heads;
-  hipLaunchKernelGGL(attn_bwd_q_f32_kernel<D>, dim3((unsigned)q_blocks), dim3(f32k::NT), 0, s, p, a);
+  hipLaunchKernelGGL(attn_bwd_q_f32_kernel<D>, dim3((unsigned)p.num_fwd_blocks), dim3(f32k::NT), 0, s, p, a);
   return hipGetLastError();
 }
 

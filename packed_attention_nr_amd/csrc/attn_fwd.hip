@@ -9,59 +9,83 @@
 // (NR-MMDiT)"; findtube.ai transcript at [00:03:16]). This kernel is its own
 // design for CDNA4, not a port:
 //
-//  * one workgroup = 4 waves = one 128-query tile of one sample and one head,
-//    taken from the plan's longest-first work list;
+//  * one workgroup = 8 waves = one 256-query tile of one sample and one head,
+//    taken from the plan's XCD-aware, longest-first block map; two waves per
+//    SIMD;
 //  * every wave owns 32 queries and computes the TRANSPOSED scores
 //    S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so each lane holds one query's
 //    scores: the row max and row sum are in-lane plus one permlane32 swap;
 //  * the probabilities P^T stay in registers and feed O^T += V^T P^T directly
 //    as the B operand (no LDS round trip); V^T fragments come from LDS with
 //    ds_read_b64_tr_b16, in the key order the score accumulator uses;
-//  * K/V tiles of 64 keys are double-buffered in LDS; only the last tile of a
-//    segment is masked;
+//  * ping-pong: the waves form two groups (one wave of each per SIMD) that run
+//    one barrier phase apart. Phase A is matrix work (PV of the previous tile,
+//    then QK^T of the current one), phase B is the softmax (vector ALU) plus
+//    issuing the loads of the tile two ahead. While one group is in A the other
+//    is in B, so the MFMA pipe of each SIMD stays busy during the softmax;
+//  * K/V tiles of 64 keys go global -> LDS directly (global_load_lds_dwordx4,
+//    no register staging) into a 4-stage ring of unpadded XOR-swizzled tiles;
+//    only the last tile of a segment is masked;
 //  * online softmax in fp32 in the exp2 domain, with the running reference max
 //    only moved when a new score exceeds it by more than 8 (log2 units), so
 //    the O^T rescale is rare and the result is unchanged.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
 namespace mmdit {
 
 namespace fwd {
-constexpr int BM = 128;            // queries per workgroup (= kFwdTile)
-constexpr int BN = 64;             // keys per iteration
-// LDS row strides (elements past d), chosen by measured LDS throughput on
-// gfx950: K rows are read 16 B per lane down 32 consecutive rows (a 272-byte
-// stride is conflict-free), V is read with ds_read_b64_tr_b16 in 4x16 blocks
-// (a 320-byte stride is fastest).
-constexpr int PAD_K = 8;
-constexpr int PAD_V = 32;
+constexpr int NW = 8;              // waves per workgroup
+constexpr int BM = 32 * NW;        // queries per workgroup (= kFwdTileBf16)
+constexpr int BN = 64;             // keys per tile
+constexpr int NS = 4;              // stages of the K/V ring
 constexpr float kRescaleThreshold = 8.0f;
 }  // namespace fwd
 
-static_assert(fwd::BM == kFwdTile, "forward tile must match the plan");
+static_assert(fwd::BM == kFwdTileBf16, "forward tile must match the plan");
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(PlanDev p, AttnFwdArgs a) {
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFwdArgs a) {
   using namespace fwd;
   constexpr int KS = D / 16;       // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
-  constexpr int LDK = D + PAD_K;   // LDS row strides (elements)
-  constexpr int LDV = D + PAD_V;
-  constexpr int CHUNKS = BN * D / 8 / 256;  // 16-byte chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) bf16 k_s[2][BN * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 v_s[2][BN * LDV];
+  constexpr int TILE = BN * D;
+  // One LDS object per ring stage: distinct objects let the compiler prove
+  // that a DMA into one stage does not alias reads of another.
+  __shared__ __attribute__((aligned(16))) bf16 k0s[TILE], k1s[TILE], k2s[TILE], k3s[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 v0s[TILE], v1s[TILE], v2s[TILE], v3s[TILE];
+  static_assert(NS == 4, "ring stages are spelled out");
+  auto kst = [&](auto stage) __attribute__((always_inline)) -> bf16 * {
+    constexpr int SG = decltype(stage)::value;
+    if constexpr (SG == 0) return k0s;
+    else if constexpr (SG == 1) return k1s;
+    else if constexpr (SG == 2) return k2s;
+    else return k3s;
+  };
+  auto vst = [&](auto stage) __attribute__((always_inline)) -> bf16 * {
+    constexpr int SG = decltype(stage)::value;
+    if constexpr (SG == 0) return v0s;
+    else if constexpr (SG == 1) return v1s;
+    else if constexpr (SG == 2) return v2s;
+    else return v3s;
+  };
 
-  const int H = p.num_heads;
-  const int item = blockIdx.x / H, h = blockIdx.x % H;
-  const int4 it = p.fwd_items[item];
+  const int2 wb = p.fwd_blocks[blockIdx.x];
+  if (wb.x < 0) return;  // idle slot of the block map (whole workgroup)
+  const int4 it = p.fwd_items[wb.x];
+  const int h = wb.y;
   const int seg0 = it.x, seg1 = it.y, q0 = it.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;       // waves w and w+4 share a SIMD
   const int lq = lane & 31, g = lane >> 5;
-  const int64_t HD = (int64_t)H * D;
+  const int64_t HD = (int64_t)p.num_heads * D;
   const bf16 *qh = static_cast<const bf16 *>(a.q_hat);
-  const bf16 *kh = static_cast<const bf16 *>(a.k_hat);
-  const bf16 *vv = static_cast<const bf16 *>(a.v);
+  const bf16 *kh = static_cast<const bf16 *>(a.k_hat) + h * D;
+  const bf16 *vv = static_cast<const bf16 *>(a.v) + h * D;
+  const int64_t vs = a.v_stride;
 
   // Q^T as the B operand: lane holds query q0 + 32*wave + lq, d = 16s + 8g + 0..7.
   const int qi = q0 + wave * 32 + lq;
@@ -73,37 +97,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
     for (int s = 0; s < KS; ++s) qf[s] = as_bf16x8(ld16(src + 16 * s));
   }
 
-  // Global -> register staging of one K/V tile. Thread tid moves 16-byte
-  // chunk c8 of rows r0 + RSTEP*c; rows are clamped into the segment only in
-  // its last tile.
-  constexpr int RSTEP = 256 / (D / 8);
-  const int r0 = tid / (D / 8), c8 = tid % (D / 8);
-  const bf16 *kbase = kh + (int64_t)r0 * HD + h * D + 8 * c8;
-  const bf16 *vbase = vv + (int64_t)r0 * a.v_stride + h * D + 8 * c8;
-  uint4 kreg[CHUNKS], vreg[CHUNKS];
-  auto load_tile = [&](int kb0) {
+  const int ntiles = (seg1 - seg0 + BN - 1) / BN;
+  // Direct global -> LDS loads of tile t into ring stage t % NS (rows past the
+  // segment end clamped to its last row; masked later). Every ring access uses
+  // a compile-time stage, so the compiler sees that loads into one stage never
+  // alias reads of another and adds no waits for them.
+  TileLoader<D, SWZ_ROWS, BN, NW> kload;
+  TileLoader<D, SWZ_TRANS, BN, NW> vload;
+  kload.init(wave, lane);
+  vload.init(wave, lane);
+  const bf16 *krow0 = kh + (int64_t)kload.r0 * HD;
+  const bf16 *vrow0 = vv + (int64_t)vload.r0 * vs;
+  auto issue = [&](auto stage, int t) __attribute__((always_inline)) {
+    if (t >= ntiles) return;
+    const int kb0 = seg0 + t * BN;
     if (kb0 + BN <= seg1) {
-      const bf16 *kp = kbase + (int64_t)kb0 * HD;
-      const bf16 *vp = vbase + (int64_t)kb0 * a.v_stride;
-#pragma unroll
-      for (int c = 0; c < CHUNKS; ++c) {
-        kreg[c] = ld16(kp + (int64_t)(RSTEP * c) * HD);
-        vreg[c] = ld16(vp + (int64_t)(RSTEP * c) * a.v_stride);
-      }
+      kload.issue(kst(stage), krow0 + (int64_t)kb0 * HD, HD);
+      vload.issue(vst(stage), vrow0 + (int64_t)kb0 * vs, vs);
     } else {
-#pragma unroll
-      for (int c = 0; c < CHUNKS; ++c) {
-        const int key = min(kb0 + r0 + RSTEP * c, seg1 - 1);
-        kreg[c] = ld16(kh + (int64_t)key * HD + h * D + 8 * c8);
-        vreg[c] = ld16(vv + (int64_t)key * a.v_stride + h * D + 8 * c8);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-      st16(&k_s[buf][(r0 + RSTEP * c) * LDK + 8 * c8], kreg[c]);
-      st16(&v_s[buf][(r0 + RSTEP * c) * LDV + 8 * c8], vreg[c]);
+      kload.issue_clamped(kst(stage), kh, HD, kb0, seg1 - 1);
+      vload.issue_clamped(vst(stage), vv, vs, kb0, seg1 - 1);
     }
   };
 
@@ -114,40 +127,43 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
     for (int i = 0; i < 16; ++i) o[b][i] = 0.f;
   float m_ref = -INFINITY, l_part = 0.f;
   const float c2 = a.scale_log2;
+  f32x16 s[BN / 32];
+  bf16x8 pf[BN / 16];
 
-  const int ntiles = (seg1 - seg0 + BN - 1) / BN;
-  load_tile(seg0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const int kb0 = seg0 + j * BN;
-    if (j + 1 < ntiles) load_tile(kb0 + BN);
-    const bf16 *Ks = k_s[buf];
-    const bf16 *Vs = v_s[buf];
-
-    // S^T = K Q^T : two 32-key blocks.
-    f32x16 s[BN / 32];
+  // Phase A pieces (matrix work).
+  auto scores = [&](auto stage) __attribute__((always_inline)) {  // s = K Q^T from ring stage
+    const bf16 *Ks = kst(stage);
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 kf = as_bf16x8(ld16(&Ks[(kb * 32 + lq) * LDK + 16 * ks + 8 * g]));
+        const bf16x8 kf = as_bf16x8(ld16(&Ks[swz_off<D, SWZ_ROWS>(kb * 32 + lq, 16 * ks + 8 * g)]));
         s[kb] = mfma32(kf, qf[ks], s[kb]);
       }
     }
-    // Mask keys past the segment end (only the last tile has any).
-    if (kb0 + BN > seg1) {
+  };
+  auto accumulate = [&](auto stage) __attribute__((always_inline)) {  // O^T += V^T P^T from ring stage
+    const bf16 *Vs = vst(stage);
+#pragma unroll
+    for (int u = 0; u < BN / 16; ++u)
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        const bf16x8 vf = lds_read_tr_swz<D, SWZ_TRANS>(Vs, u * 16, b * 32, lane);
+        o[b] = mfma32(vf, pf[u], o[b]);
+      }
+  };
+  // Phase B piece (vector ALU): online softmax of tile t's scores -> pf.
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    const int kb0 = seg0 + t * BN;
+    if (kb0 + BN > seg1) {  // keys past the segment end (last tile only)
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (kb0 + kb * 32 + acc_row(i, g) >= seg1) s[kb][i] = -INFINITY;
     }
-    // Online softmax (exp2 domain).
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
@@ -164,7 +180,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
         for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
       m_ref = mn;
     }
-    bf16x8 pf[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
@@ -176,18 +191,42 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
       pf[2 * kb] = acc_to_bf16(s[kb], 0);
       pf[2 * kb + 1] = acc_to_bf16(s[kb], 8);
     }
-    // O^T += V^T P^T : 16 keys per MFMA.
-#pragma unroll
-    for (int t = 0; t < BN / 16; ++t)
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        bf16x8 vf = lds_read_tr(Vs, LDV, t * 16, b * 32, lane);
-        o[b] = mfma32(vf, pf[t], o[b]);
-      }
+  };
 
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+  // Schedule (every wave passes the same number of barriers; group 1 runs one
+  // phase behind group 0):
+  //   A_0 = scores(0); then for each tile t: [wait own loads, barrier]
+  //   B_t = issue(t+2), softmax(t); [barrier] A_{t+1} = accumulate(t), scores(t+1).
+  // Tile t+2 reuses the stage of tile t-2, whose last reader (accumulate(t-2)
+  // in A_{t-1}) both groups have passed before either issues in B_t; each wave
+  // waits for its own loads at the end of its next A phase, at least one
+  // barrier before any wave reads the tile.
+  auto step = [&](auto stage, int t) __attribute__((always_inline)) {  // stage = t % NS
+    constexpr int SG = decltype(stage)::value;
+    wait_vmem();
+    phase_barrier();
+    issue(std::integral_constant<int, (SG + 2) % NS>{}, t + 2);
+    softmax(t);
+    phase_barrier();
+    accumulate(stage);
+    if (t + 1 < ntiles) scores(std::integral_constant<int, (SG + 1) % NS>{});
+  };
+  issue(std::integral_constant<int, 0>{}, 0);
+  issue(std::integral_constant<int, 1>{}, 1);
+  wait_vmem();
+  lds_barrier();
+  if (grp == 1) lds_barrier();
+  scores(std::integral_constant<int, 0>{});
+  for (int t = 0; t < ntiles; t += NS) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 >= ntiles) break;
+    step(std::integral_constant<int, 1>{}, t + 1);
+    if (t + 2 >= ntiles) break;
+    step(std::integral_constant<int, 2>{}, t + 2);
+    if (t + 3 >= ntiles) break;
+    step(std::integral_constant<int, 3>{}, t + 3);
   }
+  if (grp == 0) lds_barrier();
 
   // Epilogue: normalise, store O (rows inside the segment) and lse.
   const float l = half_sum(l_part);
@@ -213,8 +252,8 @@ hipError_t launch_attn_fwd_f32(const PlanDev &p, const AttnFwdArgs &a, hipStream
 
 template <int D>
 static hipError_t attn_fwd_bf16(const PlanDev &p, const AttnFwdArgs &a, hipStream_t s) {
-  const int64_t blocks = (int64_t)p.num_fwd_items * p.num_heads;
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, s, p, a);
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel<D>, dim3((unsigned)p.num_fwd_blocks), dim3(64 * fwd::NW), 0, s, p,
+                     a);
   return hipGetLastError();
 }
 

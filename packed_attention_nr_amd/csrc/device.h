@@ -99,6 +99,119 @@ __device__ __forceinline__ bf16x8 lds_read_tr(const bf16 *m, int ld, int k0, int
   return r;
 }
 
+// ---------------------------------------------------------------------------
+// Unpadded, XOR-swizzled LDS tiles filled by direct global->LDS loads.
+// A tile row holds CPR 16-byte chunks; logical chunk c of row r sits at
+// physical chunk c ^ swz(r). Two swizzles, picked by measured gfx950 LDS
+// throughput: ROWS for tiles read 16 bytes per lane down consecutive rows,
+// TRANS for tiles read with ds_read_b64_tr_b16 (rows r..r+3 of a 4x16 block
+// land in four different 64-byte bank groups).
+// ---------------------------------------------------------------------------
+enum Swz { SWZ_ROWS = 0, SWZ_TRANS = 1 };
+
+template <int CPR, int SW>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (SW == SWZ_ROWS) return (((r & 7) << 1) | ((r >> 3) & 1)) & (CPR - 1);
+  else return (4 * (r & 3)) & (CPR - 1);
+}
+
+// Element offset of (row r, element e) in a swizzled tile of D-element rows.
+template <int D, int SW>
+__device__ __forceinline__ int swz_off(int r, int e) {
+  constexpr int CPR = D / 8;
+  return r * D + (((e >> 3) ^ swz<CPR, SW>(r)) << 3) + (e & 7);
+}
+
+// 16-byte global -> LDS copy for every lane of the wave: lane l's 16 bytes
+// land at lds_wave_base + 16*l (lds_wave_base must be wave-uniform).
+__device__ __forceinline__ void g2lds16(const void *src, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+
+// Wait until this wave's outstanding global (and global->LDS) loads are done.
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations, so global
+// (and global->LDS) loads in flight stay in flight across it. Global data a
+// wave loaded for others must be covered by its own wait_vmem() before a
+// barrier that precedes the readers.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The same barrier as a hard scheduling boundary: the compiler moves no
+// instruction across it (keeps the two halves of a ping-pong schedule apart).
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Direct global -> LDS loader of a swizzled D-wide tile of ROWS rows, shared
+// by NW waves. Each wave-wide load fills 64/CPR consecutive rows; lane l of
+// load u covers tile row r0 + u*RPL (r0 = first row of this lane) and
+// physical chunk l % CPR, fetching the logical chunk that the swizzle puts
+// there. Per-lane offsets are computed once.
+template <int D, int SW, int ROWS, int NW>
+struct TileLoader {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPL = 64 / CPR;          // rows per wave-wide load
+  static constexpr int LOADS = ROWS / RPL / NW; // loads per wave
+  static_assert(ROWS % (RPL * NW) == 0, "tile rows must split evenly over the waves");
+  int r0;                 // tile row of this lane in load 0
+  int lds0;               // element offset of this wave's first load (uniform)
+  int chunk[LOADS];       // element offset of the logical chunk, per load
+
+  __device__ __forceinline__ void init(int wave_uniform, int lane) {
+    r0 = wave_uniform * LOADS * RPL + lane / CPR;
+    lds0 = wave_uniform * LOADS * RPL * D;
+    const int pc = lane % CPR;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) chunk[u] = 8 * (pc ^ swz<CPR, SW>(r0 + u * RPL));
+  }
+  // Rows kb0 + r for r < ROWS, all inside the source: row_ptr = element 0 of
+  // source row (kb0 + r0), stride = elements between source rows.
+  __device__ __forceinline__ void issue(bf16 *tile, const bf16 *row_ptr, int64_t stride) const {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+      g2lds16(row_ptr + (int64_t)(u * RPL) * stride + chunk[u], tile + lds0 + u * RPL * D);
+  }
+  // Same, with source rows clamped to last_row: base = element 0 of row 0.
+  __device__ __forceinline__ void issue_clamped(bf16 *tile, const bf16 *base, int64_t stride, int kb0,
+                                                int last_row) const {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int row = min(kb0 + r0 + u * RPL, last_row);
+      g2lds16(base + (int64_t)row * stride + chunk[u], tile + lds0 + u * RPL * D);
+    }
+  }
+};
+
+// Swizzled counterpart of lds_read_tr (same fragment, same k order).
+template <int D, int SW>
+__device__ __forceinline__ bf16x8 lds_read_tr_swz(const bf16 *m, int k0, int n0, int lane) {
+  const int G = lane >> 4, i = lane & 15;
+  const int g = G >> 1, nh = G & 1;
+  const int r = k0 + 4 * g + (i >> 2);
+  const int e = n0 + nh * 16 + 4 * (i & 3);
+  const bf16 *p0 = m + swz_off<D, SW>(r, e);
+  const bf16 *p1 = m + swz_off<D, SW>(r + 8, e);
+  bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
+  bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p1);
+  bf16x8 out;
+  out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
+  out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
+  return out;
+}
+
 // Row of the 32x32 accumulator held in register i by lanes of half g.
 __device__ __forceinline__ constexpr int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
 

@@ -12,8 +12,11 @@
 
 namespace mmdit {
 
-// Rows of one forward query tile / one backward key tile (work-list granularity).
-constexpr int kFwdTile = 128;
+// Rows of one query tile (forward and dQ) / one key tile (dK, dV): the
+// work-list granularity. bf16 packs use 256-query tiles (8-wave workgroups);
+// fp32 packs use 128-row tiles for both.
+constexpr int kFwdTileBf16 = 256;
+constexpr int kFwdTileF32 = 128;
 constexpr int kBwdTile = 128;
 // Limits checked by the plan.
 constexpr int kMaxGridSide = 32768;             // row and col fit in 15 bits of tok_meta
@@ -22,6 +25,8 @@ constexpr int64_t kMaxElements = 1ll << 40;     // N*H*d
 // Prologue backward: tokens per block and the cap on blocks (= gain partials).
 constexpr int kPbwdTokensPerBlock = 64;
 constexpr int kPbwdMaxBlocks = 1024;
+// XCDs (each with its own L2) of the target GPU; workgroup b runs on XCD b % kXcds.
+constexpr int kXcds = 8;
 
 constexpr uint32_t kBlobMagic = 0x50444D4Du;    // "MMDP"
 constexpr uint64_t kBlobHeaderBytes = 64;
@@ -53,9 +58,11 @@ struct PlanDev {
   const int32_t *tok_meta;     // [N]
   const int4 *fwd_items;       // [num_fwd_items]
   const int4 *bwd_items;       // [num_bwd_items]
+  const int2 *fwd_blocks;      // [num_fwd_blocks] {item, head} or {-1, -1}
+  const int2 *bwd_blocks;      // [num_bwd_blocks]
   const float2 *rope;          // [rope_rows][d/4] (cos, sin)
   int32_t num_samples, total_tokens, num_heads, head_dim;
-  int32_t num_fwd_items, num_bwd_items, rope_rows;
+  int32_t num_fwd_items, num_bwd_items, num_fwd_blocks, num_bwd_blocks, rope_rows;
   float rms_eps;
 };
 

@@ -33,9 +33,8 @@ uint64_t plan_fingerprint(const mmdit_plan &p) {
 static uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 int fwd_tile(int dtype, int d) {
-  (void)dtype;
   (void)d;
-  return kFwdTile;
+  return dtype == MMDIT_BF16 ? kFwdTileBf16 : kFwdTileF32;
 }
 int bwd_tile(int dtype, int d) {
   (void)dtype;
@@ -106,7 +105,38 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
     return n;
   };
   const int64_t n_fwd = count_items(qt), n_bwd = count_items(kt);
+  if ((n_fwd + kXcds) * H > INT32_MAX / 4 || (n_bwd + kXcds) * H > INT32_MAX / 4)
+    return fail(MMDIT_ERR_INVALID_ARG, "too many work items");
   const int rope_rows = (int)std::max<int64_t>(1, max_side);
+  // Workgroup -> (item, head) maps: chunks of all tiles of one (sample, head),
+  // dealt round-robin over the XCDs in longest-first order.
+  auto block_map = [&](int tile, std::vector<int32_t> &out) {
+    std::vector<std::vector<int32_t>> seq(kXcds);
+    int64_t item0 = 0, chunk = 0;
+    for (int s : order) {
+      const int64_t nt = (L[s] + tile - 1) / tile;
+      for (int64_t hh = 0; hh < H; ++hh, ++chunk) {
+        auto &q = seq[chunk % kXcds];
+        for (int64_t t = 0; t < nt; ++t) {
+          q.push_back((int32_t)(item0 + t));
+          q.push_back((int32_t)hh);
+        }
+      }
+      item0 += nt;
+    }
+    size_t longest = 0;
+    for (auto &q : seq) longest = std::max(longest, q.size() / 2);
+    out.assign(2 * longest * kXcds, -1);
+    for (int x = 0; x < kXcds; ++x)
+      for (size_t pos = 0; pos < seq[x].size() / 2; ++pos) {
+        out[2 * (pos * kXcds + x) + 0] = seq[x][2 * pos + 0];
+        out[2 * (pos * kXcds + x) + 1] = seq[x][2 * pos + 1];
+      }
+  };
+
+  std::vector<int32_t> fwd_blocks, bwd_blocks;
+  block_map(qt, fwd_blocks);
+  block_map(kt, bwd_blocks);
 
   mmdit_plan p;
   std::memset(&p, 0, sizeof(p));
@@ -120,6 +150,8 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
   p.kv_tile = kt;
   p.num_fwd_items = (int32_t)n_fwd;
   p.num_bwd_items = (int32_t)n_bwd;
+  p.num_fwd_blocks = (int32_t)(fwd_blocks.size() / 2);
+  p.num_bwd_blocks = (int32_t)(bwd_blocks.size() / 2);
   p.rope_rows = rope_rows;
   p.rope_theta = desc->rope_theta;
   p.rms_eps = desc->rms_eps;
@@ -132,6 +164,10 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
   off = align_up(off + 16ull * n_fwd, 256);
   p.off_bwd_items = off;
   off = align_up(off + 16ull * n_bwd, 256);
+  p.off_fwd_blocks = off;
+  off = align_up(off + 4ull * fwd_blocks.size(), 256);
+  p.off_bwd_blocks = off;
+  off = align_up(off + 4ull * bwd_blocks.size(), 256);
   p.off_rope = off;
   off = align_up(off + 8ull * rope_rows * (d / 4), 256);
   p.blob_bytes = off;
@@ -186,6 +222,9 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
   };
   fill_items(reinterpret_cast<int32_t *>(blob + p.off_fwd_items), qt);
   fill_items(reinterpret_cast<int32_t *>(blob + p.off_bwd_items), kt);
+
+  std::memcpy(blob + p.off_fwd_blocks, fwd_blocks.data(), 4 * fwd_blocks.size());
+  std::memcpy(blob + p.off_bwd_blocks, bwd_blocks.data(), 4 * bwd_blocks.size());
 
   // RoPE table: angle pos * theta^(-4j/d), j < d/4, in double, rounded once.
   float *rope = reinterpret_cast<float *>(blob + p.off_rope);

@@ -62,6 +62,31 @@ def _check_plan(inp, dtype_code):
         assert set(map(tuple, it.tolist())) == expect and len(it) == len(expect)
         lens = it[:, 1] - it[:, 0]
         assert np.all(np.diff(lens) <= 0)
+    # workgroup -> (item, head) maps: each pair exactly once; -1 = idle; all
+    # tiles of one (sample, head) on one XCD (workgroup b runs on XCD b % 8),
+    # in tile order
+    for n_items, n_blocks, off_it, off_bl in ((plan.num_fwd_items, plan.num_fwd_blocks,
+                                               plan.off_fwd_items, plan.off_fwd_blocks),
+                                              (plan.num_bwd_items, plan.num_bwd_blocks,
+                                               plan.off_bwd_items, plan.off_bwd_blocks)):
+        it = _blob_section(blob, off_it, 4 * n_items, np.int32).reshape(-1, 4)
+        bl = _blob_section(blob, off_bl, 2 * n_blocks, np.int32).reshape(-1, 2)
+        assert n_blocks % 8 == 0
+        live = bl[bl[:, 0] >= 0]
+        assert np.all(bl[bl[:, 0] < 0] == -1)
+        pairs = set(map(tuple, live.tolist()))
+        assert len(pairs) == len(live) == n_items * H
+        assert pairs == {(i, hh) for i in range(n_items) for hh in range(H)}
+        xcd_of = {}
+        last_pos = {}
+        for b, (i, hh) in enumerate(bl.tolist()):
+            if i < 0:
+                continue
+            key = (int(it[i, 3]), hh)          # (sample, head)
+            assert xcd_of.setdefault(key, b % 8) == b % 8
+            assert last_pos.get(key, (-1, -1))[0] < b   # tiles in order
+            assert it[i, 2] > last_pos.get(key, (-1, -1))[1]
+            last_pos[key] = (b, int(it[i, 2]))
     # RoPE table: cos/sin of pos * theta^(-4j/d), rounded once to fp32
     rope = _blob_section(blob, plan.off_rope, plan.rope_rows * (d // 4) * 2, np.float32)
     rope = rope.reshape(plan.rope_rows, d // 4, 2)
