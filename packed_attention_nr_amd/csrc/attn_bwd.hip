@@ -14,13 +14,17 @@
 //    so P^T and dS^T are per-lane and dS^T feeds dQ^T += K^T dS^T as the B
 //    operand straight from registers; K^T fragments are read transposed from
 //    LDS (ds_read_b64_tr_b16). It also computes and stores D for its queries.
-//  * dK/dV kernel (key-tile items): each wave owns 32 keys with K and V rows
-//    held in registers, loops over the sample's queries 64 at a time, forms
-//    S = Q K^T and dP = dO V^T with one key per lane, and accumulates
-//    dV^T += dO^T P and dK^T += Q^T dS with P and dS as B operands from
-//    registers and dO^T / Q^T read transposed from LDS.
+//  * dK/dV kernel (key-tile items): 128 keys per workgroup, split over two
+//    wave roles that share P through LDS (one holds K rows and produces P and
+//    dV, the other holds V rows and produces dS and dK); they loop over the
+//    sample's queries 64 at a time with one key per lane, forming S = Q K^T
+//    and dP = dO V^T and accumulating dV^T += dO^T P and dK^T += Q^T dS with
+//    P and dS as B operands from registers and dO^T / Q^T read transposed
+//    from a ring of LDS tiles filled by direct global->LDS loads.
 // dQ is recomputed rather than accumulated across key tiles: device-wide
 // fp32 atomics from eight XCDs cost far more than the extra S and dP products.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -85,9 +89,9 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
     const bf16 *os = oo + (int64_t)qc * HD + h * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      qf[s] = as_bf16x8(ld16(qs + 16 * s));
-      gf[s] = as_bf16x8(ld16(gs + 16 * s));
-      const bf16x8 of = as_bf16x8(ld16(os + 16 * s));
+      qf[s] = ld_bf16x8(qs + 16 * s);
+      gf[s] = ld_bf16x8(gs + 16 * s);
+      const bf16x8 of = ld_bf16x8(os + 16 * s);
 #pragma unroll
       for (int j = 0; j < 8; ++j) dlt = fmaf((float)gf[s][j], (float)of[j], dlt);
     }
@@ -157,8 +161,8 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = as_bf16x8(ld16(&Ks[(kb * 32 + lq) * LDK + 16 * ks + 8 * g]));
-        const bf16x8 vf = as_bf16x8(ld16(&Vs[(kb * 32 + lq) * LDV + 16 * ks + 8 * g]));
+        const bf16x8 kf = ld_bf16x8(&Ks[(kb * 32 + lq) * LDK + 16 * ks + 8 * g]);
+        const bf16x8 vf = ld_bf16x8(&Vs[(kb * 32 + lq) * LDV + 16 * ks + 8 * g]);
         s = mfma32(kf, qf[ks], s);
         dp = mfma32(vf, gf[ks], dp);
       }
@@ -203,18 +207,57 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
 
 // ---------------------------------------------------------------------------
 // dK-hat and dV for one 128-key tile of one sample and head.
+//
+// Eight waves in two roles, paired per SIMD (wave w and w+4 share keys
+// 32*(w%4)..+31 and, by the round-robin wave placement, one SIMD):
+//  * P/dV waves hold their 32 K-hat rows as B operands, form S = Q K^T and
+//    P = exp2(S*c - lse2) for a 64-query tile, publish P (bf16, in the MFMA
+//    accumulator order) through LDS and accumulate dV^T += dO^T P;
+//  * dS/dK waves hold their 32 V rows, form dP = dO V^T, read P back, form
+//    dS = P * (dP - D) and accumulate dK^T += Q^T dS.
+// Each tile takes two phases between workgroup barriers; in each phase one
+// role issues matrix instructions while the other does its vector work:
+//   phase 1: P/dV waves: softmax(t) -> P(t) to LDS
+//            dS/dK waves: dK(t-1), dP(t)
+//   phase 2: P/dV waves: dV(t), S(t+1)
+//            dS/dK waves: dS(t) (reads P(t)); load tile t+3
+// Q-hat / dO tiles, lse and D come by direct global->LDS loads into a
+// 4-stage ring; tile t+3 reuses the stage of tile t-1, whose last reader
+// (dK(t-1)) ran before the barrier that opens phase 2 of tile t. Each wave
+// waits for its own loads of tile t+1 before that barrier, so tile t+1 is
+// visible one phase before S(t+1) reads it.
 // ---------------------------------------------------------------------------
+namespace bwd {
+constexpr int KV_NW = 8;   // waves of a dK/dV workgroup
+constexpr int KV_NS = 4;   // Q-hat / dO ring stages
+}  // namespace bwd
+
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(PlanDev p, AttnBwdArgs a) {
+__global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanDev p, AttnBwdArgs a) {
   using namespace bwd;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int QB = BMQ / 32;
-  constexpr int LD = D + PAD_BOTH;    // Q-hat and dO: row reads and transposed reads
-  constexpr int QCH = BMQ * D / 8 / 256;
-  __shared__ __attribute__((aligned(16))) bf16 q_s[2][BMQ * LD];
-  __shared__ __attribute__((aligned(16))) bf16 g_s[2][BMQ * LD];
-  __shared__ float lse_s[2][BMQ], dlt_s[2][BMQ];
+  constexpr int TILE = BMQ * D;
+  static_assert(KV_NS == 4 && BMQ == 64 && KT == 32 * KV_NW / 2, "layout below");
+  // One LDS object per ring stage, [Q-hat tile | dO tile | lse | D]: distinct
+  // objects (at most 8 of them receiving direct loads) let the compiler prove
+  // that loads into one stage do not alias reads of another.
+  constexpr int STAGE = 2 * TILE + 4 * BMQ;  // bf16 elements
+  __shared__ __attribute__((aligned(16))) bf16 st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
+  __shared__ __attribute__((aligned(16))) uint4 p_s[4 * (BMQ / 16) * 64];
+  auto stg = [&](auto stage) __attribute__((always_inline)) -> bf16 * {
+    constexpr int S = decltype(stage)::value;
+    if constexpr (S == 0) return st0; else if constexpr (S == 1) return st1;
+    else if constexpr (S == 2) return st2; else return st3;
+  };
+  auto qst = [&](auto stage) __attribute__((always_inline)) -> bf16 * { return stg(stage); };
+  auto gst = [&](auto stage) __attribute__((always_inline)) -> bf16 * { return stg(stage) + TILE; };
+  auto lst = [&](auto stage) __attribute__((always_inline)) -> float * {
+    return reinterpret_cast<float *>(stg(stage) + 2 * TILE);
+  };
+  auto dst = [&](auto stage) __attribute__((always_inline)) -> float * {
+    return reinterpret_cast<float *>(stg(stage) + 2 * TILE) + BMQ;
+  };
 
   const int H = p.num_heads;
   const int N = p.total_tokens;
@@ -223,160 +266,209 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(PlanDev p, AttnBw
   const int h = wb.y;
   const int4 it = p.bwd_items[wb.x];
   const int seg0 = it.x, seg1 = it.y, k0 = it.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform to the compiler
+  const int role = wave >> 2, sub = wave & 3;  // role 0: P/dV, role 1: dS/dK
   const int lq = lane & 31, g = lane >> 5;
   const int64_t HD = (int64_t)H * D;
-  const bf16 *qh = static_cast<const bf16 *>(a.q_hat);
-  const bf16 *kh = static_cast<const bf16 *>(a.k_hat);
-  const bf16 *vv = static_cast<const bf16 *>(a.v);
-  const bf16 *go = static_cast<const bf16 *>(a.dout);
+  const int64_t gstride = a.dout_stride;
+  const bf16 *qh = static_cast<const bf16 *>(a.q_hat) + h * D;
+  const bf16 *go = static_cast<const bf16 *>(a.dout) + h * D;
+  const float *lse_h = a.lse + (int64_t)h * N;
+  const float *dlt_h = a.delta + (int64_t)h * N;
   const float c2 = a.scale_log2;
 
-  // This lane's key: K-hat and V rows as B operands.
-  const int kr = k0 + wave * 32 + lq;
+  // This lane's key: its K-hat row (P/dV role) or V row (dS/dK role) as a
+  // B operand.
+  const int kr = k0 + sub * 32 + lq;
   const bool key_ok = kr < seg1;
   const int kc = min(kr, seg1 - 1);
-  bf16x8 kf[KS], vf[KS];
+  bf16x8 kv[KS];
   {
-    const bf16 *ks = kh + (int64_t)kc * HD + h * D + 8 * g;
-    const bf16 *vs = vv + (int64_t)kc * a.v_stride + h * D + 8 * g;
+    const bf16 *src = role == 0 ? static_cast<const bf16 *>(a.k_hat) + (int64_t)kc * HD + h * D
+                                : static_cast<const bf16 *>(a.v) + (int64_t)kc * a.v_stride + h * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kf[s] = as_bf16x8(ld16(ks + 16 * s));
-      vf[s] = as_bf16x8(ld16(vs + 16 * s));
-    }
+    for (int s = 0; s < KS; ++s) kv[s] = ld_bf16x8(src + 16 * s + 8 * g);
   }
 
-  // Q-hat / dO tile staging: thread tid moves chunk c8 of rows r0 + RSTEP*c;
-  // rows clamped into the segment only in its last tile.
-  constexpr int RSTEP = 256 / (D / 8);
-  const int r0 = tid / (D / 8), c8 = tid % (D / 8);
-  const bf16 *qbase = qh + (int64_t)r0 * HD + h * D + 8 * c8;
-  const bf16 *gbase = go + (int64_t)r0 * a.dout_stride + h * D + 8 * c8;
-  uint4 qreg[QCH], greg[QCH];
-  float lreg = 0.f, dreg = 0.f;
-  auto load_q = [&](int qb0) {
-    if (qb0 + BMQ <= seg1) {
-      const bf16 *qp = qbase + (int64_t)qb0 * HD;
-      const bf16 *gp = gbase + (int64_t)qb0 * a.dout_stride;
-#pragma unroll
-      for (int c = 0; c < QCH; ++c) {
-        qreg[c] = ld16(qp + (int64_t)(RSTEP * c) * HD);
-        greg[c] = ld16(gp + (int64_t)(RSTEP * c) * a.dout_stride);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < QCH; ++c) {
-        const int qq = min(qb0 + r0 + RSTEP * c, seg1 - 1);
-        qreg[c] = ld16(qh + (int64_t)qq * HD + h * D + 8 * c8);
-        greg[c] = ld16(go + (int64_t)qq * a.dout_stride + h * D + 8 * c8);
-      }
-    }
-    if (tid < BMQ) {
-      const int qq = qb0 + tid;
-      const bool ok = qq < seg1;
-      const int qcl = min(qq, seg1 - 1);
-      // Queries past the segment end get lse = +inf, so their P is exactly 0.
-      lreg = ok ? a.lse[(int64_t)h * N + qcl] * kLog2e : INFINITY;
-      dreg = a.delta[(int64_t)h * N + qcl];
-    }
+  const int ntq = (seg1 - seg0 + BMQ - 1) / BMQ;
+  TileLoader<D, SWZ_ROWS, BMQ, KV_NW> qload, gload;
+  qload.init(wave, lane);
+  gload.init(wave, lane);
+  constexpr int LQ = TileLoader<D, SWZ_ROWS, BMQ, KV_NW>::LOADS;
+  // Tile t -> ring stage; even waves also load lse and odd waves D (the same
+  // words from four waves each, so every wave issues the same number of loads
+  // per tile). Rows past the segment end are clamped to its last row; their P
+  // is zeroed.
+  const float *ld_src = (wave & 1) ? dlt_h : lse_h;
+  // Every step issues one tile's loads, so the compiler's in-order count of
+  // outstanding loads is exact; past the last tile the last tile is loaded
+  // again into the stage just freed, which nothing reads afterwards.
+  auto issue = [&](auto stage, int t) __attribute__((always_inline)) {
+    const int qb0 = seg0 + min(t, ntq - 1) * BMQ;
+    qload.issue_clamped(qst(stage), qh, HD, qb0, seg1 - 1);  // branch-free: exact load counts
+    gload.issue_clamped(gst(stage), go, gstride, qb0, seg1 - 1);
+    g2lds4(ld_src + min(qb0 + lane, seg1 - 1), lst(stage) + (wave & 1) * BMQ);
   };
-  auto store_q = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < QCH; ++c) {
-      st16(&q_s[buf][(r0 + RSTEP * c) * LD + 8 * c8], qreg[c]);
-      st16(&g_s[buf][(r0 + RSTEP * c) * LD + 8 * c8], greg[c]);
-    }
-    if (tid < BMQ) {
-      lse_s[buf][tid] = lreg;
-      dlt_s[buf][tid] = dreg;
-    }
-  };
+  constexpr int PER_TILE = 2 * LQ + 1;  // loads per wave per tile
 
-  f32x16 dk[DB], dv[DB];
+  f32x16 acc[DB];  // dV^T (role 0) or dK^T (role 1): lane = key, rows = d
 #pragma unroll
   for (int b = 0; b < DB; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk[b][i] = 0.f;
-      dv[b][i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+  f32x16 s[2];     // S (role 0) or dP (role 1) of 64 queries x this lane's key
+  bf16x8 pb[BMQ / 16];  // P (role 0) or dS (role 1) as B operands, 16 queries each
+  uint4 *p_mine = p_s + sub * (BMQ / 16) * 64 + lane;
 
-  const int nit = (seg1 - seg0 + BMQ - 1) / BMQ;
-  load_q(seg0);
-  store_q(0);
-  __syncthreads();
-
-  for (int itq = 0; itq < nit; ++itq) {
-    const int buf = itq & 1;
-    const int qb0 = seg0 + itq * BMQ;
-    if (itq + 1 < nit) load_q(qb0 + BMQ);
-    const bf16 *Qs = q_s[buf];
-    const bf16 *Gs = g_s[buf];
-
-    bf16x8 pb[BMQ / 16], db[BMQ / 16];   // P and dS as B operands (16 queries each)
+  // Row products with this lane's key: s[qb] = rows(qb) . kv (Q-hat rows for
+  // role 0, dO rows for role 1).
+  auto rows_x_key = [&](const bf16 *T) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 s, dp;
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
-      }
+      for (int i = 0; i < 16; ++i) s[qb][i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 qa = as_bf16x8(ld16(&Qs[(qb * 32 + lq) * LD + 16 * ks + 8 * g]));
-        const bf16x8 ga = as_bf16x8(ld16(&Gs[(qb * 32 + lq) * LD + 16 * ks + 8 * g]));
-        s = mfma32(qa, kf[ks], s);
-        dp = mfma32(ga, vf[ks], dp);
+        const bf16x8 ra = ld_bf16x8(&T[swz_off<D, SWZ_ROWS>(qb * 32 + lq, 16 * ks + 8 * g)]);
+        s[qb] = mfma32(ra, kv[ks], s[qb]);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ql = qb * 32 + acc_row(i, g);
-        // Keys past the segment end only feed their own dK/dV rows, which are
-        // never stored: no mask needed here.
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse_s[buf][ql]));
-        s[i] = pv;
-        dp[i] = pv * (dp[i] - dlt_s[buf][ql]);
-      }
-      pb[2 * qb] = acc_to_bf16(s, 0);
-      pb[2 * qb + 1] = acc_to_bf16(s, 8);
-      db[2 * qb] = acc_to_bf16(dp, 0);
-      db[2 * qb + 1] = acc_to_bf16(dp, 8);
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (queries as the k dimension).
+  };
+  // acc^T += T^T pb (dO^T P for role 0, Q-hat^T dS for role 1).
+  auto accumulate = [&](const bf16 *T) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < BMQ / 16; ++t)
+    for (int u = 0; u < BMQ / 16; ++u)
 #pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const bf16x8 gt = lds_read_tr(Gs, LD, t * 16, b * 32, lane);
-        dv[b] = mfma32(gt, pb[t], dv[b]);
-        const bf16x8 qt = lds_read_tr(Qs, LD, t * 16, b * 32, lane);
-        dk[b] = mfma32(qt, db[t], dk[b]);
+      for (int b = 0; b < DB; ++b)
+        acc[b] = mfma32(lds_read_tr_swz<D, SWZ_ROWS>(T, u * 16, b * 32, lane), pb[u], acc[b]);
+  };
+  // Role 0: P = exp2(S*c2 - lse*log2e), zero for queries past the segment.
+  auto softmax = [&](const float *Ls, int t) __attribute__((always_inline)) {
+    const int qb0 = seg0 + t * BMQ;
+    const bool tail = qb0 + BMQ > seg1;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&Ls[qb * 32 + 8 * r4 + 4 * g]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * r4 + j;
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[qb][i], c2, -l4[j] * kLog2e));
+          if (tail && qb0 + qb * 32 + acc_row(i, g) >= seg1) pv = 0.f;
+          s[qb][i] = pv;
+        }
       }
-    if (itq + 1 < nit) store_q(buf ^ 1);
-    __syncthreads();
+      pb[2 * qb] = acc_to_bf16(s[qb], 0);
+      pb[2 * qb + 1] = acc_to_bf16(s[qb], 8);
+    }
+#pragma unroll
+    for (int u = 0; u < BMQ / 16; ++u) st_bf16x8(p_mine + u * 64, pb[u]);
+  };
+  // Role 1: dS = P * (dP - D) with P read back from the paired wave.
+  auto dscores = [&](const float *Ds) __attribute__((always_inline)) {
+    bf16x8 pr[BMQ / 16];
+#pragma unroll
+    for (int u = 0; u < BMQ / 16; ++u) pr[u] = ld_bf16x8(p_mine + u * 64);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&Ds[qb * 32 + 8 * r4 + 4 * g]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * r4 + j;
+          const float pv = (float)pr[2 * qb + i / 8][i % 8];
+          s[qb][i] = pv * (s[qb][i] - d4[j]);
+        }
+      }
+      pb[2 * qb] = acc_to_bf16(s[qb], 0);
+      pb[2 * qb + 1] = acc_to_bf16(s[qb], 8);
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  issue(S0{}, 0);
+  issue(std::integral_constant<int, 1>{}, 1);
+  issue(std::integral_constant<int, 2>{}, 2);
+  wait_vmem_le<2 * PER_TILE>();  // this wave's loads of tile 0
+  phase_barrier();  // tile 0 visible
+
+  // Both roles run the same whole number of 4-step groups (every step loads,
+  // waits and passes two barriers; work is skipped past the last tile), so the
+  // loop has a single exit and barrier counts match across roles.
+  if (role == 0) {
+    rows_x_key(qst(S0{}));  // S(0)
+    auto step = [&](auto stage, int t) __attribute__((always_inline)) {
+      constexpr int SG = decltype(stage)::value;
+      if (t < ntq) softmax(lst(stage), t);
+      wait_vmem_le<PER_TILE>();  // this wave's loads of tile t+1
+      phase_barrier();  // P(t) and tile t+1 visible
+      issue(std::integral_constant<int, (SG + 3) % KV_NS>{}, t + 3);
+      if (t < ntq) {
+        accumulate(gst(stage));  // dV(t)
+        if (t + 1 < ntq) rows_x_key(qst(std::integral_constant<int, (SG + 1) % KV_NS>{}));  // S(t+1)
+      }
+      phase_barrier();  // P(t) consumed
+    };
+    for (int t = 0; t < ntq; t += KV_NS) {
+      step(S0{}, t);
+      step(std::integral_constant<int, 1>{}, t + 1);
+      step(std::integral_constant<int, 2>{}, t + 2);
+      step(std::integral_constant<int, 3>{}, t + 3);
+    }
+  } else {
+    auto step = [&](auto stage, int t) __attribute__((always_inline)) {
+      constexpr int SG = decltype(stage)::value;
+      if (t < ntq) {
+        if (t > 0) accumulate(qst(std::integral_constant<int, (SG + 3) % KV_NS>{}));  // dK(t-1)
+        rows_x_key(gst(stage));  // dP(t)
+      }
+      wait_vmem_le<PER_TILE>();  // this wave's loads of tile t+1
+      phase_barrier();  // P(t) and tile t+1 visible
+      issue(std::integral_constant<int, (SG + 3) % KV_NS>{}, t + 3);
+      if (t < ntq) {
+        dscores(dst(stage));  // dS(t)
+        if (t + 1 == ntq) accumulate(qst(stage));  // last dK
+      }
+      phase_barrier();  // P(t) consumed
+    };
+    for (int t = 0; t < ntq; t += KV_NS) {
+      step(S0{}, t);
+      step(std::integral_constant<int, 1>{}, t + 1);
+      step(std::integral_constant<int, 2>{}, t + 2);
+      step(std::integral_constant<int, 3>{}, t + 3);
+    }
   }
+
+  wait_vmem();  // no load into LDS may outlive the workgroup
 
   // Rows of this lane's key: register i of block b is d = 32b + acc_row(i, g).
   if (key_ok) {
     const int64_t off = (int64_t)kr * HD + h * D;
-    bf16 *dvp = static_cast<bf16 *>(a.dv) + off;
-    float *dkp = a.dk_acc + off;
+    if (role == 0) {
+      bf16 *dvp = static_cast<bf16 *>(a.dv) + off;
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+      for (int b = 0; b < DB; ++b)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int e = b * 32 + 8 * r4 + 4 * g;
-        bf16x4 v4;
-        const bf16x2 t0 = pack2(dv[b][4 * r4], dv[b][4 * r4 + 1]);
-        const bf16x2 t1 = pack2(dv[b][4 * r4 + 2], dv[b][4 * r4 + 3]);
-        v4[0] = t0[0]; v4[1] = t0[1]; v4[2] = t1[0]; v4[3] = t1[1];
-        *reinterpret_cast<bf16x4 *>(dvp + e) = v4;
-        *reinterpret_cast<float4 *>(dkp + e) =
-            make_float4(dk[b][4 * r4] * a.scale, dk[b][4 * r4 + 1] * a.scale,
-                        dk[b][4 * r4 + 2] * a.scale, dk[b][4 * r4 + 3] * a.scale);
-      }
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x4 v4;
+          const bf16x2 t0 = pack2(acc[b][4 * r4], acc[b][4 * r4 + 1]);
+          const bf16x2 t1 = pack2(acc[b][4 * r4 + 2], acc[b][4 * r4 + 3]);
+          v4[0] = t0[0]; v4[1] = t0[1]; v4[2] = t1[0]; v4[3] = t1[1];
+          *reinterpret_cast<bf16x4 *>(dvp + b * 32 + 8 * r4 + 4 * g) = v4;
+        }
+    } else {
+      float *dkp = a.dk_acc + off;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<float4 *>(dkp + b * 32 + 8 * r4 + 4 * g) =
+              make_float4(acc[b][4 * r4] * a.scale, acc[b][4 * r4 + 1] * a.scale,
+                          acc[b][4 * r4 + 2] * a.scale, acc[b][4 * r4 + 3] * a.scale);
+    }
   }
 }
 
@@ -389,7 +481,7 @@ static hipError_t bwd_dq(const PlanDev &p, const AttnBwdArgs &a, hipStream_t s) 
 }
 template <int D>
 static hipError_t bwd_dkdv(const PlanDev &p, const AttnBwdArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)p.num_bwd_blocks), dim3(256), 0, s, p, a);
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)p.num_bwd_blocks), dim3(64 * bwd::KV_NW), 0, s, p, a);
   return hipGetLastError();
 }
 

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
   {
     const bf16 *src = qh + (int64_t)qc * HD + h * D + 8 * g;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = as_bf16x8(ld16(src + 16 * s));
+    for (int s = 0; s < KS; ++s) qf[s] = ld_bf16x8(src + 16 * s);
   }
 
   const int ntiles = (seg1 - seg0 + BN - 1) / BN;
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = as_bf16x8(ld16(&Ks[swz_off<D, SWZ_ROWS>(kb * 32 + lq, 16 * ks + 8 * g)]));
+        const bf16x8 kf = ld_bf16x8(&Ks[swz_off<D, SWZ_ROWS>(kb * 32 + lq, 16 * ks + 8 * g)]);
         s[kb] = mfma32(kf, qf[ks], s[kb]);
       }
     }

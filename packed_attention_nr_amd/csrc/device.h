@@ -28,17 +28,27 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
 
-// 16-byte global / LDS accesses.
+// 16-byte global / LDS accesses, as single vector loads and stores (a HIP
+// uint4 struct copy splits into four 4-byte accesses in the IR).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 template <typename T>
 __device__ __forceinline__ uint4 ld16(const T *p) {
-  return *reinterpret_cast<const uint4 *>(p);
+  return __builtin_bit_cast(uint4, *reinterpret_cast<const u32x4 *>(p));
 }
 template <typename T>
 __device__ __forceinline__ void st16(T *p, uint4 v) {
-  *reinterpret_cast<uint4 *>(p) = v;
+  *reinterpret_cast<u32x4 *>(p) = __builtin_bit_cast(u32x4, v);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16-byte load straight into an MFMA operand (no struct round trip, so the
+// load stays one vector access).
+template <typename T>
+__device__ __forceinline__ bf16x8 ld_bf16x8(const T *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ void st_bf16x8(void *p, bf16x8 v) { *reinterpret_cast<bf16x8 *>(p) = v; }
 __device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
 
 // fp32 -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
@@ -129,10 +139,27 @@ __device__ __forceinline__ void g2lds16(const void *src, void *lds_wave_base) {
                                    (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
 }
 
+// 4-byte global -> LDS copy for every lane: lane l's word lands at
+// lds_wave_base + 4*l.
+__device__ __forceinline__ void g2lds4(const void *src, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)lds_wave_base, 4, 0, 0);
+}
+
 // Wait until this wave's outstanding global (and global->LDS) loads are done.
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector memory loads are outstanding.
+// Loads complete in issue order, so this waits for all but the newest N.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
   asm volatile("" ::: "memory");
 }
 

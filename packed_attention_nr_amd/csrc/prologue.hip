@@ -25,7 +25,7 @@ template <>
 struct Vec<bf16> {
   static constexpr int N = 8;
   __device__ static void load(const bf16 *p, float *x) {
-    bf16x8 v = as_bf16x8(ld16(p));
+    bf16x8 v = ld_bf16x8(p);
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
   }
