@@ -4,9 +4,10 @@
 
 One step = one pass of the whole path over one synthetic pack: the host pack
 plan and its upload, the forward (QK-norm + 2D RoPE prologue, var-len
-attention) and the backward (D = rowsum(dO*O), var-len attention backward,
-prologue backward with gain gradients). HIP events recorded on the launch
-stream between the stages give each kernel's duration inside the timed region.
+attention) and the backward (D = rowsum(dO*O), var-len attention backward
+with the prologue backward fused into its epilogues, gain-gradient reduction).
+HIP events recorded on the launch stream between the stages give each
+kernel's duration inside the timed region.
 Prints one JSON line.
 
 metric: bf16 forward+backward attention throughput in TFLOP/s, counting
@@ -136,7 +137,7 @@ def main():
         rec(3)
         pam.mmdit_attn_bwd(plan, bd, stages=B["dkdv"], **ba)
         rec(4)
-        pam.mmdit_attn_bwd(plan, bd, stages=B["prologue"], **ba)
+        pam.mmdit_attn_bwd(plan, bd, stages=B["gains"], **ba)
         rec(5)
 
     for i in range(args.warmup):
@@ -149,7 +150,7 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
-    names = ["prologue_fwd", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv", "prologue_bwd"]
+    names = ["prologue_fwd", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv", "gain_reduce"]
     kt = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
           for j, n in enumerate(names)}
     value = (fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12

@@ -123,9 +123,11 @@ mmdit_status mmdit_pack_plan(const mmdit_pack_desc *desc, mmdit_plan *plan,
  * reads the caller's q_hat / k_hat). */
 #define MMDIT_STAGE_PROLOGUE      1u  /* fwd: RMSNorm + RoPE of Q and K -> q_hat, k_hat */
 #define MMDIT_STAGE_ATTENTION     2u  /* fwd: var-len attention -> o, lse */
-#define MMDIT_STAGE_BWD_DQ        1u  /* bwd: D = rowsum(dO * O) and dQ-hat (fp32 workspace) */
-#define MMDIT_STAGE_BWD_DKDV      2u  /* bwd: dK-hat (fp32 workspace) and dV; reads D */
-#define MMDIT_STAGE_BWD_PROLOGUE  4u  /* bwd: inverse RoPE + RMSNorm backward -> dq, dk, dgains */
+#define MMDIT_STAGE_BWD_DQ        1u  /* bwd: D = rowsum(dO * O), dQ-hat, inverse RoPE + RMSNorm
+                                         backward -> dq, Q gain partials (workspace) */
+#define MMDIT_STAGE_BWD_DKDV      2u  /* bwd: dK-hat and dV (reads D), inverse RoPE + RMSNorm
+                                         backward -> dk, dv, K gain partials (workspace) */
+#define MMDIT_STAGE_BWD_GAINS     4u  /* bwd: fixed-order sum of the gain partials -> dgains */
 
 typedef struct {
   const void *q, *k, *v;              /* [N][H][d] device, dtype; pre-norm */
@@ -162,10 +164,14 @@ typedef struct {
 } mmdit_bwd_args;
 
 /* Backward of mmdit_attn_fwd for the loss sum(dout * o). workspace_bytes >=
- * plan->bwd_workspace_bytes. Workspace layout after the call (fp32, each part
- * 256-byte aligned): dQ-hat [N][H][d] at offset 0, dK-hat [N][H][d] after it,
- * then D [H][N], then the gain-gradient partials. Deterministic: the same
- * inputs give bitwise the same outputs (no atomics; fixed-order reductions). */
+ * plan->bwd_workspace_bytes. Workspace layout (fp32, each part 256-byte
+ * aligned): D [H][N] at offset 0, then the Q and K gain-gradient partials;
+ * fp32 plans also keep fp32 dQ-hat and dK-hat [N][H][d] after them. A stage
+ * subset may run per call: DQ before DKDV (which reads D), both before GAINS
+ * (which reads their partials) on the same workspace. Stage DQ needs o, q,
+ * dq; DKDV needs k, dk, dv; both need q_hat, k_hat, v, dout, lse, gains.
+ * Deterministic: the same inputs give bitwise the same outputs (no atomics;
+ * fixed-order reductions). */
 mmdit_status mmdit_attn_bwd(const mmdit_plan *plan, const void *plan_blob_dev,
                             const mmdit_bwd_args *args, void *workspace,
                             uint64_t workspace_bytes, void *hip_stream);

@@ -27,9 +27,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmmdit.so
 
 MMDIT_F32, MMDIT_BF16 = 0, 1
 STAGE_PROLOGUE, STAGE_ATTENTION = 1, 2
-STAGE_BWD_DQ, STAGE_BWD_DKDV, STAGE_BWD_PROLOGUE = 1, 2, 4
+STAGE_BWD_DQ, STAGE_BWD_DKDV, STAGE_BWD_GAINS = 1, 2, 4
 FWD_STAGES = {"prologue": STAGE_PROLOGUE, "attention": STAGE_ATTENTION}
-BWD_STAGES = {"dq": STAGE_BWD_DQ, "dkdv": STAGE_BWD_DKDV, "prologue": STAGE_BWD_PROLOGUE}
+BWD_STAGES = {"dq": STAGE_BWD_DQ, "dkdv": STAGE_BWD_DKDV, "gains": STAGE_BWD_GAINS}
 
 
 class PackDesc(C.Structure):
@@ -195,7 +195,7 @@ def _torch_dtype(dtype: int):
 def _token_stride(t, N, H, d, name):
     if t.dim() != 3 or tuple(t.shape) != (N, H, d):
         raise ValueError(f"{name} must have shape ({N}, {H}, {d}), got {tuple(t.shape)}")
-    if t.stride(2) != 1 or t.stride(1) != d:
+    if t.stride(2) != 1 or (H > 1 and t.stride(1) != d):  # a lone head's stride is immaterial
         raise ValueError(f"{name}: heads and head_dim must be contiguous")
     return t.stride(0)
 

@@ -182,24 +182,26 @@ static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmd
   mmdit_status st = check_plan(plan, blob);
   if (st) return st;
   if (!a) return fail(MMDIT_ERR_INVALID_ARG, "args must not be NULL");
-  const uint32_t all = MMDIT_STAGE_BWD_DQ | MMDIT_STAGE_BWD_DKDV | MMDIT_STAGE_BWD_PROLOGUE;
+  const uint32_t all = MMDIT_STAGE_BWD_DQ | MMDIT_STAGE_BWD_DKDV | MMDIT_STAGE_BWD_GAINS;
   const uint32_t stages = a->stages ? a->stages : all;
   if (stages & ~all) return fail(MMDIT_ERR_INVALID_ARG, "unknown backward stage bits 0x%x", stages);
   const bool sdq = stages & MMDIT_STAGE_BWD_DQ, skv = stages & MMDIT_STAGE_BWD_DKDV,
-             pro = stages & MMDIT_STAGE_BWD_PROLOGUE;
+             sgn = stages & MMDIT_STAGE_BWD_GAINS;
   const int64_t N = plan->total_tokens, H = plan->num_heads, d = plan->head_dim, HD = H * d;
-  const int elt = plan->dtype == MMDIT_BF16 ? 2 : 4;
+  const bool f32 = plan->dtype == MMDIT_F32;
+  const int elt = f32 ? 4 : 2;
   if (!ws || !aligned16(ws))
     return fail(MMDIT_ERR_INVALID_ARG, "workspace must be a non-NULL 16-byte aligned device pointer");
   if (ws_bytes < plan->bwd_workspace_bytes)
     return fail(MMDIT_ERR_BUFFER_TOO_SMALL, "backward workspace needs %llu bytes, got %llu",
                 (unsigned long long)plan->bwd_workspace_bytes, (unsigned long long)ws_bytes);
+  const BwdLayout wl = bwd_layout(*plan);
   char *w = static_cast<char *>(ws);
-  float *dq_acc = reinterpret_cast<float *>(w);
-  float *dk_acc = reinterpret_cast<float *>(w + align256((uint64_t)N * HD * 4));
-  float *delta = reinterpret_cast<float *>(w + 2 * align256((uint64_t)N * HD * 4));
-  float *partials = reinterpret_cast<float *>(w + 2 * align256((uint64_t)N * HD * 4) + align256(4ull * H * N));
-  const int nblocks = (int)bwd_partial_blocks(N);
+  float *delta = reinterpret_cast<float *>(w + wl.delta);
+  float *part_q = reinterpret_cast<float *>(w + wl.part_q);
+  float *part_k = reinterpret_cast<float *>(w + wl.part_k);
+  float *dq_acc = f32 ? reinterpret_cast<float *>(w + wl.dq_acc) : nullptr;
+  float *dk_acc = f32 ? reinterpret_cast<float *>(w + wl.dk_acc) : nullptr;
 
   std::vector<Span> spans;
   spans.push_back(Span{"workspace", reinterpret_cast<uintptr_t>(ws),
@@ -211,35 +213,36 @@ static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmd
   if (sdq || skv) {
     if ((st = check_ptr("q_hat", a->q_hat)) || (st = check_ptr("k_hat", a->k_hat)) ||
         (st = check_tensor("v", a->v, a->v_stride, HD)) ||
-        (st = check_tensor("dout", a->dout, a->dout_stride, HD)) || (st = check_ptr("lse", a->lse)))
+        (st = check_tensor("dout", a->dout, a->dout_stride, HD)) || (st = check_ptr("lse", a->lse)) ||
+        (st = check_ptr("gains", a->gains)))
       return st;
     spans.push_back(span("q_hat", a->q_hat, N, HD, HD, elt, false));
     spans.push_back(span("k_hat", a->k_hat, N, HD, HD, elt, false));
     spans.push_back(span("v", a->v, N, a->v_stride, HD, elt, false));
     spans.push_back(span("dout", a->dout, N, a->dout_stride, HD, elt, false));
     spans.push_back(span("lse", a->lse, H, N, N, 4, false));
-  }
-  if (skv) {
-    if ((st = check_ptr("dv", a->dv))) return st;
-    spans.push_back(span("dv", a->dv, N, HD, HD, elt, true));
-  }
-  if (pro) {
-    if ((st = check_tensor("q", a->q, a->q_stride, HD)) || (st = check_tensor("k", a->k, a->k_stride, HD)) ||
-        (st = check_ptr("gains", a->gains)) || (st = check_ptr("dq", a->dq)) || (st = check_ptr("dk", a->dk)))
-      return st;
-    spans.push_back(span("q", a->q, N, a->q_stride, HD, elt, false));
-    spans.push_back(span("k", a->k, N, a->k_stride, HD, elt, false));
     spans.push_back(span("gains", a->gains, 4, d, d, 4, false));
-    spans.push_back(span("dq", a->dq, N, HD, HD, elt, true));
-    spans.push_back(span("dk", a->dk, N, HD, HD, elt, true));
     if (a->rstd) {
       if ((st = check_ptr("rstd", a->rstd))) return st;
       spans.push_back(span("rstd", a->rstd, 2 * N, H, H, 4, false));
     }
-    if (a->dgains) {
-      if ((st = check_ptr("dgains", a->dgains))) return st;
-      spans.push_back(span("dgains", a->dgains, 4, d, d, 4, true));
-    }
+  }
+  if (sdq) {
+    if ((st = check_tensor("q", a->q, a->q_stride, HD)) || (st = check_ptr("dq", a->dq))) return st;
+    spans.push_back(span("q", a->q, N, a->q_stride, HD, elt, false));
+    spans.push_back(span("dq", a->dq, N, HD, HD, elt, true));
+  }
+  if (skv) {
+    if ((st = check_tensor("k", a->k, a->k_stride, HD)) || (st = check_ptr("dk", a->dk)) ||
+        (st = check_ptr("dv", a->dv)))
+      return st;
+    spans.push_back(span("k", a->k, N, a->k_stride, HD, elt, false));
+    spans.push_back(span("dk", a->dk, N, HD, HD, elt, true));
+    spans.push_back(span("dv", a->dv, N, HD, HD, elt, true));
+  }
+  if (sgn && a->dgains) {
+    if ((st = check_ptr("dgains", a->dgains))) return st;
+    spans.push_back(span("dgains", a->dgains, 4, d, d, 4, true));
   }
   if ((st = check_aliasing(spans))) return st;
 
@@ -248,20 +251,27 @@ static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmd
   const float scale = (float)(1.0 / std::sqrt((double)d));
   AttnBwdArgs ba{a->q_hat, a->k_hat, a->v, a->dout, a->o, a->v_stride, a->dout_stride, a->lse,
                  delta, dq_acc, dk_acc, a->dv, (float)(1.4426950408889634 / std::sqrt((double)d)),
-                 scale};
+                 scale, a->q, a->k, a->q_stride, a->k_stride, a->gains, a->rstd, a->dq, a->dk,
+                 part_q, part_k};
   if (sdq) {
     hipError_t e = launch_attn_bwd(plan->dtype, pd, ba, 0, s);
+    if (e == hipSuccess && f32) {
+      const PrologueBwdArgs pa{a->q, a->q_stride, a->gains, a->rstd, dq_acc, a->dq, part_q, 0, wl.nq};
+      e = launch_prologue_bwd(plan->dtype, pd, pa, s);
+    }
     if (e != hipSuccess) return hip_fail("attention backward (dQ)", e);
   }
   if (skv) {
     hipError_t e = launch_attn_bwd(plan->dtype, pd, ba, 1, s);
+    if (e == hipSuccess && f32) {
+      const PrologueBwdArgs pa{a->k, a->k_stride, a->gains, a->rstd, dk_acc, a->dk, part_k, 1, wl.nk};
+      e = launch_prologue_bwd(plan->dtype, pd, pa, s);
+    }
     if (e != hipSuccess) return hip_fail("attention backward (dK, dV)", e);
   }
-  if (pro) {
-    PrologueBwdArgs pa{a->q, a->k, a->q_stride, a->k_stride, a->gains, a->rstd, dq_acc, dk_acc,
-                       a->dq, a->dk, partials, a->dgains, nblocks};
-    hipError_t e = launch_prologue_bwd(plan->dtype, pd, pa, s);
-    if (e != hipSuccess) return hip_fail("prologue backward", e);
+  if (sgn && a->dgains) {
+    hipError_t e = launch_gain_reduce(part_q, wl.nq, part_k, wl.nk, (int)d, a->dgains, s);
+    if (e != hipSuccess) return hip_fail("gain-gradient reduction", e);
   }
   return MMDIT_OK;
 }

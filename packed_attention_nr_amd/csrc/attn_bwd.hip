@@ -47,6 +47,161 @@ constexpr float kLog2e = 1.4426950408889634f;
 static_assert(bwd::QT == kFwdTileBf16 && bwd::KT == kBwdTile, "backward tiles must match the plan");
 
 // ---------------------------------------------------------------------------
+// Backward of the prologue, fused into the attention kernels' epilogues (the
+// per-modality RMSNorm with a learned gain and the 2D RoPE of image tokens,
+// picx.dev "Mage-Flow ...", section "Native-Resolution MMDiT (NR-MMDiT)";
+// fused as the section "Training Infrastructure" describes). With
+// y = rho * g_m * x (rho = 1/sqrt(mean(x^2) + eps)) and x-hat = R(phi) y:
+//   dy = R(-phi) dx-hat,   dx = rho g_m dy - rho^3/d (sum_j g_mj dy_j x_j) x,
+//   dg_m += rho dy x  (summed over tokens and heads).
+// The gradient rows are in the 32x32 accumulator layout: lane (lq, g) holds
+// dX-hat / scale of its token at d = 32b + acc_row(i, g) in acc[b][i], the
+// other half of the row in lane lq + 32(1-g). The inputs the epilogue needs
+// are fetched early (token words and rstd in registers, gains and, where LDS
+// allows, the pre-norm rows in LDS) so that it costs at most one round trip
+// to memory.
+// ---------------------------------------------------------------------------
+// Inputs of one lane's row: meta = the token's tok_meta word, rho = its
+// rstd (negative: recompute from x), xa(d0) = its pre-norm elements d0..d0+3
+// (from LDS or global), g2 = the two gain rows of this input (text, image;
+// LDS), out = the row's element offset in the dense output. Writes dx (bf16) for a valid row and
+// leaves in red[m * D + d] (m = 0 text, 1 image) this wave's sums of
+// rho*dy*x over its 32 tokens (invalid rows add nothing).
+template <int D, typename XA>
+__device__ __forceinline__ void prologue_bwd_rows(const f32x16 (&acc)[D / 32], float scale, int32_t meta,
+                                                  float rho, bool valid, const XA &xa, const float *g2,
+                                                  const float2 *rope, float eps, bf16 *dx, int64_t out,
+                                                  float *red, int lane) {
+  constexpr int DB = D / 32, Q4 = D / 4;
+  const int lq = lane & 31, g = lane >> 5;
+  bool img;
+  int row, col;
+  tok_pos(meta, img, row, col);
+  const float *gm = g2 + (img ? D : 0);
+  float dy[DB][16], xv[DB][16];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dy[b][i] = acc[b][i] * scale;
+  if (img) {  // inverse rotation of the pairs (d, d+1), d even
+    float2 cs[DB][8];
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int pair = 16 * b + 4 * (k >> 1) + 2 * g + (k & 1);
+        const int half = pair >= Q4;
+        cs[b][k] = rope[(half ? col : row) * Q4 + pair - half * Q4];
+      }
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i0 = 2 * k;
+        const float u = dy[b][i0], w = dy[b][i0 + 1];
+        dy[b][i0] = u * cs[b][k].x + w * cs[b][k].y;
+        dy[b][i0 + 1] = w * cs[b][k].x - u * cs[b][k].y;
+      }
+  }
+  float ss = 0.f, dot = 0.f;
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = 32 * b + 8 * r4 + 4 * g;
+      const bf16x4 x4 = xa(d0);
+      const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gm + d0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * r4 + j;
+        xv[b][i] = (float)x4[j];
+        ss = fmaf(xv[b][i], xv[b][i], ss);
+        dot = fmaf(g4[j] * dy[b][i], xv[b][i], dot);
+      }
+    }
+  if (rho < 0.f) rho = rsqrtf(half_sum(ss) * (1.0f / D) + eps);
+  dot = half_sum(dot);
+  const float c3 = rho * rho * rho * dot * (1.0f / D);
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = 32 * b + 8 * r4 + 4 * g;
+      const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gm + d0);
+      float o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * r4 + j;
+        o[j] = rho * g4[j] * dy[b][i] - c3 * xv[b][i];
+        dy[b][i] = valid ? rho * dy[b][i] * xv[b][i] : 0.f;  // gain-gradient term
+      }
+      if (valid) {
+        const bf16x2 t0 = pack2(o[0], o[1]), t1 = pack2(o[2], o[3]);
+        bf16x4 o4;
+        o4[0] = t0[0]; o4[1] = t0[1]; o4[2] = t1[0]; o4[3] = t1[1];
+        *reinterpret_cast<bf16x4 *>(dx + out + d0) = o4;
+      }
+    }
+  // Sum the gain terms over the wave's 32 tokens (lanes lq = 0..31 of each
+  // half) by recursive halving: step k pairs lanes lq and lq ^ 2^k, and each
+  // keeps the half of its current values selected by bit k of lq. After five
+  // steps value s of lane lq is the sum for index j = 2*rev5(lq) + s, where
+  // j = 16b + i names d = 32b + acc_row(i, g). A wave whose valid tokens are
+  // all of one modality reduces once; a mixed wave once per modality.
+  const uint64_t has_img = __ballot(valid && img), has_txt = __ballot(valid && !img);
+  const int rev = ((lq & 1) << 4) | ((lq & 2) << 2) | (lq & 4) | ((lq & 8) >> 2) | ((lq & 16) >> 4);
+  auto reduce_into = [&](int m, bool select, bool want_img) __attribute__((always_inline)) {
+    float v[64];
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[16 * b + i] = (!select || img == want_img) ? dy[b][i] : 0.f;
+#pragma unroll
+    for (int i = 16 * DB; i < 64; ++i) v[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const int half = 32 >> k;
+      const bool up = (lq >> k) & 1;
+#pragma unroll
+      for (int j = 0; j < half; ++j) {
+        const float keep = up ? v[j + half] : v[j];
+        const float send = up ? v[j] : v[j + half];
+        v[j] = keep + __shfl_xor(send, 1 << k);
+      }
+    }
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      const int j = 2 * rev + sidx;
+      if (j < 16 * DB) red[m * D + 32 * (j >> 4) + acc_row(j & 15, g)] = v[sidx];
+    }
+  };
+  auto zero_row = [&](int m) __attribute__((always_inline)) {
+    for (int e = lane; e < D; e += 64) red[m * D + e] = 0.f;
+  };
+  if (has_img && has_txt) {
+    reduce_into(0, true, false);
+    reduce_into(1, true, true);
+  } else if (has_img) {
+    reduce_into(1, false, true);
+    zero_row(0);
+  } else {
+    reduce_into(0, false, false);  // text only (or no valid token: all zero)
+    zero_row(1);
+  }
+}
+
+// Fixed-order sum of nw per-wave gain partials red[w][2][D] into out[2][D]
+// (threads 0 .. 2D-1 of the workgroup).
+template <int D>
+__device__ __forceinline__ void sum_wave_partials(const float *red, int nw, float *out, int tid) {
+  if (tid < 2 * D) {
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += red[w * 2 * D + tid];
+    out[tid] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ-hat (and D) for one 256-query tile of one sample and head.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -60,15 +215,23 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
   constexpr int CHUNKS = BN * D / 8 / NT;
   __shared__ __attribute__((aligned(16))) bf16 k_s[2][BN * LDK];
   __shared__ __attribute__((aligned(16))) bf16 v_s[2][BN * LDV];
+  __shared__ __attribute__((aligned(16))) bf16 x_s[NWQ * 32 * D];  // pre-norm q rows, for the epilogue
+  __shared__ __attribute__((aligned(16))) float g_s[2 * D];         // Q gains: text, image
+  __shared__ float red[NWQ * 2 * D];
 
   const int H = p.num_heads;
   const int N = p.total_tokens;
   const int2 wb = p.fwd_blocks[blockIdx.x];
-  if (wb.x < 0) return;  // idle slot of the block map (whole workgroup)
+  float *part = a.part_q + (int64_t)blockIdx.x * 2 * D;
+  if (wb.x < 0) {  // idle slot of the block map (whole workgroup): empty partials
+    if (threadIdx.x < 2 * D) part[threadIdx.x] = 0.f;
+    return;
+  }
   const int h = wb.y;
   const int4 it = p.fwd_items[wb.x];
   const int seg0 = it.x, seg1 = it.y, q0 = it.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, g = lane >> 5;
   const int64_t HD = (int64_t)H * D;
   const bf16 *qh = static_cast<const bf16 *>(a.q_hat);
@@ -81,6 +244,17 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
   // This lane's query: Q-hat and dO rows as B operands (d = 16s + 8g + 0..7).
   const int qi = q0 + wave * 32 + lq;
   const int qc = min(qi, seg1 - 1);
+  // Epilogue inputs, fetched now: the wave's pre-norm q rows into LDS, the Q
+  // gains, this query's token word and rstd.
+  {
+    TileLoader<D, SWZ_ROWS, 32, 1> xload;
+    xload.init(0, lane);
+    xload.issue_clamped(x_s + wave * 32 * D, static_cast<const bf16 *>(a.q) + h * D, a.q_stride,
+                        q0 + wave * 32, seg1 - 1);
+  }
+  if (tid < 2 * D) g_s[tid] = a.gains[tid];
+  const int32_t meta = p.tok_meta[qc];
+  const float rho0 = a.rstd ? a.rstd[(int64_t)qc * H + h] : -1.f;
   bf16x8 qf[KS], gf[KS];
   float dlt = 0.f;
   {
@@ -192,17 +366,15 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
     __syncthreads();
   }
 
-  // dQ-hat row of this lane's query: register i of block b is d = 32b + acc_row(i, g).
-  if (qi < seg1) {
-    float *dst = a.dq_acc + (int64_t)qi * HD + h * D;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<float4 *>(dst + b * 32 + 8 * r4 + 4 * g) =
-            make_float4(dq[b][4 * r4] * a.scale, dq[b][4 * r4 + 1] * a.scale,
-                        dq[b][4 * r4 + 2] * a.scale, dq[b][4 * r4 + 3] * a.scale);
-  }
+  // dQ-hat row of this lane's query -> dq, and the block's Q gain partials.
+  const bf16 *xt = x_s + wave * 32 * D;
+  auto xa = [&](int d0) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x4 *>(xt + swz_off<D, SWZ_ROWS>(lq, d0));
+  };
+  prologue_bwd_rows<D>(dq, a.scale, meta, rho0, qi < seg1, xa, g_s, p.rope, p.rms_eps,
+                       static_cast<bf16 *>(a.dq), ((int64_t)qc * H + h) * D, red + wave * 2 * D, lane);
+  __syncthreads();
+  sum_wave_partials<D>(red, NWQ, part, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -245,6 +417,7 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   constexpr int STAGE = 2 * TILE + 4 * BMQ;  // bf16 elements
   __shared__ __attribute__((aligned(16))) bf16 st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
   __shared__ __attribute__((aligned(16))) uint4 p_s[4 * (BMQ / 16) * 64];
+  __shared__ __attribute__((aligned(16))) float g_s[2 * D];  // K gains: text, image
   auto stg = [&](auto stage) __attribute__((always_inline)) -> bf16 * {
     constexpr int S = decltype(stage)::value;
     if constexpr (S == 0) return st0; else if constexpr (S == 1) return st1;
@@ -262,7 +435,11 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   const int H = p.num_heads;
   const int N = p.total_tokens;
   const int2 wb = p.bwd_blocks[blockIdx.x];
-  if (wb.x < 0) return;  // idle slot of the block map (whole workgroup)
+  float *part = a.part_k + (int64_t)blockIdx.x * 2 * D;
+  if (wb.x < 0) {  // idle slot of the block map (whole workgroup): empty partials
+    if (threadIdx.x < 2 * D) part[threadIdx.x] = 0.f;
+    return;
+  }
   const int h = wb.y;
   const int4 it = p.bwd_items[wb.x];
   const int seg0 = it.x, seg1 = it.y, k0 = it.z;
@@ -284,6 +461,11 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   const bool key_ok = kr < seg1;
   const int kc = min(kr, seg1 - 1);
   bf16x8 kv[KS];
+  // Epilogue inputs of the dS/dK waves, fetched now: K gains, this key's
+  // token word and rstd.
+  if (tid < 2 * D) g_s[tid] = a.gains[2 * D + tid];
+  const int32_t meta = role ? p.tok_meta[kc] : 0;
+  const float rho0 = (role && a.rstd) ? a.rstd[((int64_t)N + kc) * H + h] : -1.f;
   {
     const bf16 *src = role == 0 ? static_cast<const bf16 *>(a.k_hat) + (int64_t)kc * HD + h * D
                                 : static_cast<const bf16 *>(a.v) + (int64_t)kc * a.v_stride + h * D;
@@ -445,10 +627,12 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   wait_vmem();  // no load into LDS may outlive the workgroup
 
   // Rows of this lane's key: register i of block b is d = 32b + acc_row(i, g).
-  if (key_ok) {
-    const int64_t off = (int64_t)kr * HD + h * D;
-    if (role == 0) {
-      bf16 *dvp = static_cast<bf16 *>(a.dv) + off;
+  // The P buffer is free after the loop's last barrier; it holds the dS/dK
+  // waves' gain partials.
+  float *red = reinterpret_cast<float *>(p_s);
+  if (role == 0) {
+    if (key_ok) {
+      bf16 *dvp = static_cast<bf16 *>(a.dv) + (int64_t)kr * HD + h * D;
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -459,17 +643,17 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
           v4[0] = t0[0]; v4[1] = t0[1]; v4[2] = t1[0]; v4[3] = t1[1];
           *reinterpret_cast<bf16x4 *>(dvp + b * 32 + 8 * r4 + 4 * g) = v4;
         }
-    } else {
-      float *dkp = a.dk_acc + off;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<float4 *>(dkp + b * 32 + 8 * r4 + 4 * g) =
-              make_float4(acc[b][4 * r4] * a.scale, acc[b][4 * r4 + 1] * a.scale,
-                          acc[b][4 * r4 + 2] * a.scale, acc[b][4 * r4 + 3] * a.scale);
     }
+  } else {
+    const bf16 *xg = static_cast<const bf16 *>(a.k) + (int64_t)kc * a.k_stride + h * D;
+    auto xa = [&](int d0) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x4 *>(xg + d0);
+    };
+    prologue_bwd_rows<D>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope, p.rms_eps,
+                         static_cast<bf16 *>(a.dk), ((int64_t)kc * H + h) * D, red + sub * 2 * D, lane);
   }
+  __syncthreads();
+  sum_wave_partials<D>(red, KV_NW / 2, part, tid);
 }
 
 hipError_t launch_attn_bwd_f32(const PlanDev &p, const AttnBwdArgs &a, int which, hipStream_t stream);

@@ -50,6 +50,15 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
                         uint64_t host_blob_bytes);
 uint64_t bwd_partial_blocks(int64_t n_tokens);
 
+// Backward workspace layout (byte offsets, each 256-byte aligned): D [H][N],
+// Q gain partials [nq][2][d], K gain partials [nk][2][d], then for fp32 plans
+// the dQ-hat and dK-hat accumulators [N][H][d].
+struct BwdLayout {
+  uint64_t delta, part_q, part_k, dq_acc, dk_acc, total;
+  int32_t nq, nk;
+};
+BwdLayout bwd_layout(const mmdit_plan &p);
+
 // ---------------------------------------------------------------------------
 // Kernel launch arguments (device pointers; plain data passed by value).
 // ---------------------------------------------------------------------------
@@ -94,22 +103,31 @@ struct AttnBwdArgs {
   int64_t v_stride, dout_stride;
   const float *lse;            // [H][N]
   float *delta;                // [H][N]: written by the dQ pass, read by the dK/dV pass
-  float *dq_acc;               // [N][H][d] fp32 dQ-hat (scaled by 1/sqrt(d))
-  float *dk_acc;               // [N][H][d] fp32 dK-hat (scaled by 1/sqrt(d))
+  float *dq_acc;               // fp32 path: [N][H][d] dQ-hat (scaled by 1/sqrt(d))
+  float *dk_acc;               // fp32 path: [N][H][d] dK-hat (scaled by 1/sqrt(d))
   void *dv;                    // [N][H][d] dtype
   float scale_log2;            // log2(e) / sqrt(d)
   float scale;                 // 1 / sqrt(d)
+  // bf16 path: the prologue backward runs in the kernels' epilogues.
+  const void *q, *k;           // pre-norm inputs
+  int64_t q_stride, k_stride;
+  const float *gains;          // [4][d]
+  const float *rstd;           // [2][N][H] or nullptr = recompute
+  void *dq, *dk;               // [N][H][d] dtype, dense
+  float *part_q, *part_k;      // [grid blocks][2][d] gain-gradient partials (text, image)
 };
 
+// fp32 path: prologue backward of Q (which = 0) or K (which = 1) from the
+// fp32 dX-hat accumulator.
 struct PrologueBwdArgs {
-  const void *q, *k;
-  int64_t q_stride, k_stride;
-  const float *gains;
+  const void *x;
+  int64_t x_stride;
+  const float *gains;          // [4][d]
   const float *rstd;           // [2][N][H] or nullptr = recompute
-  const float *dq_hat, *dk_hat;
-  void *dq, *dk;
-  float *partials;             // [blocks][4][d]
-  float *dgains;               // [4][d] or nullptr
+  const float *dx_hat;         // [N][H][d] fp32
+  void *dx;                    // [N][H][d] dtype, dense
+  float *partials;             // [num_blocks][2][d]
+  int32_t which;
   int32_t num_blocks;
 };
 
@@ -123,5 +141,9 @@ hipError_t launch_attn_bwd(int dtype, const PlanDev &p, const AttnBwdArgs &a, in
                            hipStream_t stream);
 hipError_t launch_prologue_bwd(int dtype, const PlanDev &p, const PrologueBwdArgs &a,
                                hipStream_t stream);
+// dgains[m][e] = fixed-order sums of the gain partials: rows m = 0, 1 from
+// part_q[0..nq), rows m = 2, 3 from part_k[0..nk).
+hipError_t launch_gain_reduce(const float *part_q, int nq, const float *part_k, int nk, int d,
+                              float *dgains, hipStream_t stream);
 
 }  // namespace mmdit

@@ -47,6 +47,29 @@ uint64_t bwd_partial_blocks(int64_t n_tokens) {
   return (uint64_t)std::max<int64_t>(1, std::min<int64_t>(b, kPbwdMaxBlocks));
 }
 
+BwdLayout bwd_layout(const mmdit_plan &p) {
+  BwdLayout w{};
+  const bool f32 = p.dtype == MMDIT_F32;
+  const uint64_t N = (uint64_t)p.total_tokens, H = (uint64_t)p.num_heads, d = (uint64_t)p.head_dim;
+  w.nq = f32 ? (int32_t)bwd_partial_blocks(p.total_tokens) : p.num_fwd_blocks;
+  w.nk = f32 ? (int32_t)bwd_partial_blocks(p.total_tokens) : p.num_bwd_blocks;
+  uint64_t off = 0;
+  w.delta = off;
+  off = align_up(off + 4 * H * N, 256);
+  w.part_q = off;
+  off = align_up(off + (uint64_t)w.nq * 2 * d * 4, 256);
+  w.part_k = off;
+  off = align_up(off + (uint64_t)w.nk * 2 * d * 4, 256);
+  w.dq_acc = w.dk_acc = off;
+  if (f32) {
+    off = align_up(off + N * H * d * 4, 256);
+    w.dk_acc = off;
+    off = align_up(off + N * H * d * 4, 256);
+  }
+  w.total = off;
+  return w;
+}
+
 mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *host_blob,
                         uint64_t host_blob_bytes) {
   if (!desc || !plan) return fail(MMDIT_ERR_INVALID_ARG, "desc and plan must not be NULL");
@@ -175,8 +198,7 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
   const uint64_t elt = desc->dtype == MMDIT_BF16 ? 2 : 4;
   const uint64_t nhd = (uint64_t)N * H * d;
   p.fwd_workspace_bytes = 2 * align_up(nhd * elt, 256);
-  p.bwd_workspace_bytes = 2 * align_up(nhd * 4, 256) + align_up(4ull * H * N, 256) +
-                          align_up(bwd_partial_blocks(N) * 4ull * d * 4, 256);
+  p.bwd_workspace_bytes = bwd_layout(p).total;
   p.fingerprint = plan_fingerprint(p);
   *plan = p;
 

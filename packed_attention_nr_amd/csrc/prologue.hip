@@ -8,8 +8,9 @@
 //    normalisation fused into single kernels);
 //  * backward preprocess: D = rowsum(dO * O) per (token, head) and clearing
 //    of the fp32 dQ-hat accumulator;
-//  * prologue backward: inverse RoPE, RMSNorm backward and per-block gain
-//    gradient partials, then a fixed-order reduction of the partials.
+//  * prologue backward for the fp32 path (inverse RoPE, RMSNorm backward and
+//    per-block gain-gradient partials; the bf16 attention kernels do this in
+//    their epilogues), and the fixed-order reduction of the partials.
 //
 // One (token, head) row of d elements is handled by LPR lanes that each move
 // 16 bytes (8 bf16 or 4 fp32); the row's sum of squares is reduced with DPP
@@ -151,8 +152,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PlanDev p, BwdPreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Prologue backward. Block b handles tokens [c*TPB, (c+1)*TPB) for chunks
-// c = b, b + gridDim.x, ...; its gain-gradient sums go to partials[b][4][D].
+// Prologue backward of Q (which = 0) or K (which = 1) from an fp32 dX-hat
+// (the fp32 path; the bf16 attention kernels do this in their epilogues).
+// Block b handles tokens [c*TPB, (c+1)*TPB) for chunks c = b, b + gridDim.x,
+// ...; its gain-gradient sums go to partials[b][2][D] (text, image).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prologue_bwd_kernel(PlanDev p, PrologueBwdArgs a) {
@@ -160,15 +163,15 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(PlanDev p, PrologueBw
   constexpr int LPR = D / VEC;
   constexpr int RPB = 256 / LPR;
   constexpr int TPB = kPbwdTokensPerBlock;
-  __shared__ float red[RPB][4][D];
+  __shared__ float red[RPB][2][D];
   const int H = p.num_heads;
   const int N = p.total_tokens;
   const int64_t rows = (int64_t)N * H;
   const int e0 = (threadIdx.x % LPR) * VEC;
   const int grp = threadIdx.x / LPR;
-  float acc[4][VEC];
+  float acc[2][VEC];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int i = 0; i < VEC; ++i) acc[m][i] = 0.f;
 
@@ -179,70 +182,85 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(PlanDev p, PrologueBw
       bool img;
       int row, col;
       tok_pos(p.tok_meta[t], img, row, col);
+      const T *xp = static_cast<const T *>(a.x) + t * a.x_stride + h * D + e0;
+      const float *dyp = a.dx_hat + r * D + e0;
+      float x[VEC], dy[VEC];
+      Vec<T>::load(xp, x);
 #pragma unroll
-      for (int which = 0; which < 2; ++which) {  // 0: Q, 1: K
-        const T *xp = static_cast<const T *>(which ? a.k : a.q) +
-                      t * (which ? a.k_stride : a.q_stride) + h * D + e0;
-        const float *dyp = (which ? a.dk_hat : a.dq_hat) + r * D + e0;
-        float x[VEC], dy[VEC];
-        Vec<T>::load(xp, x);
-#pragma unroll
-        for (int i = 0; i < VEC; i += 4) {
-          float4 v = *reinterpret_cast<const float4 *>(dyp + i);
-          dy[i] = v.x; dy[i + 1] = v.y; dy[i + 2] = v.z; dy[i + 3] = v.w;
-        }
-        if (img) rope_lane<D, VEC>(dy, p.rope, e0, row, col, -1.f);
-        float rho;
-        if (a.rstd) {
-          rho = a.rstd[which * rows + r];
-        } else {
-          float ss = 0.f;
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) ss += x[i] * x[i];
-          ss = group_sum<LPR>(ss);
-          rho = rsqrtf(ss * (1.0f / D) + p.rms_eps);
-        }
-        const int m = 2 * which + (img ? 1 : 0);
-        const float *g = a.gains + m * D + e0;
-        float dot = 0.f;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) dot += g[i] * dy[i] * x[i];
-        dot = group_sum<LPR>(dot);
-        const float c3 = rho * rho * rho * dot * (1.0f / D);
-        float dx[VEC];
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          dx[i] = rho * g[i] * dy[i] - c3 * x[i];
-          const float dg = dy[i] * x[i] * rho;
-          // m is uniform across the lane group; keep the select branch-free
-#pragma unroll
-          for (int mm = 0; mm < 4; ++mm) acc[mm][i] += (mm == m) ? dg : 0.f;
-        }
-        Vec<T>::store(static_cast<T *>(which ? a.dk : a.dq) + r * D + e0, dx);
+      for (int i = 0; i < VEC; i += 4) {
+        float4 v = *reinterpret_cast<const float4 *>(dyp + i);
+        dy[i] = v.x; dy[i + 1] = v.y; dy[i + 2] = v.z; dy[i + 3] = v.w;
       }
+      if (img) rope_lane<D, VEC>(dy, p.rope, e0, row, col, -1.f);
+      float rho;
+      if (a.rstd) {
+        rho = a.rstd[a.which * rows + r];
+      } else {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) ss += x[i] * x[i];
+        ss = group_sum<LPR>(ss);
+        rho = rsqrtf(ss * (1.0f / D) + p.rms_eps);
+      }
+      const float *g = a.gains + (2 * a.which + (img ? 1 : 0)) * D + e0;
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) dot += g[i] * dy[i] * x[i];
+      dot = group_sum<LPR>(dot);
+      const float c3 = rho * rho * rho * dot * (1.0f / D);
+      float dx[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        dx[i] = rho * g[i] * dy[i] - c3 * x[i];
+        const float dg = dy[i] * x[i] * rho;
+        acc[0][i] += img ? 0.f : dg;
+        acc[1][i] += img ? dg : 0.f;
+      }
+      Vec<T>::store(static_cast<T *>(a.dx) + r * D + e0, dx);
     }
   }
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int i = 0; i < VEC; ++i) red[grp][m][e0 + i] = acc[m][i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 4 * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < 2 * D; idx += 256) {
     const int m = idx / D, e = idx % D;
     float s = 0.f;
     for (int k = 0; k < RPB; ++k) s += red[k][m][e];
-    a.partials[(int64_t)blockIdx.x * 4 * D + idx] = s;
+    a.partials[(int64_t)blockIdx.x * 2 * D + idx] = s;
   }
 }
 
-// dgains[m][e] = sum over blocks b (in order) of partials[b][m][e].
-__global__ __launch_bounds__(256) void dgain_reduce_kernel(const float *partials, int blocks, int n,
-                                                           float *dgains) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= n) return;
+// dgains[m][e] for m = 0, 1 is the sum over blocks b < nq of part_q[b][m][e],
+// for m = 2, 3 over b < nk of part_k[b][m-2][e]. Workgroup (m, 64-column
+// chunk): wave w sums blocks w, w+16, ... in order, then the 16 wave sums are
+// added in order -- the same result on every run.
+__global__ __launch_bounds__(1024) void gain_reduce_kernel(const float *part_q, int nq, const float *part_k,
+                                                           int nk, int d, float *dgains) {
+  __shared__ float red[16][64];
+  const int m = blockIdx.x / (d / 64);
+  const int e = (blockIdx.x % (d / 64)) * 64 + (threadIdx.x & 63);
+  const int w = threadIdx.x >> 6;
+  const float *src = m < 2 ? part_q + m * d : part_k + (m - 2) * d;
+  const int nb = m < 2 ? nq : nk;
   float s = 0.f;
-  for (int b = 0; b < blocks; ++b) s += partials[(int64_t)b * n + idx];
-  dgains[idx] = s;
+  int b = w;
+  for (; b + 16 * 7 < nb; b += 16 * 8) {  // eight loads in flight, summed in order
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = src[(int64_t)(b + 16 * u) * 2 * d + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += t[u];
+  }
+  for (; b < nb; b += 16) s += src[(int64_t)b * 2 * d + e];
+  red[w][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (w == 0) {
+    float t = 0.f;
+    for (int k = 0; k < 16; ++k) t += red[k][threadIdx.x];
+    dgains[m * d + e] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -270,11 +288,6 @@ static hipError_t bwd_pre_t(const PlanDev &p, const BwdPreArgs &a, hipStream_t s
 template <typename T, int D>
 static hipError_t prologue_bwd_t(const PlanDev &p, const PrologueBwdArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((prologue_bwd_kernel<T, D>), dim3(a.num_blocks), dim3(256), 0, s, p, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !a.dgains) return e;
-  const int n = 4 * D;
-  hipLaunchKernelGGL(dgain_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a.partials,
-                     a.num_blocks, n, a.dgains);
   return hipGetLastError();
 }
 
@@ -300,6 +313,13 @@ hipError_t launch_bwd_pre(int dtype, const PlanDev &p, const BwdPreArgs &a, hipS
 hipError_t launch_prologue_bwd(int dtype, const PlanDev &p, const PrologueBwdArgs &a,
                                hipStream_t stream) {
   MMDIT_DISPATCH(prologue_bwd_t, p, a, stream);
+}
+hipError_t launch_gain_reduce(const float *part_q, int nq, const float *part_k, int nk, int d,
+                              float *dgains, hipStream_t stream) {
+  if (d % 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gain_reduce_kernel, dim3(4 * (d / 64)), dim3(1024), 0, stream, part_q, nq, part_k,
+                     nk, d, dgains);
+  return hipGetLastError();
 }
 
 }  // namespace mmdit

@@ -2,6 +2,8 @@
 running the HIP path through the binding, and the oracle on a head subset."""
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 
 import oracle
@@ -69,13 +71,6 @@ def run_gpu(inp, backward=True, device="cuda"):
     if backward and inp.dout is not None:
         g = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], saved, t["dout"])
         out.update({k: host(v) for k, v in g.items() if k != "workspace"})
-        N, H, d = pack.N, pack.H, pack.d
-        ws = g["workspace"]
-        nhd = N * H * d
-        off = (nhd * 4 + 255) // 256 * 256
-        f = ws.view(torch.uint8)
-        out["dq_hat"] = host(f[:nhd * 4].view(torch.float32).view(N, H, d))
-        out["dk_hat"] = host(f[off:off + nhd * 4].view(torch.float32).view(N, H, d))
     torch.cuda.synchronize()
     out["lse"] = out["lse"].T            # [N, H] like the oracle
     out["rstd_q"] = out["rstd"][0]
@@ -99,20 +94,11 @@ def run_oracle(inp, heads=None, backward=True):
     return out
 
 
-def prologue_bwd_from(inp, dq_hat, dk_hat):
-    """The oracle's inverse RoPE and RMSNorm backward applied to given dQ-hat /
-    dK-hat (all heads): dq, dk, dgains."""
-    lay = oracle.layout(inp.text_len, inp.grid_h, inp.grid_w)
-    d = inp.head_dim
-    ang = oracle.rope_angles(lay, d, inp.rope_theta)
-    res = {}
-    dg = []
-    for name, x, dh, which in (("dq", inp.q, dq_hat, "q"), ("dk", inp.k, dk_hat, "k")):
-        x = x.astype(np.float64)
-        g_tok = oracle.token_gains(inp.gains, lay, which)
-        _, rho = oracle.rms_norm(x, g_tok, inp.rms_eps)
-        dx, dgt = oracle.rms_norm_backward(x, g_tok, rho, oracle.rope_backward(dh, ang))
-        res[name] = dx
-        dg += [dgt[~lay.is_image].sum(axis=(0, 1)), dgt[lay.is_image].sum(axis=(0, 1))]
-    res["dgains"] = np.stack(dg)
-    return res
+def subset_heads(inp, heads):
+    """The same pack restricted to the given heads (inputs sliced, nothing
+    redrawn): heads are independent, so each kept head's outputs are those of
+    the full pack; the gain gradients become sums over the kept heads only."""
+    hs = list(heads)
+    cut = lambda a: None if a is None else np.ascontiguousarray(a[:, hs])
+    return dataclasses.replace(inp, q=cut(inp.q), k=cut(inp.k), v=cut(inp.v), dout=cut(inp.dout),
+                               heads=len(hs))

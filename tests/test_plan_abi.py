@@ -245,6 +245,13 @@ def _bwd(plan, ws_bytes=None, **kw):
     (dict(ws=None), 1),
     (dict(stages=16), 1),
     (dict(ws_bytes=64), 3),
+    (dict(stages=1, q=None), 1),          # the dQ stage writes dq from q
+    (dict(stages=1, o=None), 1),          # ... and forms D from o
+    (dict(stages=2, k=None), 1),          # the dK/dV stage writes dk from k
+    (dict(stages=2, dk=None), 1),
+    (dict(stages=2, gains=None), 1),
+    (dict(stages=2, dv=_p(12)), 1),       # dv overlaps dk
+    (dict(stages=4, dgains=_p(15)), 1),   # dgains overlaps the workspace
 ])
 def test_bwd_rejects_invalid_arguments(small_plan, kw, code):
     ws_bytes = kw.pop("ws_bytes", None)
