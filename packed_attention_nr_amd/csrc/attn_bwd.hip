@@ -248,9 +248,8 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
   // gains, this query's token word and rstd.
   {
     TileLoader<D, SWZ_ROWS, 32, 1> xload;
-    xload.init(0, lane);
-    xload.issue_clamped(x_s + wave * 32 * D, static_cast<const bf16 *>(a.q) + h * D, a.q_stride,
-                        q0 + wave * 32, seg1 - 1);
+    xload.init(0, lane, a.q_stride);
+    xload.issue(x_s + wave * 32 * D, static_cast<const bf16 *>(a.q) + h * D, q0 + wave * 32, seg1 - 1, N);
   }
   if (tid < 2 * D) g_s[tid] = a.gains[tid];
   const int32_t meta = p.tok_meta[qc];
@@ -475,22 +474,22 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
 
   const int ntq = (seg1 - seg0 + BMQ - 1) / BMQ;
   TileLoader<D, SWZ_ROWS, BMQ, KV_NW> qload, gload;
-  qload.init(wave, lane);
-  gload.init(wave, lane);
+  qload.init(wave, lane, HD);
+  gload.init(wave, lane, gstride);
   constexpr int LQ = TileLoader<D, SWZ_ROWS, BMQ, KV_NW>::LOADS;
   // Tile t -> ring stage; even waves also load lse and odd waves D (the same
   // words from four waves each, so every wave issues the same number of loads
   // per tile). Rows past the segment end are clamped to its last row; their P
   // is zeroed.
-  const float *ld_src = (wave & 1) ? dlt_h : lse_h;
+  const rsrc_t ld_rs = make_rsrc((wave & 1) ? dlt_h : lse_h, (uint32_t)min<int64_t>(4ll * N, 0x7FFFFFFF));
   // Every step issues one tile's loads, so the compiler's in-order count of
   // outstanding loads is exact; past the last tile the last tile is loaded
   // again into the stage just freed, which nothing reads afterwards.
   auto issue = [&](auto stage, int t) __attribute__((always_inline)) {
     const int qb0 = seg0 + min(t, ntq - 1) * BMQ;
-    qload.issue_clamped(qst(stage), qh, HD, qb0, seg1 - 1);  // branch-free: exact load counts
-    gload.issue_clamped(gst(stage), go, gstride, qb0, seg1 - 1);
-    g2lds4(ld_src + min(qb0 + lane, seg1 - 1), lst(stage) + (wave & 1) * BMQ);
+    qload.issue(qst(stage), qh, qb0, seg1 - 1, N);  // branch-free: exact load counts
+    gload.issue(gst(stage), go, qb0, seg1 - 1, N);
+    buf2lds<4>(ld_rs, 4u * (uint32_t)min(qb0 + lane, seg1 - 1), lst(stage) + (wave & 1) * BMQ);
   };
   constexpr int PER_TILE = 2 * LQ + 1;  // loads per wave per tile
 

@@ -104,21 +104,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
   // alias reads of another and adds no waits for them.
   TileLoader<D, SWZ_ROWS, BN, NW> kload;
   TileLoader<D, SWZ_TRANS, BN, NW> vload;
-  kload.init(wave, lane);
-  vload.init(wave, lane);
-  const bf16 *krow0 = kh + (int64_t)kload.r0 * HD;
-  const bf16 *vrow0 = vv + (int64_t)vload.r0 * vs;
+  kload.init(wave, lane, HD);
+  vload.init(wave, lane, vs);
   auto issue = [&](auto stage, int t) __attribute__((always_inline)) {
     if (t >= ntiles) return;
     const int kb0 = seg0 + t * BN;
-    if (kb0 + BN <= seg1) {
-      kload.issue(kst(stage), krow0 + (int64_t)kb0 * HD, HD);
-      vload.issue(vst(stage), vrow0 + (int64_t)kb0 * vs, vs);
-    } else {
-      kload.issue_clamped(kst(stage), kh, HD, kb0, seg1 - 1);
-      vload.issue_clamped(vst(stage), vv, vs, kb0, seg1 - 1);
-    }
+    kload.issue(kst(stage), kh, kb0, seg1 - 1, p.total_tokens);
+    vload.issue(vst(stage), vv, kb0, seg1 - 1, p.total_tokens);
   };
+
 
   f32x16 o[DB];
 #pragma unroll
@@ -208,8 +202,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
     issue(std::integral_constant<int, (SG + 2) % NS>{}, t + 2);
     softmax(t);
     phase_barrier();
+    // One basic block: past the last tile the scores of a stale stage are
+    // formed and never used (in-bounds LDS reads), so the block can be
+    // scheduled as one MFMA / LDS-read pipeline.
     accumulate(stage);
-    if (t + 1 < ntiles) scores(std::integral_constant<int, (SG + 1) % NS>{});
+    scores(std::integral_constant<int, (SG + 1) % NS>{});
+    pipeline_mfma_ds<16 * DB / 4 + KS * BN / 32, BN / 16 * DB, 2, 1, 4>();
   };
   issue(std::integral_constant<int, 0>{}, 0);
   issue(std::integral_constant<int, 1>{}, 1);

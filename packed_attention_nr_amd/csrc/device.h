@@ -132,18 +132,33 @@ __device__ __forceinline__ int swz_off(int r, int e) {
   return r * D + (((e >> 3) ^ swz<CPR, SW>(r)) << 3) + (e & 7);
 }
 
-// 16-byte global -> LDS copy for every lane of the wave: lane l's 16 bytes
-// land at lds_wave_base + 16*l (lds_wave_base must be wave-uniform).
-__device__ __forceinline__ void g2lds16(const void *src, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
-                                   (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+// Direct global -> LDS copies use the buffer form (MUBUF) of the load: the
+// global form is FLAT-encoded, and while a FLAT access to LDS is in flight the
+// compiler can only wait for all LDS reads at once (lgkmcnt(0)), which would
+// serialise every LDS operand read with the MFMAs that consume it.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufferFlags = 0x00020000;  // raw dword-granular buffer (gfx9 family)
+
+// Buffer resource over [base, base + bytes); accesses past the end read 0.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferFlags);
 }
 
-// 4-byte global -> LDS copy for every lane: lane l's word lands at
-// lds_wave_base + 4*l.
-__device__ __forceinline__ void g2lds4(const void *src, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
-                                   (__attribute__((address_space(3))) void *)lds_wave_base, 4, 0, 0);
+// Bytes addressable from element `first` of a [rows][stride] tensor through
+// `row_elems` elements of its last row, capped to the 32-bit buffer range.
+__device__ __forceinline__ uint32_t rsrc_bytes(int64_t rows_left, int64_t stride, int row_elems, int elt) {
+  const int64_t b = ((rows_left - 1) * stride + row_elems) * elt;
+  return b > 0x7FFFFFFF ? 0x7FFFFFFFu : (uint32_t)b;
+}
+
+// SIZE-byte global -> LDS copy for every lane of the wave: lane l's bytes at
+// rsrc + voffset land at lds_wave_base + SIZE*l (lds_wave_base wave-uniform).
+template <int SIZE>
+__device__ __forceinline__ void buf2lds(rsrc_t r, uint32_t voffset, void *lds_wave_base) {
+  static_assert(SIZE == 4 || SIZE == 16, "dword or dwordx4");
+  auto *lds = (__attribute__((address_space(3))) void *)lds_wave_base;
+  if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voffset, 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voffset, 0, 0, 0);
 }
 
 // Wait until this wave's outstanding global (and global->LDS) loads are done.
@@ -182,11 +197,40 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Scheduling hint for one basic block holding NM MFMAs whose A operands come
+// from LDS: MFMA i (in program order) needs RA DS reads for i < NA and RB
+// after. The block is ordered as a pipeline: the reads of the first DIST
+// MFMAs, then each MFMA followed by the reads of the MFMA DIST places ahead,
+// so LDS latency hides behind DIST MFMAs. Call it at the end of the block.
+template <int NA, int RA, int RB>
+__device__ constexpr int ds_reads_of(int j, int nm) {
+  return j < NA ? RA : (j < nm ? RB : 0);
+}
+template <int I, int NM, int NA, int RA, int RB, int DIST>
+__device__ __forceinline__ void pipeline_steps() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int r = ds_reads_of<NA, RA, RB>(I + DIST, NM);
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // DS reads
+    pipeline_steps<I + 1, NM, NA, RA, RB, DIST>();
+  }
+}
+template <int NM, int NA, int RA, int RB, int DIST>
+__device__ __forceinline__ void pipeline_mfma_ds() {
+  constexpr int pre = [] {
+    int n = 0;
+    for (int j = 0; j < DIST; ++j) n += ds_reads_of<NA, RA, RB>(j, NM);
+    return n;
+  }();
+  __builtin_amdgcn_sched_group_barrier(0x100, pre, 0);
+  pipeline_steps<0, NM, NA, RA, RB, DIST>();
+}
+
 // Direct global -> LDS loader of a swizzled D-wide tile of ROWS rows, shared
 // by NW waves. Each wave-wide load fills 64/CPR consecutive rows; lane l of
 // load u covers tile row r0 + u*RPL (r0 = first row of this lane) and
 // physical chunk l % CPR, fetching the logical chunk that the swizzle puts
-// there. Per-lane offsets are computed once.
+// there. Per-lane byte offsets (row and chunk parts) are computed once.
 template <int D, int SW, int ROWS, int NW>
 struct TileLoader {
   static constexpr int CPR = D / 8;
@@ -195,30 +239,32 @@ struct TileLoader {
   static_assert(ROWS % (RPL * NW) == 0, "tile rows must split evenly over the waves");
   int r0;                 // tile row of this lane in load 0
   int lds0;               // element offset of this wave's first load (uniform)
-  int chunk[LOADS];       // element offset of the logical chunk, per load
+  uint32_t rowb[LOADS];   // byte offset of the lane's row, per load
+  uint32_t chunkb[LOADS]; // byte offset of the logical chunk in the row
+  int64_t stride;         // elements between source rows
 
-  __device__ __forceinline__ void init(int wave_uniform, int lane) {
+  __device__ __forceinline__ void init(int wave_uniform, int lane, int64_t row_stride) {
+    stride = row_stride;
     r0 = wave_uniform * LOADS * RPL + lane / CPR;
     lds0 = wave_uniform * LOADS * RPL * D;
     const int pc = lane % CPR;
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) chunk[u] = 8 * (pc ^ swz<CPR, SW>(r0 + u * RPL));
+    for (int u = 0; u < LOADS; ++u) {
+      rowb[u] = (uint32_t)((r0 + u * RPL) * row_stride * 2);
+      chunkb[u] = (uint32_t)(16 * (pc ^ swz<CPR, SW>(r0 + u * RPL)));
+    }
   }
-  // Rows kb0 + r for r < ROWS, all inside the source: row_ptr = element 0 of
-  // source row (kb0 + r0), stride = elements between source rows.
-  __device__ __forceinline__ void issue(bf16 *tile, const bf16 *row_ptr, int64_t stride) const {
+  // Source rows kb0 + r for r < ROWS, clamped to last_row (>= kb0); base =
+  // element (0, 0) of the source at the wanted head, rows_total = its rows.
+  __device__ __forceinline__ void issue(bf16 *tile, const bf16 *base, int64_t kb0, int64_t last_row,
+                                        int64_t rows_total) const {
+    const int64_t k0 = kb0 < last_row ? kb0 : last_row;  // a tile wholly past last_row repeats it
+    const bf16 *b0 = base + k0 * stride;
+    const rsrc_t r = make_rsrc(b0, rsrc_bytes(rows_total - k0, stride, D, 2));
+    const uint32_t lastb = (uint32_t)((last_row - k0) * stride * 2);
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
-      g2lds16(row_ptr + (int64_t)(u * RPL) * stride + chunk[u], tile + lds0 + u * RPL * D);
-  }
-  // Same, with source rows clamped to last_row: base = element 0 of row 0.
-  __device__ __forceinline__ void issue_clamped(bf16 *tile, const bf16 *base, int64_t stride, int kb0,
-                                                int last_row) const {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int row = min(kb0 + r0 + u * RPL, last_row);
-      g2lds16(base + (int64_t)row * stride + chunk[u], tile + lds0 + u * RPL * D);
-    }
+      buf2lds<16>(r, min(rowb[u], lastb) + chunkb[u], tile + lds0 + u * RPL * D);
   }
 };
 
