@@ -570,11 +570,17 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   };
 
   using S0 = std::integral_constant<int, 0>;
+  // dK(t-1) runs unconditionally in every step: for t = 0 it multiplies the
+  // zeroed Q-hat part of stage 3 (tile 3 arrives there only after step 0) by
+  // dS = 0 and adds exactly nothing.
+#pragma unroll
+  for (int u = 0; u < BMQ / 16; ++u) pb[u] = bf16x8{};
+  for (int e = tid * 8; e < TILE; e += 64 * KV_NW * 8) st_bf16x8(st3 + e, bf16x8{});
   issue(S0{}, 0);
   issue(std::integral_constant<int, 1>{}, 1);
   issue(std::integral_constant<int, 2>{}, 2);
   wait_vmem_le<2 * PER_TILE>();  // this wave's loads of tile 0
-  phase_barrier();  // tile 0 visible
+  phase_barrier();  // tile 0 and the zeroed stage visible
 
   // Both roles run the same whole number of 4-step groups (every step loads,
   // waits and passes two barriers; work is skipped past the last tile), so the
@@ -587,9 +593,12 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
       wait_vmem_le<PER_TILE>();  // this wave's loads of tile t+1
       phase_barrier();  // P(t) and tile t+1 visible
       issue(std::integral_constant<int, (SG + 3) % KV_NS>{}, t + 3);
-      if (t < ntq) {
+      if (t < ntq) {  // one basic block, scheduled as an MFMA / LDS-read pipeline
         accumulate(gst(stage));  // dV(t)
-        if (t + 1 < ntq) rows_x_key(qst(std::integral_constant<int, (SG + 1) % KV_NS>{}));  // S(t+1)
+        // S(t+1); past the last tile the stage holds a repeat of the last
+        // tile and the result goes unused
+        rows_x_key(qst(std::integral_constant<int, (SG + 1) % KV_NS>{}));
+        pipeline_mfma_ds<(BMQ / 16) * DB + 2 * KS, (BMQ / 16) * DB, 2, 1, 4>();
       }
       phase_barrier();  // P(t) consumed
     };
@@ -602,9 +611,10 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   } else {
     auto step = [&](auto stage, int t) __attribute__((always_inline)) {
       constexpr int SG = decltype(stage)::value;
-      if (t < ntq) {
-        if (t > 0) accumulate(qst(std::integral_constant<int, (SG + 3) % KV_NS>{}));  // dK(t-1)
+      if (t < ntq) {  // one basic block, scheduled as an MFMA / LDS-read pipeline
+        accumulate(qst(std::integral_constant<int, (SG + 3) % KV_NS>{}));  // dK(t-1)
         rows_x_key(gst(stage));  // dP(t)
+        pipeline_mfma_ds<(BMQ / 16) * DB + 2 * KS, (BMQ / 16) * DB, 2, 1, 4>();
       }
       wait_vmem_le<PER_TILE>();  // this wave's loads of tile t+1
       phase_barrier();  // P(t) and tile t+1 visible
