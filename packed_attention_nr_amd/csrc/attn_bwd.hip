@@ -473,10 +473,10 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   }
 
   const int ntq = (seg1 - seg0 + BMQ - 1) / BMQ;
-  TileLoader<D, SWZ_ROWS, BMQ, KV_NW> qload, gload;
+  TileLoader<D, SWZ_BOTH, BMQ, KV_NW> qload, gload;
   qload.init(wave, lane, HD);
   gload.init(wave, lane, gstride);
-  constexpr int LQ = TileLoader<D, SWZ_ROWS, BMQ, KV_NW>::LOADS;
+  constexpr int LQ = TileLoader<D, SWZ_BOTH, BMQ, KV_NW>::LOADS;
   // Tile t -> ring stage; even waves also load lse and odd waves D (the same
   // words from four waves each, so every wave issues the same number of loads
   // per tile). Rows past the segment end are clamped to its last row; their P
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
       for (int i = 0; i < 16; ++i) s[qb][i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ra = ld_bf16x8(&T[swz_off<D, SWZ_ROWS>(qb * 32 + lq, 16 * ks + 8 * g)]);
+        const bf16x8 ra = ld_bf16x8(&T[swz_off<D, SWZ_BOTH>(qb * 32 + lq, 16 * ks + 8 * g)]);
         s[qb] = mfma32(ra, kv[ks], s[qb]);
       }
     }
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
     for (int u = 0; u < BMQ / 16; ++u)
 #pragma unroll
       for (int b = 0; b < DB; ++b)
-        acc[b] = mfma32(lds_read_tr_swz<D, SWZ_ROWS>(T, u * 16, b * 32, lane), pb[u], acc[b]);
+        acc[b] = mfma32(lds_read_tr_swz<D, SWZ_BOTH>(T, u * 16, b * 32, lane), pb[u], acc[b]);
   };
   // Role 0: P = exp2(S*c2 - lse*log2e), zero for queries past the segment.
   auto softmax = [&](const float *Ls, int t) __attribute__((always_inline)) {

@@ -112,17 +112,21 @@ __device__ __forceinline__ bf16x8 lds_read_tr(const bf16 *m, int ld, int k0, int
 // ---------------------------------------------------------------------------
 // Unpadded, XOR-swizzled LDS tiles filled by direct global->LDS loads.
 // A tile row holds CPR 16-byte chunks; logical chunk c of row r sits at
-// physical chunk c ^ swz(r). Two swizzles, picked by measured gfx950 LDS
-// throughput: ROWS for tiles read 16 bytes per lane down consecutive rows,
-// TRANS for tiles read with ds_read_b64_tr_b16 (rows r..r+3 of a 4x16 block
-// land in four different 64-byte bank groups).
+// physical chunk c ^ swz(r). Swizzles by access pattern: ROWS for tiles read
+// 16 bytes per lane down consecutive rows, TRANS for tiles read with
+// ds_read_b64_tr_b16 (rows r..r+3 of a 4x16 block land in four different
+// 64-byte bank groups), BOTH for tiles read both ways.
 // ---------------------------------------------------------------------------
-enum Swz { SWZ_ROWS = 0, SWZ_TRANS = 1 };
+enum Swz { SWZ_ROWS = 0, SWZ_TRANS = 1, SWZ_BOTH = 2 };
 
+// BOTH serves tiles read both ways; for 256-byte rows it was picked by
+// measured gfx950 LDS throughput (about 205 B/clk per CU for row reads and
+// 275 for transposed reads, against 180 / 205 for ROWS); shorter rows use ROWS.
 template <int CPR, int SW>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (SW == SWZ_ROWS) return (((r & 7) << 1) | ((r >> 3) & 1)) & (CPR - 1);
-  else return (4 * (r & 3)) & (CPR - 1);
+  if constexpr (SW == SWZ_TRANS) return (4 * (r & 3)) & (CPR - 1);
+  else if constexpr (SW == SWZ_BOTH && CPR == 16) return 4 * (r & 3) + 2 * ((r >> 2) & 1) + ((r >> 3) & 1);
+  else return (((r & 7) << 1) | ((r >> 3) & 1)) & (CPR - 1);
 }
 
 // Element offset of (row r, element e) in a swizzled tile of D-element rows.
