@@ -17,6 +17,8 @@ divided by the whole step time (plan, prologues and preprocess included).
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -40,7 +42,35 @@ def sum_l2(inp):
     return int((L * L).sum())
 
 
-def cpu_baseline(inp, heads, seconds_target=20.0):
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernels_mixed6_hbm_traffic.md")
+
+
+def source_fingerprint() -> str:
+    """sha256 (first 16 hex) over the kernel sources' names and bytes."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "packed_attention_nr_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE
+    summary, or None when the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            line = next(l for l in fh if l.startswith("traffic_json:"))
+        rec = json.loads(line.split(":", 1)[1])
+    except (OSError, StopIteration, ValueError):
+        return None
+    if rec.get("source_fingerprint") != source_fingerprint():
+        return None
+    k = rec["kernels"].get("mmdit::" + kernel)
+    return None if k is None else k["hbm_bytes"]
+
+
+def cpu_baseline(inp, heads):
     """Time the fp64 oracle (fwd+bwd) on a subset of heads; report TFLOP/s of
     the same algorithmic count, scaled to the metric's unit."""
     import oracle
@@ -68,7 +98,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed6", choices=["mixed6", "gen2048", "small64"])
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for HBM counter scaling)")
@@ -167,7 +197,8 @@ def main():
     ach = cand[dom][0] / (kt[dom] * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": cand[dom][1], "achieved": round(ach, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "traffic": None, "algorithmic_flop_per_launch": cand[dom][0]}
+            "traffic": measured_traffic(cand[dom][1]) if args.workload == "mixed6" else None,
+            "algorithmic_flop_per_launch": cand[dom][0]}
     pro_bytes = 8.0 * N * H * d
     pro_gbs = pro_bytes / (kt["prologue_fwd"] * 1e-3) / 1e9
 
