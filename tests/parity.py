@@ -102,3 +102,21 @@ def subset_heads(inp, heads):
     cut = lambda a: None if a is None else np.ascontiguousarray(a[:, hs])
     return dataclasses.replace(inp, q=cut(inp.q), k=cut(inp.k), v=cut(inp.v), dout=cut(inp.dout),
                                heads=len(hs))
+
+
+def sample_offsets(inp):
+    L = inp.seqlens().astype(np.int64)
+    return np.concatenate([[0], np.cumsum(L)])
+
+
+def subset_samples(inp, order):
+    """The pack made of the given samples, in the given order (token rows
+    moved with their samples, nothing redrawn)."""
+    off = sample_offsets(inp)
+    rows = np.concatenate([np.arange(off[i], off[i + 1]) for i in order])
+    pick = lambda a: None if a is None else np.ascontiguousarray(a[rows])
+    sel = lambda a: np.asarray(a)[list(order)]
+    return dataclasses.replace(inp, text_len=sel(inp.text_len), grid_h=sel(inp.grid_h),
+                               grid_w=sel(inp.grid_w), q=pick(inp.q), k=pick(inp.k), v=pick(inp.v),
+                               dout=pick(inp.dout)), rows
+
