@@ -30,7 +30,8 @@
  *
  * Tensor layout: Q, K, V, O and their gradients are [N][H][d] (token-major,
  * then head, then the d elements contiguous). "stride" arguments give the
- * number of ELEMENTS between consecutive tokens (>= H*d, a multiple of 8), so
+ * number of ELEMENTS between consecutive tokens (>= H*d, a multiple of 8, at
+ * most MMDIT_MAX_ROW_STRIDE), so
  * Q/K/V may be views into a fused [N][3][H][d] projection output. Output
  * tensors are always dense [N][H][d]. lse and D are [H][N] fp32.
  *
@@ -54,6 +55,9 @@ extern "C" {
 
 #define MMDIT_ABI_VERSION 1
 
+/* Largest accepted token stride, in elements (2^24). */
+#define MMDIT_MAX_ROW_STRIDE (1ll << 24)
+
 typedef enum {
   MMDIT_OK = 0,
   MMDIT_ERR_INVALID_ARG = 1,       /* NULL / negative / misaligned / inconsistent argument */
@@ -67,7 +71,8 @@ typedef enum { MMDIT_F32 = 0, MMDIT_BF16 = 1 } mmdit_dtype;
 
 /* Description of one pack (host memory, read during mmdit_pack_plan only).
  * Sample i holds text_len[i] text tokens followed by a grid_h[i] x grid_w[i]
- * latent grid (both 0 for a text-only sample); every sample has >= 1 token. */
+ * latent grid (both 0 for a text-only sample); every sample has >= 1 token;
+ * the pack holds at most 2^29 tokens. */
 typedef struct {
   int32_t num_samples;          /* S >= 1 */
   const int32_t *text_len;      /* [S], >= 0 */

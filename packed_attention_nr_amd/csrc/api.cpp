@@ -66,9 +66,9 @@ static mmdit_status check_plan(const mmdit_plan *plan, const void *blob) {
 static mmdit_status check_tensor(const char *name, const void *p, int64_t stride, int64_t hd) {
   if (!p) return fail(MMDIT_ERR_INVALID_ARG, "%s must not be NULL", name);
   if (!aligned16(p)) return fail(MMDIT_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
-  if (stride < hd || stride % 8 != 0)
-    return fail(MMDIT_ERR_INVALID_ARG, "%s stride %lld must be >= H*d (%lld) and a multiple of 8", name,
-                (long long)stride, (long long)hd);
+  if (stride < hd || stride % 8 != 0 || stride > MMDIT_MAX_ROW_STRIDE)
+    return fail(MMDIT_ERR_INVALID_ARG, "%s stride %lld must be >= H*d (%lld), <= %lld and a multiple of 8", name,
+                (long long)stride, (long long)hd, (long long)MMDIT_MAX_ROW_STRIDE);
   return MMDIT_OK;
 }
 

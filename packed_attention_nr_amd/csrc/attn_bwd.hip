@@ -249,7 +249,7 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
   {
     TileLoader<D, SWZ_ROWS, 32, 1> xload;
     xload.init(0, lane, a.q_stride);
-    xload.issue(x_s + wave * 32 * D, static_cast<const bf16 *>(a.q) + h * D, q0 + wave * 32, seg1 - 1, N);
+    xload.issue(x_s + wave * 32 * D, static_cast<const bf16 *>(a.q) + h * D, q0 + wave * 32, seg1 - 1);
   }
   if (tid < 2 * D) g_s[tid] = a.gains[tid];
   const int32_t meta = p.tok_meta[qc];
@@ -387,16 +387,20 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
 //  * dS/dK waves hold their 32 V rows, form dP = dO V^T, read P back, form
 //    dS = P * (dP - D) and accumulate dK^T += Q^T dS.
 // Each tile takes two phases between workgroup barriers; in each phase one
-// role issues matrix instructions while the other does its vector work:
-//   phase 1: P/dV waves: softmax(t) -> P(t) to LDS
+// role issues matrix instructions while the other does its vector and
+// memory work:
+//   phase 1: P/dV waves: softmax(t) -> P(t) to LDS; load lse(t+1)
 //            dS/dK waves: dK(t-1), dP(t)
 //   phase 2: P/dV waves: dV(t), S(t+1)
-//            dS/dK waves: dS(t) (reads P(t)); load tile t+3
-// Q-hat / dO tiles, lse and D come by direct global->LDS loads into a
-// 4-stage ring; tile t+3 reuses the stage of tile t-1, whose last reader
-// (dK(t-1)) ran before the barrier that opens phase 2 of tile t. Each wave
-// waits for its own loads of tile t+1 before that barrier, so tile t+1 is
-// visible one phase before S(t+1) reads it.
+//            dS/dK waves: load tile t+3; dS(t) (reads P(t))
+// Only the dS/dK waves load tiles: Q-hat / dO (and D) come by direct
+// global->LDS loads into a 4-stage ring; tile t+3 reuses the stage of tile
+// t-1, whose last reader (dK(t-1)) ran before the barrier that opens phase 2
+// of tile t. They wait for their loads of tile t+1 before that barrier, so
+// tile t+1 is visible one phase before S(t+1) reads it. Issuing loads costs
+// issue cycles, so it goes to the waves that are not feeding the matrix
+// cores in that phase. The P/dV waves take the per-query lse straight into
+// registers, one tile ahead, after the softmax that used the previous one.
 // ---------------------------------------------------------------------------
 namespace bwd {
 constexpr int KV_NW = 8;   // waves of a dK/dV workgroup
@@ -410,10 +414,10 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   constexpr int DB = D / 32;
   constexpr int TILE = BMQ * D;
   static_assert(KV_NS == 4 && BMQ == 64 && KT == 32 * KV_NW / 2, "layout below");
-  // One LDS object per ring stage, [Q-hat tile | dO tile | lse | D]: distinct
+  // One LDS object per ring stage, [Q-hat tile | dO tile | D]: distinct
   // objects (at most 8 of them receiving direct loads) let the compiler prove
   // that loads into one stage do not alias reads of another.
-  constexpr int STAGE = 2 * TILE + 4 * BMQ;  // bf16 elements
+  constexpr int STAGE = 2 * TILE + 2 * BMQ;  // bf16 elements
   __shared__ __attribute__((aligned(16))) bf16 st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
   __shared__ __attribute__((aligned(16))) uint4 p_s[4 * (BMQ / 16) * 64];
   __shared__ __attribute__((aligned(16))) float g_s[2 * D];  // K gains: text, image
@@ -424,11 +428,8 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   };
   auto qst = [&](auto stage) __attribute__((always_inline)) -> bf16 * { return stg(stage); };
   auto gst = [&](auto stage) __attribute__((always_inline)) -> bf16 * { return stg(stage) + TILE; };
-  auto lst = [&](auto stage) __attribute__((always_inline)) -> float * {
-    return reinterpret_cast<float *>(stg(stage) + 2 * TILE);
-  };
   auto dst = [&](auto stage) __attribute__((always_inline)) -> float * {
-    return reinterpret_cast<float *>(stg(stage) + 2 * TILE) + BMQ;
+    return reinterpret_cast<float *>(stg(stage) + 2 * TILE);
   };
 
   const int H = p.num_heads;
@@ -473,25 +474,41 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   }
 
   const int ntq = (seg1 - seg0 + BMQ - 1) / BMQ;
-  TileLoader<D, SWZ_BOTH, BMQ, KV_NW> qload, gload;
-  qload.init(wave, lane, HD);
-  gload.init(wave, lane, gstride);
-  constexpr int LQ = TileLoader<D, SWZ_BOTH, BMQ, KV_NW>::LOADS;
-  // Tile t -> ring stage; even waves also load lse and odd waves D (the same
-  // words from four waves each, so every wave issues the same number of loads
-  // per tile). Rows past the segment end are clamped to its last row; their P
-  // is zeroed.
-  const rsrc_t ld_rs = make_rsrc((wave & 1) ? dlt_h : lse_h, (uint32_t)min<int64_t>(4ll * N, 0x7FFFFFFF));
-  // Every step issues one tile's loads, so the compiler's in-order count of
-  // outstanding loads is exact; past the last tile the last tile is loaded
-  // again into the stage just freed, which nothing reads afterwards.
+  // Loaders run by the four dS/dK waves (sub = their index among them).
+  TileLoader<D, SWZ_BOTH, BMQ, KV_NW / 2> qload, gload;
+  qload.init(sub, lane, HD);
+  gload.init(sub, lane, gstride);
+  constexpr int LQ = TileLoader<D, SWZ_BOTH, BMQ, KV_NW / 2>::LOADS;
+  // Tile t -> ring stage. Every step issues one tile's loads, so the
+  // compiler's in-order count of outstanding loads is exact; past the last
+  // tile the last tile is loaded again into the stage just freed, which
+  // nothing reads afterwards.
+  // Queries past the segment end need no mask: their Q-hat and dO rows land
+  // as zeros and their lse reads as 0 (its descriptor ends at the segment),
+  // so S = 0 and P = exp2(0) = 1 there, finite, and both dV^T += dO^T P and
+  // dK^T += Q-hat^T dS add zero for them.
+  const uint32_t vec_bytes = 4u * (uint32_t)seg1;  // lse / D words up to the segment end
+  // The dS/dK waves also load D of the tile's queries into the stage (the
+  // same 64 words from each of the four).
+  const rsrc_t d_rs = make_rsrc(dlt_h, vec_bytes);
   auto issue = [&](auto stage, int t) __attribute__((always_inline)) {
     const int qb0 = seg0 + min(t, ntq - 1) * BMQ;
-    qload.issue(qst(stage), qh, qb0, seg1 - 1, N);  // branch-free: exact load counts
-    gload.issue(gst(stage), go, qb0, seg1 - 1, N);
-    buf2lds<4>(ld_rs, 4u * (uint32_t)min(qb0 + lane, seg1 - 1), lst(stage) + (wave & 1) * BMQ);
+    qload.issue(qst(stage), qh, qb0, seg1 - 1);  // branch-free: exact load counts
+    gload.issue(gst(stage), go, qb0, seg1 - 1);
+    buf2lds<4>(d_rs, 4u * (uint32_t)(qb0 + lane), dst(stage));
   };
-  constexpr int PER_TILE = 2 * LQ + 1;  // loads per wave per tile
+  constexpr int PER_TILE = 2 * LQ + 1;  // loads per dS/dK wave per tile
+  // lse of a tile's queries in the P/dV waves' registers: lv[4 qb + r4] holds
+  // queries qb*32 + 8*r4 + 4*g + 0..3 of the tile, the rows of accumulator
+  // registers 4*r4..4*r4+3 of block qb in this lane.
+  const rsrc_t lv_rs = make_rsrc(lse_h, vec_bytes);
+  constexpr int ROW_LOADS = 2 * 4;  // f32x4 loads per wave per tile
+  f32x4 lv[ROW_LOADS];
+  auto load_rows = [&](int t) __attribute__((always_inline)) {
+    const uint32_t qb0 = (uint32_t)(seg0 + min(t, ntq - 1) * BMQ);
+#pragma unroll
+    for (int j = 0; j < ROW_LOADS; ++j) lv[j] = buf_load_f32x4(lv_rs, 4u * (qb0 + 8 * j + 4 * g));
+  };
 
   f32x16 acc[DB];  // dV^T (role 0) or dK^T (role 1): lane = key, rows = d
 #pragma unroll
@@ -524,23 +541,16 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
       for (int b = 0; b < DB; ++b)
         acc[b] = mfma32(lds_read_tr_swz<D, SWZ_BOTH>(T, u * 16, b * 32, lane), pb[u], acc[b]);
   };
-  // Role 0: P = exp2(S*c2 - lse*log2e), zero for queries past the segment.
-  auto softmax = [&](const float *Ls, int t) __attribute__((always_inline)) {
-    const int qb0 = seg0 + t * BMQ;
-    const bool tail = qb0 + BMQ > seg1;
+  // Role 0: P = exp2(S*c2 - lse*log2e).
+  auto softmax = [&]() __attribute__((always_inline)) {
+    f32x4 nl[ROW_LOADS];
+#pragma unroll
+    for (int j = 0; j < ROW_LOADS; ++j) nl[j] = lv[j] * -kLog2e;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&Ls[qb * 32 + 8 * r4 + 4 * g]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * r4 + j;
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[qb][i], c2, -l4[j] * kLog2e));
-          if (tail && qb0 + qb * 32 + acc_row(i, g) >= seg1) pv = 0.f;
-          s[qb][i] = pv;
-        }
-      }
+      for (int i = 0; i < 16; ++i)
+        s[qb][i] = __builtin_amdgcn_exp2f(fmaf(s[qb][i], c2, nl[4 * qb + (i >> 2)][i & 3]));
       pb[2 * qb] = acc_to_bf16(s[qb], 0);
       pb[2 * qb + 1] = acc_to_bf16(s[qb], 8);
     }
@@ -552,17 +562,15 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
     bf16x8 pr[BMQ / 16];
 #pragma unroll
     for (int u = 0; u < BMQ / 16; ++u) pr[u] = ld_bf16x8(p_mine + u * 64);
+    f32x4 d4[ROW_LOADS];
+#pragma unroll
+    for (int j = 0; j < ROW_LOADS; ++j) d4[j] = *reinterpret_cast<const f32x4 *>(&Ds[8 * j + 4 * g]);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&Ds[qb * 32 + 8 * r4 + 4 * g]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * r4 + j;
-          const float pv = (float)pr[2 * qb + i / 8][i % 8];
-          s[qb][i] = pv * (s[qb][i] - d4[j]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const float pv = (float)pr[2 * qb + i / 8][i % 8];
+        s[qb][i] = pv * (s[qb][i] - d4[4 * qb + (i >> 2)][i & 3]);
       }
       pb[2 * qb] = acc_to_bf16(s[qb], 0);
       pb[2 * qb + 1] = acc_to_bf16(s[qb], 8);
@@ -576,23 +584,20 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
 #pragma unroll
   for (int u = 0; u < BMQ / 16; ++u) pb[u] = bf16x8{};
   for (int e = tid * 8; e < TILE; e += 64 * KV_NW * 8) st_bf16x8(st3 + e, bf16x8{});
-  issue(S0{}, 0);
-  issue(std::integral_constant<int, 1>{}, 1);
-  issue(std::integral_constant<int, 2>{}, 2);
-  wait_vmem_le<2 * PER_TILE>();  // this wave's loads of tile 0
-  phase_barrier();  // tile 0 and the zeroed stage visible
 
   // Both roles run the same whole number of 4-step groups (every step loads,
   // waits and passes two barriers; work is skipped past the last tile), so the
   // loop has a single exit and barrier counts match across roles.
   if (role == 0) {
+    load_rows(0);
+    phase_barrier();  // tile 0 and the zeroed stage visible
     rows_x_key(qst(S0{}));  // S(0)
     auto step = [&](auto stage, int t) __attribute__((always_inline)) {
       constexpr int SG = decltype(stage)::value;
-      if (t < ntq) softmax(lst(stage), t);
-      wait_vmem_le<PER_TILE>();  // this wave's loads of tile t+1
+      wait_vmem();  // lse of tile t
+      if (t < ntq) softmax();
+      load_rows(t + 1);
       phase_barrier();  // P(t) and tile t+1 visible
-      issue(std::integral_constant<int, (SG + 3) % KV_NS>{}, t + 3);
       if (t < ntq) {  // one basic block, scheduled as an MFMA / LDS-read pipeline
         accumulate(gst(stage));  // dV(t)
         // S(t+1); past the last tile the stage holds a repeat of the last
@@ -609,6 +614,11 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
       step(std::integral_constant<int, 3>{}, t + 3);
     }
   } else {
+    issue(S0{}, 0);
+    issue(std::integral_constant<int, 1>{}, 1);
+    issue(std::integral_constant<int, 2>{}, 2);
+    wait_vmem_le<2 * PER_TILE>();  // this wave's loads of tile 0
+    phase_barrier();  // tile 0 and the zeroed stage visible
     auto step = [&](auto stage, int t) __attribute__((always_inline)) {
       constexpr int SG = decltype(stage)::value;
       if (t < ntq) {  // one basic block, scheduled as an MFMA / LDS-read pipeline

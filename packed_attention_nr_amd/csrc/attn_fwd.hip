@@ -109,8 +109,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
   auto issue = [&](auto stage, int t) __attribute__((always_inline)) {
     if (t >= ntiles) return;
     const int kb0 = seg0 + t * BN;
-    kload.issue(kst(stage), kh, kb0, seg1 - 1, p.total_tokens);
-    vload.issue(vst(stage), vv, kb0, seg1 - 1, p.total_tokens);
+    kload.issue(kst(stage), kh, kb0, seg1 - 1);
+    vload.issue(vst(stage), vv, kb0, seg1 - 1);
   };
 
 

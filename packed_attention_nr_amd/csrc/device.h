@@ -148,13 +148,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferFlags);
 }
 
-// Bytes addressable from element `first` of a [rows][stride] tensor through
-// `row_elems` elements of its last row, capped to the 32-bit buffer range.
-__device__ __forceinline__ uint32_t rsrc_bytes(int64_t rows_left, int64_t stride, int row_elems, int elt) {
-  const int64_t b = ((rows_left - 1) * stride + row_elems) * elt;
-  return b > 0x7FFFFFFF ? 0x7FFFFFFFu : (uint32_t)b;
-}
-
 // SIZE-byte global -> LDS copy for every lane of the wave: lane l's bytes at
 // rsrc + voffset land at lds_wave_base + SIZE*l (lds_wave_base wave-uniform).
 template <int SIZE>
@@ -241,36 +234,39 @@ struct TileLoader {
   static constexpr int RPL = 64 / CPR;          // rows per wave-wide load
   static constexpr int LOADS = ROWS / RPL / NW; // loads per wave
   static_assert(ROWS % (RPL * NW) == 0, "tile rows must split evenly over the waves");
-  int r0;                 // tile row of this lane in load 0
   int lds0;               // element offset of this wave's first load (uniform)
-  uint32_t rowb[LOADS];   // byte offset of the lane's row, per load
-  uint32_t chunkb[LOADS]; // byte offset of the logical chunk in the row
-  int64_t stride;         // elements between source rows
+  uint32_t off[LOADS];    // byte offset of the lane's row and logical chunk, per load
+  uint32_t stride_b;      // bytes between source rows
 
+  // row_stride in elements; ROWS rows of it must span under 4 GiB.
   __device__ __forceinline__ void init(int wave_uniform, int lane, int64_t row_stride) {
-    stride = row_stride;
-    r0 = wave_uniform * LOADS * RPL + lane / CPR;
+    stride_b = (uint32_t)(2 * row_stride);
+    const int r0 = wave_uniform * LOADS * RPL + lane / CPR;
     lds0 = wave_uniform * LOADS * RPL * D;
     const int pc = lane % CPR;
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      rowb[u] = (uint32_t)((r0 + u * RPL) * row_stride * 2);
-      chunkb[u] = (uint32_t)(16 * (pc ^ swz<CPR, SW>(r0 + u * RPL)));
-    }
-  }
-  // Source rows kb0 + r for r < ROWS, clamped to last_row (>= kb0); base =
-  // element (0, 0) of the source at the wanted head, rows_total = its rows.
-  __device__ __forceinline__ void issue(bf16 *tile, const bf16 *base, int64_t kb0, int64_t last_row,
-                                        int64_t rows_total) const {
-    const int64_t k0 = kb0 < last_row ? kb0 : last_row;  // a tile wholly past last_row repeats it
-    const bf16 *b0 = base + k0 * stride;
-    const rsrc_t r = make_rsrc(b0, rsrc_bytes(rows_total - k0, stride, D, 2));
-    const uint32_t lastb = (uint32_t)((last_row - k0) * stride * 2);
-#pragma unroll
     for (int u = 0; u < LOADS; ++u)
-      buf2lds<16>(r, min(rowb[u], lastb) + chunkb[u], tile + lds0 + u * RPL * D);
+      off[u] = (uint32_t)(r0 + u * RPL) * stride_b + (uint32_t)(16 * (pc ^ swz<CPR, SW>(r0 + u * RPL)));
+  }
+  // Source rows kb0 + r for r < ROWS; base = element (0, 0) of the source at
+  // the wanted head. Rows past last_row are not read and land as zeros: the
+  // descriptor ends with the last valid row (a buffer load past a
+  // descriptor's size returns zero words).
+  __device__ __forceinline__ void issue(bf16 *tile, const bf16 *base, int kb0, int last_row) const {
+    const char *b0 = reinterpret_cast<const char *>(base) + (uint64_t)(uint32_t)kb0 * stride_b;
+    const int rows = last_row + 1 - kb0;
+    const uint32_t bytes = rows <= 0 ? 0u : (uint32_t)((rows < ROWS ? rows : ROWS) - 1) * stride_b + 2 * D;
+    const rsrc_t r = make_rsrc(b0, bytes);
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) buf2lds<16>(r, off[u], tile + lds0 + u * RPL * D);
   }
 };
+
+// Four consecutive fp32 words at byte offset voffset of a buffer, into
+// registers; words past the descriptor's size read as zero.
+__device__ __forceinline__ f32x4 buf_load_f32x4(rsrc_t r, uint32_t voffset) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, 0, 0));
+}
 
 // Swizzled counterpart of lds_read_tr (same fragment, same k order).
 template <int D, int SW>

@@ -20,7 +20,7 @@ constexpr int kFwdTileF32 = 128;
 constexpr int kBwdTile = 128;
 // Limits checked by the plan.
 constexpr int kMaxGridSide = 32768;             // row and col fit in 15 bits of tok_meta
-constexpr int64_t kMaxTokens = 1ll << 30;
+constexpr int64_t kMaxTokens = 1ll << 29;  // byte offsets of [N] fp32 vectors fit 31 bits
 constexpr int64_t kMaxElements = 1ll << 40;     // N*H*d
 // Prologue backward: tokens per block and the cap on blocks (= gain partials).
 constexpr int kPbwdTokensPerBlock = 64;
