@@ -148,6 +148,7 @@ def _desc_call(text, gh, gw, H=2, d=64, dtype=1, theta=1e4, eps=1e-6, budget=0, 
     (dict(text=[3], gh=[2], gw=[2], eps=-1.0), 1),       # bad eps
     (dict(text=[3], gh=[2], gw=[2], eps=float("nan")), 1),
     (dict(text=[30, 5], gh=[4, 1], gw=[4, 1], budget=40), 4),   # over budget (52 tokens)
+    (dict(text=[0, 0], gh=[20000, 20000], gw=[20000, 20000]), 1),  # over 2^29 tokens
 ])
 def test_plan_rejects_invalid_descriptors(L, case, code):
     st, _ = _desc_call(**case)
@@ -200,6 +201,7 @@ def _fwd(plan, **kw):
     (dict(q=_p(1) + 8), 1),               # misaligned
     (dict(q_stride=64), 1),               # stride < H*d
     (dict(k_stride=132), 1),              # not a multiple of 8
+    (dict(v_stride=(1 << 24) + 8), 1),    # above the largest accepted stride
     (dict(gains=None), 1),
     (dict(o=None), 1),
     (dict(k_hat=None), 1),                # only one of q_hat / k_hat
@@ -242,6 +244,7 @@ def _bwd(plan, ws_bytes=None, **kw):
     (dict(dq=_p(12) + 16), 1),            # dq overlaps dk
     (dict(dv=_p(3)), 1),                  # dv overlaps v
     (dict(dout_stride=64), 1),
+    (dict(dout_stride=(1 << 24) + 8), 1),
     (dict(ws=None), 1),
     (dict(stages=16), 1),
     (dict(ws_bytes=64), 3),
