@@ -389,18 +389,18 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
 // Each tile takes two phases between workgroup barriers; in each phase one
 // role issues matrix instructions while the other does its vector and
 // memory work:
-//   phase 1: P/dV waves: softmax(t) -> P(t) to LDS; load lse(t+1)
+//   phase 1: P/dV waves: softmax(t) -> P(t) to LDS
 //            dS/dK waves: dK(t-1), dP(t)
 //   phase 2: P/dV waves: dV(t), S(t+1)
 //            dS/dK waves: load tile t+3; dS(t) (reads P(t))
-// Only the dS/dK waves load tiles: Q-hat / dO (and D) come by direct
-// global->LDS loads into a 4-stage ring; tile t+3 reuses the stage of tile
-// t-1, whose last reader (dK(t-1)) ran before the barrier that opens phase 2
-// of tile t. They wait for their loads of tile t+1 before that barrier, so
-// tile t+1 is visible one phase before S(t+1) reads it. Issuing loads costs
-// issue cycles, so it goes to the waves that are not feeding the matrix
-// cores in that phase. The P/dV waves take the per-query lse straight into
-// registers, one tile ahead, after the softmax that used the previous one.
+// Only the dS/dK waves load: Q-hat / dO tiles and the tile's lse and D come
+// by direct global->LDS loads into a 4-stage ring; tile t+3 reuses the stage
+// of tile t-1, whose last reader (dK(t-1)) ran before the barrier that opens
+// phase 2 of tile t. They wait for their loads of tile t+1 before that
+// barrier, so tile t+1 is visible one phase before S(t+1) reads it. Loads
+// cost issue cycles, so they go to the waves that are not feeding the matrix
+// cores in that phase; and no load in the loop returns into registers, whose
+// writes would compete with the matrix instructions on the same SIMD.
 // ---------------------------------------------------------------------------
 namespace bwd {
 constexpr int KV_NW = 8;   // waves of a dK/dV workgroup
@@ -414,10 +414,10 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   constexpr int DB = D / 32;
   constexpr int TILE = BMQ * D;
   static_assert(KV_NS == 4 && BMQ == 64 && KT == 32 * KV_NW / 2, "layout below");
-  // One LDS object per ring stage, [Q-hat tile | dO tile | D]: distinct
-  // objects (at most 8 of them receiving direct loads) let the compiler prove
-  // that loads into one stage do not alias reads of another.
-  constexpr int STAGE = 2 * TILE + 2 * BMQ;  // bf16 elements
+  // One LDS object per ring stage, [Q-hat tile | dO tile | lse | D]:
+  // distinct objects (at most 8 of them receiving direct loads) let the
+  // compiler prove that loads into one stage do not alias reads of another.
+  constexpr int STAGE = 2 * TILE + 4 * BMQ;  // bf16 elements
   __shared__ __attribute__((aligned(16))) bf16 st0[STAGE], st1[STAGE], st2[STAGE], st3[STAGE];
   __shared__ __attribute__((aligned(16))) uint4 p_s[4 * (BMQ / 16) * 64];
   __shared__ __attribute__((aligned(16))) float g_s[2 * D];  // K gains: text, image
@@ -428,8 +428,11 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   };
   auto qst = [&](auto stage) __attribute__((always_inline)) -> bf16 * { return stg(stage); };
   auto gst = [&](auto stage) __attribute__((always_inline)) -> bf16 * { return stg(stage) + TILE; };
-  auto dst = [&](auto stage) __attribute__((always_inline)) -> float * {
+  auto lst = [&](auto stage) __attribute__((always_inline)) -> float * {
     return reinterpret_cast<float *>(stg(stage) + 2 * TILE);
+  };
+  auto dst = [&](auto stage) __attribute__((always_inline)) -> float * {
+    return reinterpret_cast<float *>(stg(stage) + 2 * TILE) + BMQ;
   };
 
   const int H = p.num_heads;
@@ -488,26 +491,26 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   // so S = 0 and P = exp2(0) = 1 there, finite, and both dV^T += dO^T P and
   // dK^T += Q-hat^T dS add zero for them.
   const uint32_t vec_bytes = 4u * (uint32_t)seg1;  // lse / D words up to the segment end
-  // The dS/dK waves also load D of the tile's queries into the stage (the
-  // same 64 words from each of the four).
+  // The dS/dK waves also load lse and D of the tile's queries into the stage
+  // (the same 64 words of each from each of the four).
+  const rsrc_t l_rs = make_rsrc(lse_h, vec_bytes);
   const rsrc_t d_rs = make_rsrc(dlt_h, vec_bytes);
   auto issue = [&](auto stage, int t) __attribute__((always_inline)) {
     const int qb0 = seg0 + min(t, ntq - 1) * BMQ;
     qload.issue(qst(stage), qh, qb0, seg1 - 1);  // branch-free: exact load counts
     gload.issue(gst(stage), go, qb0, seg1 - 1);
+    buf2lds<4>(l_rs, 4u * (uint32_t)(qb0 + lane), lst(stage));
     buf2lds<4>(d_rs, 4u * (uint32_t)(qb0 + lane), dst(stage));
   };
-  constexpr int PER_TILE = 2 * LQ + 1;  // loads per dS/dK wave per tile
-  // lse of a tile's queries in the P/dV waves' registers: lv[4 qb + r4] holds
-  // queries qb*32 + 8*r4 + 4*g + 0..3 of the tile, the rows of accumulator
-  // registers 4*r4..4*r4+3 of block qb in this lane.
-  const rsrc_t lv_rs = make_rsrc(lse_h, vec_bytes);
-  constexpr int ROW_LOADS = 2 * 4;  // f32x4 loads per wave per tile
-  f32x4 lv[ROW_LOADS];
-  auto load_rows = [&](int t) __attribute__((always_inline)) {
-    const uint32_t qb0 = (uint32_t)(seg0 + min(t, ntq - 1) * BMQ);
+  constexpr int PER_TILE = 2 * LQ + 2;  // loads per dS/dK wave per tile
+  // A per-query vector of the tile (lse or D) for this lane's accumulator
+  // rows: v[4 qb + r4] holds queries qb*32 + 8*r4 + 4*g + 0..3, the rows of
+  // registers 4*r4..4*r4+3 of block qb. All eight reads are issued before
+  // the first use.
+  constexpr int ROW_LOADS = 2 * 4;
+  auto read_rows = [&](const float *vec, f32x4 (&v)[ROW_LOADS]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < ROW_LOADS; ++j) lv[j] = buf_load_f32x4(lv_rs, 4u * (qb0 + 8 * j + 4 * g));
+    for (int j = 0; j < ROW_LOADS; ++j) v[j] = *reinterpret_cast<const f32x4 *>(&vec[8 * j + 4 * g]);
   };
 
   f32x16 acc[DB];  // dV^T (role 0) or dK^T (role 1): lane = key, rows = d
@@ -542,10 +545,11 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
         acc[b] = mfma32(lds_read_tr_swz<D, SWZ_BOTH>(T, u * 16, b * 32, lane), pb[u], acc[b]);
   };
   // Role 0: P = exp2(S*c2 - lse*log2e).
-  auto softmax = [&]() __attribute__((always_inline)) {
+  auto softmax = [&](const float *Ls) __attribute__((always_inline)) {
     f32x4 nl[ROW_LOADS];
+    read_rows(Ls, nl);
 #pragma unroll
-    for (int j = 0; j < ROW_LOADS; ++j) nl[j] = lv[j] * -kLog2e;
+    for (int j = 0; j < ROW_LOADS; ++j) nl[j] = nl[j] * -kLog2e;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -563,8 +567,7 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
 #pragma unroll
     for (int u = 0; u < BMQ / 16; ++u) pr[u] = ld_bf16x8(p_mine + u * 64);
     f32x4 d4[ROW_LOADS];
-#pragma unroll
-    for (int j = 0; j < ROW_LOADS; ++j) d4[j] = *reinterpret_cast<const f32x4 *>(&Ds[8 * j + 4 * g]);
+    read_rows(Ds, d4);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -589,14 +592,11 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   // waits and passes two barriers; work is skipped past the last tile), so the
   // loop has a single exit and barrier counts match across roles.
   if (role == 0) {
-    load_rows(0);
     phase_barrier();  // tile 0 and the zeroed stage visible
     rows_x_key(qst(S0{}));  // S(0)
     auto step = [&](auto stage, int t) __attribute__((always_inline)) {
       constexpr int SG = decltype(stage)::value;
-      wait_vmem();  // lse of tile t
-      if (t < ntq) softmax();
-      load_rows(t + 1);
+      if (t < ntq) softmax(lst(stage));
       phase_barrier();  // P(t) and tile t+1 visible
       if (t < ntq) {  // one basic block, scheduled as an MFMA / LDS-read pipeline
         accumulate(gst(stage));  // dV(t)
