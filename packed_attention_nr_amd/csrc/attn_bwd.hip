@@ -389,18 +389,21 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
 // Each tile takes two phases between workgroup barriers; in each phase one
 // role issues matrix instructions while the other does its vector and
 // memory work:
-//   phase 1: P/dV waves: softmax(t) -> P(t) to LDS
+//   phase 1: P/dV waves: load Q-hat, lse of tile t+2; softmax(t) -> P(t) to LDS
 //            dS/dK waves: dK(t-1), dP(t)
 //   phase 2: P/dV waves: dV(t), S(t+1)
-//            dS/dK waves: load tile t+3; dS(t) (reads P(t))
-// Only the dS/dK waves load: Q-hat / dO tiles and the tile's lse and D come
-// by direct global->LDS loads into a 4-stage ring; tile t+3 reuses the stage
-// of tile t-1, whose last reader (dK(t-1)) ran before the barrier that opens
-// phase 2 of tile t. They wait for their loads of tile t+1 before that
-// barrier, so tile t+1 is visible one phase before S(t+1) reads it. Loads
-// cost issue cycles, so they go to the waves that are not feeding the matrix
-// cores in that phase; and no load in the loop returns into registers, whose
-// writes would compete with the matrix instructions on the same SIMD.
+//            dS/dK waves: load dO, D of tile t+3; dS(t) (reads P(t))
+// All tile data comes by direct global->LDS loads into a 4-stage ring. Tile
+// t+2 (phase 1 of tile t) reuses the stage of tile t-2 and tile t+3 (phase
+// 2) that of tile t-1; the last reader of either (dK(t-2), dK(t-1)) ran
+// before the barrier that precedes the load. Each wave waits for its own
+// loads of tile t+1 before the barrier that opens phase 2 of tile t, so tile
+// t+1 is visible one phase before S(t+1) reads it. Loads cost issue cycles,
+// so each role issues its half in the phase where it is not feeding the
+// matrix cores, and no load in the loop returns into registers (such returns
+// compete with the matrix instructions of the other wave on the SIMD). The
+// matrix blocks run at raised wave priority, so that the partner wave's
+// vector instructions do not delay their MFMA and LDS-read issue.
 // ---------------------------------------------------------------------------
 namespace bwd {
 constexpr int KV_NW = 8;   // waves of a dK/dV workgroup
@@ -477,7 +480,8 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   }
 
   const int ntq = (seg1 - seg0 + BMQ - 1) / BMQ;
-  // Loaders run by the four dS/dK waves (sub = their index among them).
+  // Q-hat tiles are loaded by the four P/dV waves, dO tiles by the four dS/dK
+  // waves (sub = a wave's index within its role).
   TileLoader<D, SWZ_BOTH, BMQ, KV_NW / 2> qload, gload;
   qload.init(sub, lane, HD);
   gload.init(sub, lane, gstride);
@@ -491,18 +495,21 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   // so S = 0 and P = exp2(0) = 1 there, finite, and both dV^T += dO^T P and
   // dK^T += Q-hat^T dS add zero for them.
   const uint32_t vec_bytes = 4u * (uint32_t)seg1;  // lse / D words up to the segment end
-  // The dS/dK waves also load lse and D of the tile's queries into the stage
-  // (the same 64 words of each from each of the four).
+  // With its tile, each role loads one per-query vector into the stage: lse
+  // (P/dV waves) or D (dS/dK waves), the same 64 words from each of the four.
   const rsrc_t l_rs = make_rsrc(lse_h, vec_bytes);
   const rsrc_t d_rs = make_rsrc(dlt_h, vec_bytes);
-  auto issue = [&](auto stage, int t) __attribute__((always_inline)) {
+  auto issue_q = [&](auto stage, int t) __attribute__((always_inline)) {
     const int qb0 = seg0 + min(t, ntq - 1) * BMQ;
     qload.issue(qst(stage), qh, qb0, seg1 - 1);  // branch-free: exact load counts
-    gload.issue(gst(stage), go, qb0, seg1 - 1);
     buf2lds<4>(l_rs, 4u * (uint32_t)(qb0 + lane), lst(stage));
+  };
+  auto issue_g = [&](auto stage, int t) __attribute__((always_inline)) {
+    const int qb0 = seg0 + min(t, ntq - 1) * BMQ;
+    gload.issue(gst(stage), go, qb0, seg1 - 1);
     buf2lds<4>(d_rs, 4u * (uint32_t)(qb0 + lane), dst(stage));
   };
-  constexpr int PER_TILE = 2 * LQ + 2;  // loads per dS/dK wave per tile
+  constexpr int PER_TILE = LQ + 1;  // loads per wave per tile
   // A per-query vector of the tile (lse or D) for this lane's accumulator
   // rows: v[4 qb + r4] holds queries qb*32 + 8*r4 + 4*g + 0..3, the rows of
   // registers 4*r4..4*r4+3 of block qb. All eight reads are issued before
@@ -592,12 +599,18 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   // waits and passes two barriers; work is skipped past the last tile), so the
   // loop has a single exit and barrier counts match across roles.
   if (role == 0) {
+    issue_q(S0{}, 0);
+    issue_q(std::integral_constant<int, 1>{}, 1);
+    wait_vmem_le<PER_TILE>();  // this wave's loads of tile 0
     phase_barrier();  // tile 0 and the zeroed stage visible
     rows_x_key(qst(S0{}));  // S(0)
     auto step = [&](auto stage, int t) __attribute__((always_inline)) {
       constexpr int SG = decltype(stage)::value;
+      issue_q(std::integral_constant<int, (SG + 2) % KV_NS>{}, t + 2);
       if (t < ntq) softmax(lst(stage));
+      wait_vmem_le<PER_TILE>();  // this wave's loads of tile t+1
       phase_barrier();  // P(t) and tile t+1 visible
+      __builtin_amdgcn_s_setprio(3);
       if (t < ntq) {  // one basic block, scheduled as an MFMA / LDS-read pipeline
         accumulate(gst(stage));  // dV(t)
         // S(t+1); past the last tile the stage holds a repeat of the last
@@ -605,6 +618,8 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
         rows_x_key(qst(std::integral_constant<int, (SG + 1) % KV_NS>{}));
         pipeline_mfma_ds<(BMQ / 16) * DB + 2 * KS, (BMQ / 16) * DB, 2, 1, 4>();
       }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       phase_barrier();  // P(t) consumed
     };
     for (int t = 0; t < ntq; t += KV_NS) {
@@ -614,21 +629,24 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
       step(std::integral_constant<int, 3>{}, t + 3);
     }
   } else {
-    issue(S0{}, 0);
-    issue(std::integral_constant<int, 1>{}, 1);
-    issue(std::integral_constant<int, 2>{}, 2);
+    issue_g(S0{}, 0);
+    issue_g(std::integral_constant<int, 1>{}, 1);
+    issue_g(std::integral_constant<int, 2>{}, 2);
     wait_vmem_le<2 * PER_TILE>();  // this wave's loads of tile 0
     phase_barrier();  // tile 0 and the zeroed stage visible
     auto step = [&](auto stage, int t) __attribute__((always_inline)) {
       constexpr int SG = decltype(stage)::value;
+      __builtin_amdgcn_s_setprio(3);
       if (t < ntq) {  // one basic block, scheduled as an MFMA / LDS-read pipeline
         accumulate(qst(std::integral_constant<int, (SG + 3) % KV_NS>{}));  // dK(t-1)
         rows_x_key(gst(stage));  // dP(t)
         pipeline_mfma_ds<(BMQ / 16) * DB + 2 * KS, (BMQ / 16) * DB, 2, 1, 4>();
       }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       wait_vmem_le<PER_TILE>();  // this wave's loads of tile t+1
       phase_barrier();  // P(t) and tile t+1 visible
-      issue(std::integral_constant<int, (SG + 3) % KV_NS>{}, t + 3);
+      issue_g(std::integral_constant<int, (SG + 3) % KV_NS>{}, t + 3);
       if (t < ntq) {
         dscores(dst(stage));  // dS(t)
         if (t + 1 == ntq) accumulate(qst(stage));  // last dK
