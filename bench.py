@@ -92,6 +92,96 @@ def cpu_baseline(inp, heads):
                        f"of the same pack ({dt:.1f} s); throughput of that sample")
 
 
+def pass_runner(pam, torch, dev, text, hs, ws, H, d, backward, seed):
+    """A callable that runs one whole pass (forward, and backward if asked)
+    of the library on a pack of the given geometry. Inputs are drawn on the
+    device: only the timing of such passes is used."""
+    pack = pam.Pack(text, hs, ws, H, d, "bf16", device=dev)
+    N = pack.N
+    g = torch.Generator(device=dev).manual_seed(seed)
+    rnd = lambda: torch.randn((N, H, d), generator=g, device=dev).to(torch.bfloat16)
+    q, k, v = rnd(), rnd(), rnd()
+    gains = 1.0 + 0.1 * torch.randn((4, d), generator=g, device=dev)
+    bf = torch.bfloat16
+    o = torch.empty((N, H, d), dtype=bf, device=dev)
+    q_hat, k_hat = torch.empty_like(o), torch.empty_like(o)
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev)
+    rstd = torch.empty((2, N, H), dtype=torch.float32, device=dev)
+    fa = dict(q=q, k=k, v=v, q_stride=H * d, k_stride=H * d, v_stride=H * d, gains=gains,
+              o=o, lse=lse, q_hat=q_hat, k_hat=k_hat, rstd=rstd)
+    if backward:
+        do = rnd()
+        dq, dk, dv = torch.empty_like(o), torch.empty_like(o), torch.empty_like(o)
+        dgains = torch.empty((4, d), dtype=torch.float32, device=dev)
+        wsb = pack.workspace("bwd")
+        ba = dict(q=q, k=k, v=v, q_hat=q_hat, k_hat=k_hat, o=o, dout=do, q_stride=H * d,
+                  k_stride=H * d, v_stride=H * d, dout_stride=H * d, gains=gains, lse=lse,
+                  rstd=rstd, dq=dq, dk=dk, dv=dv, dgains=dgains, workspace=wsb)
+
+    def run():
+        pam.mmdit_attn_fwd(pack.plan, pack.blob_dev, **fa)
+        if backward:
+            pam.mmdit_attn_bwd(pack.plan, pack.blob_dev, **ba)
+    return run
+
+
+def time_passes(torch, runs, reps=20):
+    """Milliseconds per round of the given callables run back to back."""
+    for _ in range(3):
+        for r in runs:
+            r()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        for r in runs:
+            r()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def packed_cfg_1024(pam, torch, dev, H, d):
+    """Packed classifier-free guidance at 1024^2: the conditional sample
+    (512 text tokens + 64x64 latents) and its unconditional twin (same grid,
+    a null prompt) as one forward pass, against the two branches as two
+    passes. Null prompt of 0 tokens (empty) and of 512 (padded prompt)."""
+    out = {}
+    for null in (0, 512):
+        t, h, w = pam.mmdit_cfg_pack_desc([512], [64], [64], null)
+        packed = pass_runner(pam, torch, dev, t, h, w, H, d, False, 1)
+        cond = pass_runner(pam, torch, dev, t[:1], h[:1], w[:1], H, d, False, 2)
+        unc = pass_runner(pam, torch, dev, t[1:], h[1:], w[1:], H, d, False, 3)
+        t_packed = time_passes(torch, [packed], 50)
+        t_two = time_passes(torch, [cond, unc], 50)
+        out[f"null_text_{null}"] = {"packed_ms": round(t_packed, 4), "two_passes_ms": round(t_two, 4),
+                                    "speedup": round(t_two / t_packed, 3)}
+    return out
+
+
+def bucket_padding(pam, torch, dev, inp, H, d):
+    """The same samples as dense per-bucket batches: one batch per distinct
+    latent grid, every text padded to the longest prompt of the workload's
+    range (512, or the longest drawn), padded tokens computed. Forward +
+    backward of all bucket batches, against the packed pass."""
+    text_pad = max(512, int(np.max(inp.text_len)))
+    buckets = {}
+    for hh, ww in zip(inp.grid_h.tolist(), inp.grid_w.tolist()):
+        buckets[(hh, ww)] = buckets.get((hh, ww), 0) + 1
+    runs = []
+    padded_l2 = 0.0
+    for j, ((hh, ww), n) in enumerate(sorted(buckets.items())):
+        runs.append(pass_runner(pam, torch, dev, [text_pad] * n, [hh] * n, [ww] * n, H, d, True, 10 + j))
+        padded_l2 += n * float(text_pad + hh * ww) ** 2
+    t_buckets = time_passes(torch, runs, 10)
+    packed = pass_runner(pam, torch, dev, inp.text_len, inp.grid_h, inp.grid_w, H, d, True, 9)
+    packed_ms = time_passes(torch, [packed], 10)
+    return {"buckets": len(buckets), "text_padded_to": text_pad,
+            "padded_flop_ratio": round(padded_l2 / sum_l2(inp), 3),
+            "bucketed_ms": round(t_buckets, 4), "packed_ms": round(packed_ms, 4),
+            "time_ratio": round(t_buckets / packed_ms, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +316,9 @@ def main():
     ms_layer_1024 = e0.elapsed_time(e1) / reps
     gen_fwd_tflops = 4.0 * g.heads * g.head_dim * sum_l2(g) / (ms_layer_1024 * 1e-3) / 1e12
 
+    cfg = packed_cfg_1024(pam, torch, dev, H, d)
+    bucket = bucket_padding(pam, torch, dev, inp, H, d)
+
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -259,6 +352,8 @@ def main():
         "ms_per_layer_1024": round(ms_layer_1024, 4),
         "gen1024_fwd_tflops": round(gen_fwd_tflops, 2),
         "roofline": roof,
+        "packed_cfg_1024": cfg,
+        "bucket_padding": bucket,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_heads)

@@ -123,6 +123,25 @@ typedef struct {
 mmdit_status mmdit_pack_plan(const mmdit_pack_desc *desc, mmdit_plan *plan,
                              void *host_blob, uint64_t host_blob_bytes);
 
+/* Packed classifier-free guidance (picx.dev "Mage-Flow ...", section
+ * "Native-Resolution MMDiT (NR-MMDiT)", the packed CFG inference bullet, and
+ * its results on native-resolution packing, Table 3; the video page at
+ * [00:04:03]): one pack that evaluates the conditional and unconditional
+ * branches in a single pass. Writes the descriptor of a pack of 2S samples:
+ * the S samples of `cond` (conditional branches) followed, in the same order,
+ * by their unconditional twins, which keep the latent grid and carry
+ * null_text_len text tokens (0 = an empty prompt) instead of the prompt.
+ * The caller provides the three arrays (capacity >= 2S entries each); *out
+ * gets them and every other field of *cond (heads, d, dtype, theta, eps,
+ * token budget, which the plan then checks against the doubled pack). Token
+ * order of the pack: all conditional samples, then all unconditional ones.
+ * Host only. Errors: INVALID_ARG (NULL pointers, S < 1, null_text_len < 0,
+ * capacity < 2S, or a text-only conditional sample whose twin would be empty
+ * because null_text_len is 0); nothing is written on error. */
+mmdit_status mmdit_cfg_pack_desc(const mmdit_pack_desc *cond, int32_t null_text_len,
+                                 int32_t *text_len, int32_t *grid_h, int32_t *grid_w,
+                                 int32_t capacity, mmdit_pack_desc *out);
+
 /* Stage selection for mmdit_fwd_args.stages / mmdit_bwd_args.stages. 0 = all.
  * A later stage alone reads what the earlier ones wrote (e.g. ATTENTION alone
  * reads the caller's q_hat / k_hat). */

@@ -92,6 +92,10 @@ def lib():
         L = C.CDLL(LIB_PATH)
         L.mmdit_pack_plan.restype = C.c_int
         L.mmdit_pack_plan.argtypes = [C.POINTER(PackDesc), C.POINTER(Plan), C.c_void_p, C.c_uint64]
+        L.mmdit_cfg_pack_desc.restype = C.c_int
+        L.mmdit_cfg_pack_desc.argtypes = [C.POINTER(PackDesc), C.c_int32, C.POINTER(C.c_int32),
+                                          C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.c_int32,
+                                          C.POINTER(PackDesc)]
         L.mmdit_attn_fwd.restype = C.c_int
         L.mmdit_attn_fwd.argtypes = [C.POINTER(Plan), C.c_void_p, C.POINTER(FwdArgs), C.c_void_p,
                                      C.c_uint64, C.c_void_p]
@@ -146,6 +150,29 @@ def mmdit_pack_plan(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequ
     blob = np.zeros(plan.blob_bytes, dtype=np.uint8)
     _check(lib().mmdit_pack_plan(C.byref(desc), C.byref(plan), blob.ctypes.data, blob.nbytes))
     return plan, blob
+
+
+def mmdit_cfg_pack_desc(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int],
+                        null_text_len: int = 0):
+    """Run mmdit_cfg_pack_desc on a conditional pack's geometry. Returns the
+    (text_len, grid_h, grid_w) int32 arrays of the packed conditional +
+    unconditional pack: the conditional samples first, then their twins with
+    the same grids and null_text_len text tokens."""
+    t = np.ascontiguousarray(text_len, dtype=np.int32)
+    h = np.ascontiguousarray(grid_h, dtype=np.int32)
+    w = np.ascontiguousarray(grid_w, dtype=np.int32)
+    if not (len(t) == len(h) == len(w)):
+        raise ValueError("text_len, grid_h and grid_w must have the same length")
+    P = C.POINTER(C.c_int32)
+    cond = PackDesc(len(t), t.ctypes.data_as(P), h.ctypes.data_as(P), w.ctypes.data_as(P),
+                    1, 64, MMDIT_BF16, 10000.0, 1e-6, 0)
+    n = 2 * len(t)
+    ot, oh, ow = (np.zeros(max(n, 1), dtype=np.int32) for _ in range(3))
+    out = PackDesc()
+    _check(lib().mmdit_cfg_pack_desc(C.byref(cond), int(null_text_len), ot.ctypes.data_as(P),
+                                     oh.ctypes.data_as(P), ow.ctypes.data_as(P), n, C.byref(out)))
+    assert out.num_samples == n
+    return ot[:n].copy(), oh[:n].copy(), ow[:n].copy()
 
 
 def _ptr(t) -> Optional[int]:

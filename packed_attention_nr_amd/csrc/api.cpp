@@ -290,6 +290,12 @@ mmdit_status mmdit_pack_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void
   }
 }
 
+mmdit_status mmdit_cfg_pack_desc(const mmdit_pack_desc *cond, int32_t null_text_len, int32_t *text_len,
+                                 int32_t *grid_h, int32_t *grid_w, int32_t capacity, mmdit_pack_desc *out) {
+  mmdit::clear_error();
+  return mmdit::cfg_pack_desc(cond, null_text_len, text_len, grid_h, grid_w, capacity, out);
+}
+
 mmdit_status mmdit_attn_fwd(const mmdit_plan *plan, const void *plan_blob_dev, const mmdit_fwd_args *args,
                             void *workspace, uint64_t workspace_bytes, void *hip_stream) {
   mmdit::clear_error();

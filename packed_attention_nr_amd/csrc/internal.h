@@ -48,6 +48,8 @@ void clear_error();
 uint64_t plan_fingerprint(const mmdit_plan &p);
 mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *host_blob,
                         uint64_t host_blob_bytes);
+mmdit_status cfg_pack_desc(const mmdit_pack_desc *cond, int32_t null_text_len, int32_t *text_len,
+                           int32_t *grid_h, int32_t *grid_w, int32_t capacity, mmdit_pack_desc *out);
 uint64_t bwd_partial_blocks(int64_t n_tokens);
 
 // Backward workspace layout (byte offsets, each 256-byte aligned): D [H][N],

@@ -261,4 +261,32 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
   return MMDIT_OK;
 }
 
+mmdit_status cfg_pack_desc(const mmdit_pack_desc *cond, int32_t null_text_len, int32_t *text_len,
+                           int32_t *grid_h, int32_t *grid_w, int32_t capacity, mmdit_pack_desc *out) {
+  if (!cond || !out || !text_len || !grid_h || !grid_w)
+    return fail(MMDIT_ERR_INVALID_ARG, "cond, out and the three arrays must not be NULL");
+  const int32_t S = cond->num_samples;
+  if (S < 1) return fail(MMDIT_ERR_INVALID_ARG, "num_samples must be >= 1");
+  if (!cond->text_len || !cond->grid_h || !cond->grid_w)
+    return fail(MMDIT_ERR_INVALID_ARG, "cond's text_len, grid_h and grid_w must not be NULL");
+  if (null_text_len < 0) return fail(MMDIT_ERR_INVALID_ARG, "null_text_len must be >= 0");
+  if (S > INT32_MAX / 2 || capacity < 2 * S)
+    return fail(MMDIT_ERR_INVALID_ARG, "capacity %d is below 2 * num_samples (%d)", capacity, S);
+  for (int32_t i = 0; i < S; ++i)
+    if (null_text_len == 0 && (cond->grid_h[i] == 0 || cond->grid_w[i] == 0))
+      return fail(MMDIT_ERR_INVALID_ARG, "sample %d is text-only: its unconditional twin would be empty", i);
+  for (int32_t i = 0; i < S; ++i) {
+    text_len[i] = cond->text_len[i];
+    grid_h[i] = grid_h[S + i] = cond->grid_h[i];
+    grid_w[i] = grid_w[S + i] = cond->grid_w[i];
+    text_len[S + i] = null_text_len;
+  }
+  *out = *cond;
+  out->num_samples = 2 * S;
+  out->text_len = text_len;
+  out->grid_h = grid_h;
+  out->grid_w = grid_w;
+  return MMDIT_OK;
+}
+
 }  // namespace mmdit

@@ -259,3 +259,38 @@ def _bwd(plan, ws_bytes=None, **kw):
 def test_bwd_rejects_invalid_arguments(small_plan, kw, code):
     ws_bytes = kw.pop("ws_bytes", None)
     assert _bwd(small_plan, ws_bytes=ws_bytes, **kw) == code, pam.mmdit_last_error()
+
+
+# --------------------------------------------------------------------------
+# packed classifier-free guidance: descriptor of conditional + unconditional
+# --------------------------------------------------------------------------
+def test_cfg_pack_desc_geometry(L):
+    t, h, w = pam.mmdit_cfg_pack_desc([5, 0, 12], [2, 4, 0], [3, 4, 0], null_text_len=3)
+    assert t.tolist() == [5, 0, 12, 3, 3, 3]
+    assert h.tolist() == [2, 4, 0, 2, 4, 0]
+    assert w.tolist() == [3, 4, 0, 3, 4, 0]
+    plan, blob = pam.mmdit_pack_plan(t, h, w, 2, 64, 1)
+    cu = np.frombuffer(blob.tobytes(), dtype=np.int32)[plan.off_cu_seqlens // 4:][:7]
+    assert cu.tolist() == [0, 11, 27, 39, 48, 67, 70]
+
+
+def test_cfg_pack_desc_rejects(L):
+    with pytest.raises(pam.MmditError):
+        pam.mmdit_cfg_pack_desc([5], [2], [3], null_text_len=-1)
+    with pytest.raises(pam.MmditError):       # text-only sample, empty null prompt
+        pam.mmdit_cfg_pack_desc([5, 7], [2, 0], [3, 0], null_text_len=0)
+    t = np.array([5, 1], np.int32); h = np.array([2, 3], np.int32); w = np.array([3, 3], np.int32)
+    P = C.POINTER(C.c_int32)
+    cond = pam.PackDesc(2, t.ctypes.data_as(P), h.ctypes.data_as(P), w.ctypes.data_as(P),
+                        2, 64, 1, 1e4, 1e-6, 20)
+    buf = [np.zeros(4, np.int32) for _ in range(3)]
+    out = pam.PackDesc()
+    st = pam.lib().mmdit_cfg_pack_desc(C.byref(cond), 0, *(b.ctypes.data_as(P) for b in buf), 3,
+                                       C.byref(out))
+    assert st == 1 and pam.mmdit_last_error()           # capacity below 2S
+    assert not buf[0].any()                              # nothing written on error
+    st = pam.lib().mmdit_cfg_pack_desc(C.byref(cond), 0, *(b.ctypes.data_as(P) for b in buf), 4,
+                                       C.byref(out))
+    assert st == 0 and out.num_samples == 4 and out.token_budget == 20
+    plan = pam.Plan()                                    # 6 + 10 + 6 + 9 = 31 tokens > 20
+    assert pam.lib().mmdit_pack_plan(C.byref(out), C.byref(plan), None, 0) == 4
