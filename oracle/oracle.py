@@ -20,6 +20,10 @@ Mage-Flow pages describe it:
   per (Q or K, text or image);
 * a per-sample 2D rotary embedding of image tokens by their own (row, col)
   (transcript at [00:03:16]; aiany.app entry, "Key Capabilities");
+* for editing, the source image's latents joined to the target latents in
+  the same sample and told apart by the frame dimension of a 3D rotary
+  embedding (picx.dev, section "Native-Resolution MMDiT (NR-MMDiT)",
+  conditioning bullet);
 * joint text+image self-attention restricted to each sample, i.e. block
   diagonal over the cumulative offsets (picx.dev, same section: FlashAttention
   with per-sample cumulative offsets).
@@ -37,17 +41,25 @@ are silent (each also listed in the design doc):
 * RoPE: the first d/2 dimensions rotate by the row index and the last d/2 by
   the column index, 0-based; inside each half, adjacent pairs (2j, 2j+1)
   rotate by angle pos * theta^(-4j/d), j < d/4; text tokens are not rotated;
+* editing packs: a sample's source grid follows its target grid (text,
+  target, source), the target on frame 0 and the source on frame 1; every
+  image token of such a pack turns by three axes, the first d/8 pairs by the
+  frame, the next 3d/16 by the row and the last 3d/16 by the column; pair j of
+  a section of n pairs turns by pos * theta^(-j/n) (which for n = d/4 is the
+  2D rule);
 * softmax scale 1/sqrt(d), no causal mask, no dropout, natural-log lse.
 
 Parity status of each function (how it is pinned by tests other than itself):
-``layout`` (pure-Python enumeration, token counts), ``rms_norm`` (closed
-forms), ``rope_apply`` (hand values at d=4 and d=8, norm preservation,
-relative-position property), ``attention_forward`` (pure-Python brute force,
+``layout`` (pure-Python enumeration, token counts, editing order),
+``rms_norm`` (closed forms), ``rope_apply`` (hand values at d=4 and d=8,
+norm preservation, relative-position property), ``rope_angles`` (hand
+values of the 2D and 3D schedules, 3D relative-position property, frame-0
+tokens unrotated on the frame pairs), ``attention_forward`` (pure-Python brute force,
 torch fp64 library attention, closed forms, packing invariants),
 ``attention_backward`` / ``rope_backward`` / ``rms_norm_backward``
 (central finite differences, torch fp64 autograd, closed forms).
-The RoPE pair layout, frequency schedule and position origin themselves are
-readings, not statements of the pages: against the pages they are parity
+The RoPE pair layout, frequency schedule, position origin and the 3D split
+themselves are readings, not statements of the pages: against the pages they are parity
 unpinned; the code is pinned only against that written reading.
 """
 from __future__ import annotations
@@ -58,7 +70,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "Layout", "layout", "rope_frequencies", "rope_angles", "rope_apply",
+    "Layout", "layout", "rope_frequencies", "rope_section_frequencies", "rope_sections",
+    "rope_angles", "rope_apply",
     "rope_backward", "rms_norm", "rms_norm_backward", "token_gains",
     "prologue", "attention_forward", "attention_backward", "forward",
     "backward",
@@ -77,13 +90,16 @@ class Layout:
     is_image: np.ndarray     # bool  [N]
     row: np.ndarray          # int64 [N], 0 for text tokens
     col: np.ndarray          # int64 [N], 0 for text tokens
+    frame: Optional[np.ndarray] = None  # int64 [N]: 1 for source-image tokens, else 0
+    three_axes: bool = False            # editing pack: RoPE over (frame, row, col)
 
     @property
     def num_tokens(self) -> int:
         return int(self.cu_seqlens[-1])
 
 
-def layout(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int]) -> Layout:
+def layout(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int],
+           src_h: Optional[Sequence[int]] = None, src_w: Optional[Sequence[int]] = None) -> Layout:
     """Packing of samples into one contiguous token batch.
 
     Sample i occupies tokens cu[i] .. cu[i+1]-1 where cu[i+1] = cu[i] + T_i + h_i*w_i:
@@ -93,11 +109,20 @@ def layout(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int]
     variable-length token sequence by flattening and is packed together with
     its text under cumulative offsets; transcript [00:03:16]: all samples share
     one contiguous batch.)
+
+    With src_h, src_w (an editing pack; picx.dev, same section, conditioning
+    bullet: the source latents are concatenated with the target latents), the
+    sample's sh_i x sw_i source grid follows its target grid, row-major, with
+    frame index 1; the target grid keeps frame 0, and the pack's RoPE runs over
+    three axes.
     """
     T = np.asarray(text_len, dtype=np.int64)
     h = np.asarray(grid_h, dtype=np.int64)
     w = np.asarray(grid_w, dtype=np.int64)
-    L = T + h * w
+    edit = src_h is not None
+    sh = np.asarray(src_h if edit else np.zeros_like(h), dtype=np.int64)
+    sw = np.asarray(src_w if edit else np.zeros_like(h), dtype=np.int64)
+    L = T + h * w + sh * sw
     cu = np.zeros(len(L) + 1, dtype=np.int64)
     cu[1:] = np.cumsum(L)
     N = int(cu[-1])
@@ -105,41 +130,70 @@ def layout(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int]
     is_image = np.zeros(N, dtype=bool)
     row = np.zeros(N, dtype=np.int64)
     col = np.zeros(N, dtype=np.int64)
+    frame = np.zeros(N, dtype=np.int64)
     for i in range(len(L)):
         segment[cu[i]:cu[i + 1]] = i
-        n_img = int(h[i] * w[i])
-        if n_img:
-            idx = cu[i] + T[i] + np.arange(n_img)
-            is_image[idx] = True
-            row[idx] = np.arange(n_img) // w[i]
-            col[idx] = np.arange(n_img) % w[i]
-    return Layout(cu, segment, is_image, row, col)
+        start = cu[i] + T[i]
+        for f, (gh, gw) in enumerate(((h[i], w[i]), (sh[i], sw[i]))):
+            n_img = int(gh * gw)
+            if n_img:
+                idx = start + np.arange(n_img)
+                is_image[idx] = True
+                row[idx] = np.arange(n_img) // gw
+                col[idx] = np.arange(n_img) % gw
+                frame[idx] = f
+                start += n_img
+    return Layout(cu, segment, is_image, row, col, frame, edit)
 
 
 # --------------------------------------------------------------------------
 # 2D rotary embedding (image tokens only)
 # --------------------------------------------------------------------------
+def rope_section_frequencies(n: int, theta: float = 10000.0) -> np.ndarray:
+    """omega_j = theta^(-j/n) for the n pairs of one axis: a 1D rotary
+    embedding of 2n dimensions (frequencies theta^(-2j/(2n)))."""
+    return np.power(float(theta), -np.arange(n, dtype=np.float64) / n)
+
+
 def rope_frequencies(d: int, theta: float = 10000.0) -> np.ndarray:
-    """omega_j = theta^(-4j/d) for j < d/4: each half of the head dimension is a
-    1D rotary embedding of size d/2 (frequencies theta^(-2j/(d/2)))."""
+    """2D: omega_j = theta^(-4j/d) for j < d/4, each half of the head dimension
+    being a 1D rotary embedding of size d/2."""
     if d % 4:
         raise ValueError("head_dim must be a multiple of 4 for 2D RoPE")
-    j = np.arange(d // 4, dtype=np.float64)
-    return np.power(float(theta), -4.0 * j / d)
+    return rope_section_frequencies(d // 4, theta)
+
+
+def rope_sections(d: int, three_axes: bool = False):
+    """The axes of the d/2 dimension pairs, in pair order, as (axis, count):
+    2D: row on d/4 pairs, then column on d/4; 3D (editing): frame on d/8,
+    row on 3d/16, column on 3d/16."""
+    if not three_axes:
+        return [("row", d // 4), ("col", d // 4)]
+    if d % 16:
+        raise ValueError("head_dim must be a multiple of 16 for 3D RoPE")
+    return [("frame", d // 8), ("row", 3 * d // 16), ("col", 3 * d // 16)]
 
 
 def rope_angles(lay: Layout, d: int, theta: float = 10000.0) -> np.ndarray:
     """Rotation angle of each of the d/2 dimension pairs of each token, [N, d/2].
 
-    Pair p < d/4 (dimensions 2p, 2p+1) turns by row * omega_p; pair d/4 + j
-    (dimensions d/2 + 2j, d/2 + 2j + 1) turns by col * omega_j. Text tokens get
-    angle 0, i.e. no rotation. (Transcript [00:03:16]: per-sample 2D rotary
-    positional embeddings keeping each sample's own pixel layout.)
+    The pairs are split into consecutive sections, one per axis
+    (``rope_sections``); pair j of a section of n pairs turns by
+    pos * theta^(-j/n), pos the token's index on that axis. 2D: pair p < d/4
+    (dimensions 2p, 2p+1) turns by row * theta^(-4p/d) and pair d/4 + j by
+    col * theta^(-4j/d). Text tokens get angle 0, i.e. no rotation.
+    (Transcript [00:03:16]: per-sample 2D rotary positional embeddings keeping
+    each sample's own pixel layout; picx.dev, "Native-Resolution MMDiT
+    (NR-MMDiT)", conditioning bullet: a third, frame axis for editing.)
     """
-    om = rope_frequencies(d, theta)
-    r = np.where(lay.is_image, lay.row, 0).astype(np.float64)
-    c = np.where(lay.is_image, lay.col, 0).astype(np.float64)
-    return np.concatenate([r[:, None] * om[None, :], c[:, None] * om[None, :]], axis=1)
+    frame = lay.frame if lay.frame is not None else np.zeros_like(lay.row)
+    pos = {"frame": frame, "row": lay.row, "col": lay.col}
+    parts = []
+    for axis, n in rope_sections(d, lay.three_axes):
+        om = rope_section_frequencies(n, theta)
+        x = np.where(lay.is_image, pos[axis], 0).astype(np.float64)
+        parts.append(x[:, None] * om[None, :])
+    return np.concatenate(parts, axis=1)
 
 
 def rope_apply(x: np.ndarray, angles: np.ndarray) -> np.ndarray:

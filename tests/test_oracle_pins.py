@@ -36,6 +36,20 @@ def _enumerate_tokens(text, hs, ws):
     return toks
 
 
+def _enumerate_tokens_edit(text, hs, ws, sh, sw):
+    """Pure-Python token list of an editing pack: (segment, is_image, row,
+    col, frame); per sample its text, the target grid on frame 0, then the
+    source grid on frame 1."""
+    toks = []
+    for s in range(len(text)):
+        toks += [(s, False, 0, 0, 0)] * int(text[s])
+        for f, (h, w) in enumerate(((hs[s], ws[s]), (sh[s], sw[s]))):
+            for r in range(h):
+                for c in range(w):
+                    toks.append((s, True, r, c, f))
+    return toks
+
+
 def _brute_attention(qh, kh, v, seg):
     """Pure-Python loops: O[t] = sum_j softmax_j(q_t.k_j/sqrt d) v_j over the
     tokens j of t's own sample."""
@@ -146,6 +160,27 @@ def pin_layout_enumeration():
     assert list(lay.cu_seqlens) == [0, 288, 440]
 
 
+def pin_layout_edit_enumeration():
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        S = int(rng.integers(1, 6))
+        T = rng.integers(0, 9, S); hs = rng.integers(1, 5, S); ws = rng.integers(1, 5, S)
+        sh = rng.integers(0, 5, S); sw = rng.integers(1, 5, S)
+        sh = np.where(rng.random(S) < 0.3, 0, sh); sw = np.where(sh == 0, 0, sw)
+        lay = oracle.layout(T, hs, ws, sh, sw)
+        assert lay.three_axes
+        got = list(zip(lay.segment.tolist(), lay.is_image.tolist(), lay.row.tolist(),
+                       lay.col.tolist(), lay.frame.tolist()))
+        assert got == _enumerate_tokens_edit(T, hs, ws, sh, sw)
+    # one 1024^2 edit: 512 text tokens, 64x64 target and 64x64 source latents
+    lay = oracle.layout([512], [64], [64], [64], [64])
+    assert list(lay.cu_seqlens) == [0, 512 + 2 * 4096]
+    assert lay.frame[512:512 + 4096].max() == 0 and lay.frame[512 + 4096:].min() == 1
+    # a generation pack has no frame axis and frame 0 everywhere
+    g = oracle.layout([3], [2], [2])
+    assert not g.three_axes and not np.any(g.frame)
+
+
 def pin_rmsnorm_closed_forms():
     rng = np.random.default_rng(2)
     eps = 1e-6
@@ -244,6 +279,75 @@ def pin_rope_properties():
     # frequencies: omega_0 = 1, and the last one is theta^(-(d-4)/d)
     om_ = oracle.rope_frequencies(128)
     assert om_[0] == 1.0 and abs(om_[-1] / 10000.0 ** (-124.0 / 128.0) - 1) < 1e-14
+
+
+def _edit_token(d, f, r, c, image=True):
+    """Layout of an editing pack holding the given token, and its index."""
+    if not image:
+        return oracle.layout([1], [0], [0], [0], [0]), 0
+    if f == 0:
+        return oracle.layout([0], [r + 1], [c + 1], [0], [0]), r * (c + 1) + c
+    return oracle.layout([0], [1], [1], [r + 1], [c + 1]), 1 + r * (c + 1) + c
+
+
+def pin_rope3d_golden():
+    with open(os.path.join(GOLDEN, "rope3d_angles.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    assert len(rows) >= 6
+    for p in rows:
+        d, theta, mod = int(p[0]), float(p[1]), p[2]
+        f_, r, c = int(p[3]), int(p[4]), int(p[5])
+        want = np.array([float(x) for x in p[6:]])
+        assert len(want) == d // 2
+        lay, t = _edit_token(d, f_, r, c, mod == "i")
+        assert lay.frame[t] == f_ and lay.row[t] == (r if mod == "i" else 0)
+        got = oracle.rope_angles(lay, d, theta)[t]
+        assert np.max(np.abs(got - want)) <= 1e-14 * max(1.0, np.max(np.abs(want))), (p, got)
+
+
+def pin_rope3d_properties():
+    rng = np.random.default_rng(12)
+    for d in (64, 128):
+        fp = d // 8
+        lay = oracle.layout([4, 3], [5, 3], [6, 7], [4, 0], [3, 0])
+        ang = oracle.rope_angles(lay, d)
+        x = rng.standard_normal((lay.num_tokens, 2, d))
+        y = oracle.rope_apply(x, ang)
+        _close(y[..., 0::2] ** 2 + y[..., 1::2] ** 2, x[..., 0::2] ** 2 + x[..., 1::2] ** 2, 1e-13)
+        _close(y[~lay.is_image], x[~lay.is_image], 0.0)
+        # frame-0 (target) tokens leave the frame pairs unrotated; frame-1
+        # (source) tokens do not
+        tgt = lay.is_image & (lay.frame == 0)
+        src = lay.is_image & (lay.frame == 1)
+        _close(y[tgt][..., :2 * fp], x[tgt][..., :2 * fp], 0.0)
+        assert np.all(np.abs(y[src][..., 0:2] - x[src][..., 0:2]) > 0)
+        # the same (row, col) on both frames differs only in the frame pairs
+        i0 = np.flatnonzero(tgt & (lay.row == 2) & (lay.col == 1))[0]
+        i1 = np.flatnonzero(src & (lay.row == 2) & (lay.col == 1))[0]
+        _close(ang[i0, fp:], ang[i1, fp:], 0.0)
+        assert np.all(ang[i1, :fp] != ang[i0, :fp])
+        # q.k after rotation depends only on (dframe, drow, dcol)
+        q = rng.standard_normal(d); k = rng.standard_normal(d)
+
+        def score(p1, p2):
+            pts = np.array([p1, p2], np.int64)
+            L = oracle.Layout(np.array([0, 2]), np.zeros(2, np.int64), np.ones(2, bool),
+                              pts[:, 1], pts[:, 2], pts[:, 0], True)
+            a_ = oracle.rope_angles(L, d)
+            qq = oracle.rope_apply(q[None, None, :].copy(), a_[:1])[0, 0]
+            kk = oracle.rope_apply(k[None, None, :].copy(), a_[1:])[0, 0]
+            return float(qq @ kk)
+        base = score((1, 3, 5), (0, 10, 2))
+        for sh in [(1, 0, 0), (0, 1, 0), (0, 0, 7), (5, 20, 20), (-1, -3, 4)]:
+            s2 = score((1 + sh[0], 3 + sh[1], 5 + sh[2]), (sh[0], 10 + sh[1], 2 + sh[2]))
+            assert abs(s2 - base) < 1e-10 * max(1.0, abs(base))
+        # and each axis matters
+        for other in [(0, 3, 5), (1, 4, 5), (1, 3, 6)]:
+            assert abs(score(other, (0, 10, 2)) - base) > 1e-6
+        # section sizes: 1/8, 3/16, 3/16 of d in pairs, covering d/2
+        secs = oracle.rope_sections(d, True)
+        assert [n for _, n in secs] == [d // 8, 3 * d // 16, 3 * d // 16]
+        assert sum(n for _, n in secs) == d // 2
 
 
 def pin_attention_bruteforce():
@@ -386,8 +490,9 @@ def pin_backward_closed_forms():
         _close(b[key], -2.5 * a[key], 1e-13)
 
 
-PINS = [pin_layout_golden, pin_layout_enumeration, pin_rmsnorm_closed_forms,
-        pin_modality_separation, pin_rope_golden, pin_rope_properties,
+PINS = [pin_layout_golden, pin_layout_enumeration, pin_layout_edit_enumeration,
+        pin_rmsnorm_closed_forms, pin_modality_separation, pin_rope_golden,
+        pin_rope_properties, pin_rope3d_golden, pin_rope3d_properties,
         pin_attention_bruteforce, pin_attention_library, pin_attention_closed_forms,
         pin_packing_invariants, pin_backward_finite_differences,
         pin_backward_autograd, pin_backward_closed_forms]
@@ -430,6 +535,50 @@ def _mut_angles_swap(lay, d, theta=10000.0):
 
 def _mut_freq(d, theta=10000.0):
     return np.power(float(theta), -2.0 * np.arange(d // 4) / d)
+
+
+def _mut_section_freq(n, theta=10000.0):
+    return np.power(float(theta), -2.0 * np.arange(n) / n)
+
+
+def _mut_3d_frame_dropped(d, three_axes=False):
+    return [("row", d // 4), ("col", d // 4)]
+
+
+def _mut_3d_sections_reordered(d, three_axes=False):
+    if not three_axes:
+        return [("row", d // 4), ("col", d // 4)]
+    return [("row", 3 * d // 16), ("col", 3 * d // 16), ("frame", d // 8)]
+
+
+def _mut_3d_even_split(d, three_axes=False):
+    if not three_axes:
+        return [("row", d // 4), ("col", d // 4)]
+    n = d // 6
+    return [("frame", n), ("row", n), ("col", d // 2 - 2 * n)]
+
+
+def _mut_layout_frames_swapped(text_len, grid_h, grid_w, src_h=None, src_w=None):
+    lay = om.__dict__["_orig_layout"](text_len, grid_h, grid_w, src_h, src_w)
+    if lay.three_axes:
+        lay.frame = np.where(lay.is_image, 1 - lay.frame, 0)
+    return lay
+
+
+def _mut_layout_source_first(text_len, grid_h, grid_w, src_h=None, src_w=None):
+    orig = om.__dict__["_orig_layout"]
+    if src_h is None:
+        return orig(text_len, grid_h, grid_w)
+    hs, ws = np.asarray(grid_h), np.asarray(grid_w)
+    sh, sw = np.asarray(src_h), np.asarray(src_w)
+    has = sh * sw > 0
+    # a sample with a source grid lists it first (frame 1), then the target
+    lay = orig(text_len, np.where(has, sh, hs), np.where(has, sw, ws),
+               np.where(has, hs, 0), np.where(has, ws, 0))
+    for i in np.flatnonzero(has):
+        seg = (lay.segment == i) & lay.is_image
+        lay.frame[seg] = 1 - lay.frame[seg]
+    return lay
 
 
 def _mut_rms_eps_out(x, g_tok, eps):
@@ -497,6 +646,12 @@ MUTANTS = {
     "rope_rotate_half": ("rope_apply", _mut_rope_half),
     "rope_row_col_swapped": ("rope_angles", _mut_angles_swap),
     "rope_freq_schedule": ("rope_frequencies", _mut_freq),
+    "rope_section_freq_schedule": ("rope_section_frequencies", _mut_section_freq),
+    "rope3d_frame_axis_dropped": ("rope_sections", _mut_3d_frame_dropped),
+    "rope3d_sections_reordered": ("rope_sections", _mut_3d_sections_reordered),
+    "rope3d_even_split": ("rope_sections", _mut_3d_even_split),
+    "layout_edit_frames_swapped": ("layout", _mut_layout_frames_swapped),
+    "layout_edit_source_first": ("layout", _mut_layout_source_first),
     "rms_eps_outside_sqrt": ("rms_norm", _mut_rms_eps_out),
     "rms_sum_not_mean": ("rms_norm", _mut_rms_sum),
     "gains_modality_swapped": ("token_gains", _mut_gain_swap),
