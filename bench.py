@@ -92,11 +92,13 @@ def cpu_baseline(inp, heads):
                        f"of the same pack ({dt:.1f} s); throughput of that sample")
 
 
-def pass_runner(pam, torch, dev, text, hs, ws, H, d, backward, seed):
+def pass_runner(pam, torch, dev, text, hs, ws, H, d, backward, seed, src=None):
     """A callable that runs one whole pass (forward, and backward if asked)
-    of the library on a pack of the given geometry. Inputs are drawn on the
-    device: only the timing of such passes is used."""
-    pack = pam.Pack(text, hs, ws, H, d, "bf16", device=dev)
+    of the library on a pack of the given geometry (src = (src_h, src_w):
+    an editing pack). Inputs are drawn on the device: only the timing of such
+    passes is used."""
+    sh, sw = (None, None) if src is None else src
+    pack = pam.Pack(text, hs, ws, H, d, "bf16", device=dev, src_h=sh, src_w=sw)
     N = pack.N
     g = torch.Generator(device=dev).manual_seed(seed)
     rnd = lambda: torch.randn((N, H, d), generator=g, device=dev).to(torch.bfloat16)
@@ -157,6 +159,23 @@ def packed_cfg_1024(pam, torch, dev, H, d):
         out[f"null_text_{null}"] = {"packed_ms": round(t_packed, 4), "two_passes_ms": round(t_two, 4),
                                     "speedup": round(t_two / t_packed, 3)}
     return out
+
+
+def edit_1024(pam, torch, dev):
+    """One 1024^2 editing step's attention core: 512 text tokens, the 64x64
+    target latents and the 64x64 source latents on a second RoPE frame
+    (8,704 tokens, H=24, d=128): whole forward call, and forward + backward."""
+    w = workloads.get("edit1024")
+    t, hs, ws = list(w.text), [g[0] for g in w.grids], [g[1] for g in w.grids]
+    src = ([g[0] for g in w.src], [g[1] for g in w.src])
+    fwd = pass_runner(pam, torch, dev, t, hs, ws, w.heads, w.head_dim, False, 4, src)
+    both = pass_runner(pam, torch, dev, t, hs, ws, w.heads, w.head_dim, True, 5, src)
+    L = t[0] + hs[0] * ws[0] + src[0][0] * src[1][0]
+    flop1 = w.heads * w.head_dim * float(L) ** 2
+    t_f = time_passes(torch, [fwd], 50)
+    t_fb = time_passes(torch, [both], 20)
+    return {"tokens": L, "fwd_ms": round(t_f, 4), "fwd_tflops": round(4 * flop1 / t_f / 1e9, 1),
+            "fwd_bwd_ms": round(t_fb, 4), "fwd_bwd_tflops": round(14 * flop1 / t_fb / 1e9, 1)}
 
 
 def bucket_padding(pam, torch, dev, inp, H, d):
@@ -317,6 +336,7 @@ def main():
     gen_fwd_tflops = 4.0 * g.heads * g.head_dim * sum_l2(g) / (ms_layer_1024 * 1e-3) / 1e12
 
     cfg = packed_cfg_1024(pam, torch, dev, H, d)
+    edit = edit_1024(pam, torch, dev)
     bucket = bucket_padding(pam, torch, dev, inp, H, d)
 
     if args.copy_calibration:
@@ -353,6 +373,7 @@ def main():
         "gen1024_fwd_tflops": round(gen_fwd_tflops, 2),
         "roofline": roof,
         "packed_cfg_1024": cfg,
+        "edit_1024": edit,
         "bucket_padding": bucket,
     }
     if not args.no_cpu_baseline:

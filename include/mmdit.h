@@ -26,6 +26,11 @@
  *   - RoPE: dims [0, d/2) turn by the row index, dims [d/2, d) by the column
  *     index (0-based); inside each half, adjacent pairs (2j, 2j+1) turn by
  *     pos * theta^(-4j/d); text tokens are not rotated;
+ *   - editing packs (mmdit_pack_plan_edit) use a third, frame axis: the first
+ *     d/8 pairs turn by the frame index (0 for target tokens, 1 for source
+ *     tokens), the next 3d/16 pairs by the row and the last 3d/16 by the
+ *     column; pair j of a section of n pairs turns by pos * theta^(-j/n),
+ *     which for n = d/4 is the 2D rule above;
  *   - softmax scale 1/sqrt(d), no causal mask, natural-log lse.
  *
  * Tensor layout: Q, K, V, O and their gradients are [N][H][d] (token-major,
@@ -53,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MMDIT_ABI_VERSION 1
+#define MMDIT_ABI_VERSION 2
 
 /* Largest accepted token stride, in elements (2^24). */
 #define MMDIT_MAX_ROW_STRIDE (1ll << 24)
@@ -91,7 +96,8 @@ typedef struct {
  * copied by the caller to device memory (16-byte aligned) once, and that copy
  * passed as plan_blob_dev. Blob sections (offsets in bytes, 256-aligned):
  *   cu_seqlens  int32 [S+1]
- *   tok_meta    int32 [N]   bit 31 = image, bits 30..16 = row, bits 15..0 = col
+ *   tok_meta    int32 [N]   bit 31 = image, bits 30..16 = row, bit 15 = frame,
+ *                           bits 14..0 = col
  *   fwd_items   int32 [num_fwd_items][4] = {seg_start, seg_end, tile_start, sample}
  *               one per q_tile-row query tile, longest segment first
  *   bwd_items   int32 [num_bwd_items][4], same for kv_tile-row key tiles
@@ -101,11 +107,14 @@ typedef struct {
  *               the GPU's 8 XCDs in longest-first order so that each sample's
  *               K/V stay in one XCD's L2 (workgroup b runs on XCD b % 8).
  *   bwd_blocks  int32 [num_bwd_blocks][2], the same for the key-tile kernel
- *   rope        fp32  [rope_rows][d/4][2] = {cos, sin}(pos * theta^(-4j/d)),
- *               computed in double precision and rounded once. */
+ *   rope        fp32  [rope_rows][d/2][2] = {cos, sin}(pos * omega_p) for
+ *               each of the d/2 pairs p (the frequency of its section, see
+ *               the RoPE conventions above), computed in double precision and
+ *               rounded once. rope_frame_pairs = number of frame pairs (0 for
+ *               a generation pack, d/8 for an editing pack). */
 typedef struct {
   int32_t num_samples, total_tokens, max_seqlen, num_heads, head_dim, dtype;
-  int32_t q_tile, kv_tile, num_fwd_items, num_bwd_items, rope_rows, reserved;
+  int32_t q_tile, kv_tile, num_fwd_items, num_bwd_items, rope_rows, rope_frame_pairs;
   int32_t num_fwd_blocks, num_bwd_blocks;
   float rope_theta, rms_eps;
   uint64_t blob_bytes;
@@ -122,6 +131,22 @@ typedef struct {
  * BUDGET, BUFFER_TOO_SMALL (host_blob_bytes < plan->blob_bytes). */
 mmdit_status mmdit_pack_plan(const mmdit_pack_desc *desc, mmdit_plan *plan,
                              void *host_blob, uint64_t host_blob_bytes);
+
+/* Plan of an editing pack (picx.dev "Mage-Flow ...", section
+ * "Native-Resolution MMDiT (NR-MMDiT)", the conditioning bullet: source image
+ * latents join the target latents in the sequence, told apart by a frame
+ * dimension of a 3D RoPE; instruction-based editing timings on the video page
+ * at [00:07:49]). Sample i holds text_len[i] text tokens, its grid_h[i] x
+ * grid_w[i] target grid (frame 0) and then its src_h[i] x src_w[i] source
+ * grid (frame 1), both row-major; src 0 x 0 = a generation sample (frame 0
+ * only) in the same pack. Every image token of the pack is rotated with the
+ * frame/row/column split. src_h and src_w
+ * are [S] host arrays (>= 0, < 32768, both zero or both positive; a source
+ * grid needs a target grid). Otherwise as mmdit_pack_plan, whose errors it
+ * shares; the plan works with mmdit_attn_fwd / mmdit_attn_bwd unchanged. */
+mmdit_status mmdit_pack_plan_edit(const mmdit_pack_desc *desc, const int32_t *src_h,
+                                  const int32_t *src_w, mmdit_plan *plan,
+                                  void *host_blob, uint64_t host_blob_bytes);
 
 /* Packed classifier-free guidance (picx.dev "Mage-Flow ...", section
  * "Native-Resolution MMDiT (NR-MMDiT)", the packed CFG inference bullet, and

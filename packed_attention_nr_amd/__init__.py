@@ -18,11 +18,13 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "MmditError", "lib", "mmdit_pack_plan", "mmdit_attn_fwd", "mmdit_attn_bwd",
+    "MmditError", "lib", "mmdit_pack_plan", "mmdit_pack_plan_edit", "mmdit_attn_fwd",
+    "mmdit_attn_bwd", "mmdit_cfg_pack_desc",
     "mmdit_status_str", "mmdit_last_error", "mmdit_abi_version", "Pack",
     "forward", "backward", "FWD_STAGES", "BWD_STAGES", "LIB_PATH",
 ]
 
+ABI_VERSION = 2
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmmdit.so")
 
 MMDIT_F32, MMDIT_BF16 = 0, 1
@@ -42,7 +44,7 @@ class PackDesc(C.Structure):
 class Plan(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "num_samples", "total_tokens", "max_seqlen", "num_heads", "head_dim", "dtype",
-        "q_tile", "kv_tile", "num_fwd_items", "num_bwd_items", "rope_rows", "reserved",
+        "q_tile", "kv_tile", "num_fwd_items", "num_bwd_items", "rope_rows", "rope_frame_pairs",
         "num_fwd_blocks", "num_bwd_blocks")] + [
         ("rope_theta", C.c_float), ("rms_eps", C.c_float)] + [(n, C.c_uint64) for n in (
         "blob_bytes", "off_cu_seqlens", "off_tok_meta", "off_fwd_items", "off_bwd_items",
@@ -92,6 +94,10 @@ def lib():
         L = C.CDLL(LIB_PATH)
         L.mmdit_pack_plan.restype = C.c_int
         L.mmdit_pack_plan.argtypes = [C.POINTER(PackDesc), C.POINTER(Plan), C.c_void_p, C.c_uint64]
+        L.mmdit_pack_plan_edit.restype = C.c_int
+        L.mmdit_pack_plan_edit.argtypes = [C.POINTER(PackDesc), C.POINTER(C.c_int32),
+                                           C.POINTER(C.c_int32), C.POINTER(Plan), C.c_void_p,
+                                           C.c_uint64]
         L.mmdit_cfg_pack_desc.restype = C.c_int
         L.mmdit_cfg_pack_desc.argtypes = [C.POINTER(PackDesc), C.c_int32, C.POINTER(C.c_int32),
                                           C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.c_int32,
@@ -108,7 +114,7 @@ def lib():
         L.mmdit_last_error.argtypes = []
         L.mmdit_abi_version.restype = C.c_int32
         L.mmdit_abi_version.argtypes = []
-        if L.mmdit_abi_version() != 1:
+        if L.mmdit_abi_version() != ABI_VERSION:
             raise ImportError("libmmdit ABI version mismatch")
         _lib = L
     return _lib
@@ -131,11 +137,8 @@ def _check(status: int):
         raise MmditError(status, mmdit_last_error())
 
 
-def mmdit_pack_plan(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int],
-                    num_heads: int, head_dim: int, dtype: int, rope_theta: float = 10000.0,
-                    rms_eps: float = 1e-6, token_budget: int = 0):
-    """Run mmdit_pack_plan. Returns (plan, blob) with blob a uint8 numpy array
-    holding the host copy of the plan blob."""
+def _plan(text_len, grid_h, grid_w, num_heads, head_dim, dtype, rope_theta, rms_eps,
+          token_budget, src_h=None, src_w=None):
     t = np.ascontiguousarray(text_len, dtype=np.int32)
     h = np.ascontiguousarray(grid_h, dtype=np.int32)
     w = np.ascontiguousarray(grid_w, dtype=np.int32)
@@ -146,10 +149,40 @@ def mmdit_pack_plan(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequ
                     int(num_heads), int(head_dim), int(dtype), float(rope_theta), float(rms_eps),
                     int(token_budget))
     plan = Plan()
-    _check(lib().mmdit_pack_plan(C.byref(desc), C.byref(plan), None, 0))
+    if src_h is None:
+        call = lambda blob, n: lib().mmdit_pack_plan(C.byref(desc), C.byref(plan), blob, n)
+    else:
+        sh = np.ascontiguousarray(src_h, dtype=np.int32)
+        sw = np.ascontiguousarray(src_w, dtype=np.int32)
+        if not (len(sh) == len(sw) == len(t)):
+            raise ValueError("src_h and src_w must have one entry per sample")
+        call = lambda blob, n: lib().mmdit_pack_plan_edit(
+            C.byref(desc), sh.ctypes.data_as(P), sw.ctypes.data_as(P), C.byref(plan), blob, n)
+    _check(call(None, 0))
     blob = np.zeros(plan.blob_bytes, dtype=np.uint8)
-    _check(lib().mmdit_pack_plan(C.byref(desc), C.byref(plan), blob.ctypes.data, blob.nbytes))
+    _check(call(blob.ctypes.data, blob.nbytes))
     return plan, blob
+
+
+def mmdit_pack_plan(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int],
+                    num_heads: int, head_dim: int, dtype: int, rope_theta: float = 10000.0,
+                    rms_eps: float = 1e-6, token_budget: int = 0):
+    """Run mmdit_pack_plan. Returns (plan, blob) with blob a uint8 numpy array
+    holding the host copy of the plan blob."""
+    return _plan(text_len, grid_h, grid_w, num_heads, head_dim, dtype, rope_theta, rms_eps,
+                 token_budget)
+
+
+def mmdit_pack_plan_edit(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int],
+                         src_h: Sequence[int], src_w: Sequence[int], num_heads: int,
+                         head_dim: int, dtype: int, rope_theta: float = 10000.0,
+                         rms_eps: float = 1e-6, token_budget: int = 0):
+    """Run mmdit_pack_plan_edit (editing pack: each sample's source grid
+    follows its target grid, on frame 1 of a 3D RoPE). Returns (plan, blob)."""
+    if src_h is None or src_w is None:
+        raise ValueError("src_h and src_w are required")
+    return _plan(text_len, grid_h, grid_w, num_heads, head_dim, dtype, rope_theta, rms_eps,
+                 token_budget, src_h, src_w)
 
 
 def mmdit_cfg_pack_desc(text_len: Sequence[int], grid_h: Sequence[int], grid_w: Sequence[int],
@@ -231,11 +264,20 @@ class Pack:
     """Plan of one pack plus its device blob (copied once)."""
 
     def __init__(self, text_len, grid_h, grid_w, num_heads, head_dim, dtype="bf16",
-                 rope_theta=10000.0, rms_eps=1e-6, token_budget=0, device="cuda"):
+                 rope_theta=10000.0, rms_eps=1e-6, token_budget=0, device="cuda",
+                 src_h=None, src_w=None):
+        """src_h, src_w (per-sample source grids) make an editing pack
+        (mmdit_pack_plan_edit); None makes a generation pack."""
         import torch
         self.dtype_code = MMDIT_BF16 if dtype in ("bf16", MMDIT_BF16) else MMDIT_F32
-        self.plan, self.blob = mmdit_pack_plan(text_len, grid_h, grid_w, num_heads, head_dim,
-                                               self.dtype_code, rope_theta, rms_eps, token_budget)
+        if src_h is None and src_w is None:
+            self.plan, self.blob = mmdit_pack_plan(text_len, grid_h, grid_w, num_heads, head_dim,
+                                                   self.dtype_code, rope_theta, rms_eps,
+                                                   token_budget)
+        else:
+            self.plan, self.blob = mmdit_pack_plan_edit(text_len, grid_h, grid_w, src_h, src_w,
+                                                        num_heads, head_dim, self.dtype_code,
+                                                        rope_theta, rms_eps, token_budget)
         self.blob_dev = torch.from_numpy(self.blob).to(device)
         self.N = self.plan.total_tokens
         self.H = self.plan.num_heads

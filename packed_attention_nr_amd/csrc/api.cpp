@@ -97,6 +97,7 @@ static PlanDev plan_dev(const mmdit_plan &p, const void *blob) {
   d.num_fwd_blocks = p.num_fwd_blocks;
   d.num_bwd_blocks = p.num_bwd_blocks;
   d.rope_rows = p.rope_rows;
+  d.rope_frame_pairs = p.rope_frame_pairs;
   d.rms_eps = p.rms_eps;
   return d;
 }
@@ -284,7 +285,19 @@ mmdit_status mmdit_pack_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void
                              uint64_t host_blob_bytes) {
   mmdit::clear_error();
   try {
-    return mmdit::build_plan(desc, plan, host_blob, host_blob_bytes);
+    return mmdit::build_plan(desc, nullptr, nullptr, plan, host_blob, host_blob_bytes);
+  } catch (...) {
+    return mmdit::fail(MMDIT_ERR_INVALID_ARG, "pack plan failed (out of host memory?)");
+  }
+}
+
+mmdit_status mmdit_pack_plan_edit(const mmdit_pack_desc *desc, const int32_t *src_h,
+                                  const int32_t *src_w, mmdit_plan *plan, void *host_blob,
+                                  uint64_t host_blob_bytes) {
+  mmdit::clear_error();
+  if (!src_h || !src_w) return mmdit::fail(MMDIT_ERR_INVALID_ARG, "src_h and src_w must not be NULL");
+  try {
+    return mmdit::build_plan(desc, src_h, src_w, plan, host_blob, host_blob_bytes);
   } catch (...) {
     return mmdit::fail(MMDIT_ERR_INVALID_ARG, "pack plan failed (out of host memory?)");
   }

@@ -64,19 +64,20 @@ static_assert(bwd::QT == kFwdTileBf16 && bwd::KT == kBwdTile, "backward tiles mu
 // Inputs of one lane's row: meta = the token's tok_meta word, rho = its
 // rstd (negative: recompute from x), xa(d0) = its pre-norm elements d0..d0+3
 // (from LDS or global), g2 = the two gain rows of this input (text, image;
-// LDS), out = the row's element offset in the dense output. Writes dx (bf16) for a valid row and
+// LDS), fp = the plan's RoPE frame pairs, out = the row's element offset in
+// the dense output. Writes dx (bf16) for a valid row and
 // leaves in red[m * D + d] (m = 0 text, 1 image) this wave's sums of
 // rho*dy*x over its 32 tokens (invalid rows add nothing).
 template <int D, typename XA>
 __device__ __forceinline__ void prologue_bwd_rows(const f32x16 (&acc)[D / 32], float scale, int32_t meta,
                                                   float rho, bool valid, const XA &xa, const float *g2,
-                                                  const float2 *rope, float eps, bf16 *dx, int64_t out,
+                                                  const float2 *rope, int fp, float eps, bf16 *dx, int64_t out,
                                                   float *red, int lane) {
-  constexpr int DB = D / 32, Q4 = D / 4;
+  constexpr int DB = D / 32;
   const int lq = lane & 31, g = lane >> 5;
   bool img;
-  int row, col;
-  tok_pos(meta, img, row, col);
+  int row, col, frame;
+  tok_pos(meta, img, row, col, frame);
   const float *gm = g2 + (img ? D : 0);
   float dy[DB][16], xv[DB][16];
 #pragma unroll
@@ -85,13 +86,13 @@ __device__ __forceinline__ void prologue_bwd_rows(const f32x16 (&acc)[D / 32], f
     for (int i = 0; i < 16; ++i) dy[b][i] = acc[b][i] * scale;
   if (img) {  // inverse rotation of the pairs (d, d+1), d even
     float2 cs[DB][8];
+    const int re = fp + (D / 2 - fp) / 2;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int pair = 16 * b + 4 * (k >> 1) + 2 * g + (k & 1);
-        const int half = pair >= Q4;
-        cs[b][k] = rope[(half ? col : row) * Q4 + pair - half * Q4];
+        cs[b][k] = rope[rope_pos(pair, fp, re, row, col, frame) * (D / 2) + pair];
       }
 #pragma unroll
     for (int b = 0; b < DB; ++b)
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
   auto xa = [&](int d0) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x4 *>(xt + swz_off<D, SWZ_ROWS>(lq, d0));
   };
-  prologue_bwd_rows<D>(dq, a.scale, meta, rho0, qi < seg1, xa, g_s, p.rope, p.rms_eps,
+  prologue_bwd_rows<D>(dq, a.scale, meta, rho0, qi < seg1, xa, g_s, p.rope, p.rope_frame_pairs, p.rms_eps,
                        static_cast<bf16 *>(a.dq), ((int64_t)qc * H + h) * D, red + wave * 2 * D, lane);
   __syncthreads();
   sum_wave_partials<D>(red, NWQ, part, tid);
@@ -686,7 +687,7 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
     auto xa = [&](int d0) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x4 *>(xg + d0);
     };
-    prologue_bwd_rows<D>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope, p.rms_eps,
+    prologue_bwd_rows<D>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope, p.rope_frame_pairs, p.rms_eps,
                          static_cast<bf16 *>(a.dk), ((int64_t)kc * H + h) * D, red + sub * 2 * D, lane);
   }
   __syncthreads();

@@ -301,10 +301,18 @@ __device__ __forceinline__ bf16x8 acc_to_bf16(const f32x16 &c, int base) {
   return r;
 }
 
-__device__ __forceinline__ void tok_pos(int32_t meta, bool &img, int &row, int &col) {
+// Decode a tok_meta word: image flag, row, column and frame index.
+__device__ __forceinline__ void tok_pos(int32_t meta, bool &img, int &row, int &col, int &frame) {
   img = meta < 0;
   row = (meta >> 16) & 0x7FFF;
-  col = meta & 0xFFFF;
+  col = meta & 0x7FFF;
+  frame = (meta >> 15) & 1;
+}
+
+// Position along the RoPE axis of pair p: pairs [0, fp) follow the frame,
+// [fp, re) the row and [re, d/2) the column, re = fp + (d/2 - fp) / 2.
+__device__ __forceinline__ int rope_pos(int p, int fp, int re, int row, int col, int frame) {
+  return p < fp ? frame : (p < re ? row : col);
 }
 
 }  // namespace mmdit

@@ -46,8 +46,10 @@ mmdit_status fail(mmdit_status s, const char *fmt, ...);
 void clear_error();
 
 uint64_t plan_fingerprint(const mmdit_plan &p);
-mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *host_blob,
-                        uint64_t host_blob_bytes);
+// src_h == src_w == nullptr: a generation pack (2D RoPE); both given: an
+// editing pack (3D RoPE, source grids after the target grids on frame 1).
+mmdit_status build_plan(const mmdit_pack_desc *desc, const int32_t *src_h, const int32_t *src_w,
+                        mmdit_plan *plan, void *host_blob, uint64_t host_blob_bytes);
 mmdit_status cfg_pack_desc(const mmdit_pack_desc *cond, int32_t null_text_len, int32_t *text_len,
                            int32_t *grid_h, int32_t *grid_w, int32_t capacity, mmdit_pack_desc *out);
 uint64_t bwd_partial_blocks(int64_t n_tokens);
@@ -71,9 +73,10 @@ struct PlanDev {
   const int4 *bwd_items;       // [num_bwd_items]
   const int2 *fwd_blocks;      // [num_fwd_blocks] {item, head} or {-1, -1}
   const int2 *bwd_blocks;      // [num_bwd_blocks]
-  const float2 *rope;          // [rope_rows][d/4] (cos, sin)
+  const float2 *rope;          // [rope_rows][d/2] (cos, sin)
   int32_t num_samples, total_tokens, num_heads, head_dim;
   int32_t num_fwd_items, num_bwd_items, num_fwd_blocks, num_bwd_blocks, rope_rows;
+  int32_t rope_frame_pairs;    // pairs [0, fp) turn by frame, then row, then column
   float rms_eps;
 };
 

@@ -70,9 +70,29 @@ BwdLayout bwd_layout(const mmdit_plan &p) {
   return w;
 }
 
-mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *host_blob,
-                        uint64_t host_blob_bytes) {
+// Angles of the RoPE table: pair p of the d/2 pairs belongs to one section
+// (frame, row or column, in that order; frame_pairs = 0: row and column
+// only) and turns by pos * theta^(-j/n), j its index in the section and n the
+// section's size. With two sections of d/4 pairs this is pos * theta^(-4j/d).
+static double rope_omega(double theta, int d, int frame_pairs, int p) {
+  const int half = d / 2, re = frame_pairs + (half - frame_pairs) / 2;
+  int j, n;
+  if (p < frame_pairs) {
+    j = p, n = frame_pairs;
+  } else if (p < re) {
+    j = p - frame_pairs, n = re - frame_pairs;
+  } else {
+    j = p - re, n = half - re;
+  }
+  return std::pow(theta, -(double)j / (double)n);
+}
+
+mmdit_status build_plan(const mmdit_pack_desc *desc, const int32_t *src_h, const int32_t *src_w,
+                        mmdit_plan *plan, void *host_blob, uint64_t host_blob_bytes) {
   if (!desc || !plan) return fail(MMDIT_ERR_INVALID_ARG, "desc and plan must not be NULL");
+  const bool edit = src_h || src_w;
+  if (edit && !(src_h && src_w))
+    return fail(MMDIT_ERR_INVALID_ARG, "src_h and src_w must both be given");
   const int S = desc->num_samples;
   if (S < 1) return fail(MMDIT_ERR_INVALID_ARG, "num_samples must be >= 1");
   if (!desc->text_len || !desc->grid_h || !desc->grid_w)
@@ -101,6 +121,17 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
     if (h >= kMaxGridSide || w >= kMaxGridSide)
       return fail(MMDIT_ERR_INVALID_ARG, "sample %d: grid side must be < %d", i, kMaxGridSide);
     L[i] = (int64_t)t + (int64_t)h * (int64_t)w;
+    if (edit) {
+      const int32_t sh = src_h[i], sw = src_w[i];
+      if (sh < 0 || sw < 0 || (sh == 0) != (sw == 0))
+        return fail(MMDIT_ERR_INVALID_ARG, "sample %d: src_h and src_w must both be 0 or both > 0", i);
+      if (sh >= kMaxGridSide || sw >= kMaxGridSide)
+        return fail(MMDIT_ERR_INVALID_ARG, "sample %d: grid side must be < %d", i, kMaxGridSide);
+      if (sh > 0 && h == 0)
+        return fail(MMDIT_ERR_INVALID_ARG, "sample %d: a source grid needs a target grid", i);
+      L[i] += (int64_t)sh * (int64_t)sw;
+      max_side = std::max<int64_t>(max_side, std::max(sh, sw));
+    }
     if (L[i] < 1) return fail(MMDIT_ERR_INVALID_ARG, "sample %d has no tokens", i);
     N += L[i];
     if (N > kMaxTokens) return fail(MMDIT_ERR_INVALID_ARG, "total tokens exceed %lld", (long long)kMaxTokens);
@@ -130,7 +161,9 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
   const int64_t n_fwd = count_items(qt), n_bwd = count_items(kt);
   if ((n_fwd + kXcds) * H > INT32_MAX / 4 || (n_bwd + kXcds) * H > INT32_MAX / 4)
     return fail(MMDIT_ERR_INVALID_ARG, "too many work items");
-  const int rope_rows = (int)std::max<int64_t>(1, max_side);
+  // Frame positions are 0 (target) and 1 (source).
+  const int rope_rows = (int)std::max<int64_t>(edit ? 2 : 1, max_side);
+  const int frame_pairs = edit ? (int)(d / 8) : 0;
   // Workgroup -> (item, head) maps: chunks of all tiles of one (sample, head),
   // dealt round-robin over the XCDs in longest-first order.
   auto block_map = [&](int tile, std::vector<int32_t> &out) {
@@ -176,6 +209,7 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
   p.num_fwd_blocks = (int32_t)(fwd_blocks.size() / 2);
   p.num_bwd_blocks = (int32_t)(bwd_blocks.size() / 2);
   p.rope_rows = rope_rows;
+  p.rope_frame_pairs = frame_pairs;
   p.rope_theta = desc->rope_theta;
   p.rms_eps = desc->rms_eps;
   uint64_t off = align_up(kBlobHeaderBytes, 256);
@@ -192,7 +226,7 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
   p.off_bwd_blocks = off;
   off = align_up(off + 4ull * bwd_blocks.size(), 256);
   p.off_rope = off;
-  off = align_up(off + 8ull * rope_rows * (d / 4), 256);
+  off = align_up(off + 8ull * rope_rows * (d / 2), 256);
   p.blob_bytes = off;
 
   const uint64_t elt = desc->dtype == MMDIT_BF16 ? 2 : 4;
@@ -229,6 +263,14 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
     for (int32_t r = 0; r < h; ++r)
       for (int32_t c = 0; c < w; ++c)
         meta[base + (int64_t)r * w + c] = (int32_t)(0x80000000u | ((uint32_t)r << 16) | (uint32_t)c);
+    if (!edit) continue;
+    // The source grid follows the target grid, on frame 1.
+    const int64_t sbase = base + (int64_t)h * w;
+    const int32_t sh = src_h[i], sw = src_w[i];
+    for (int32_t r = 0; r < sh; ++r)
+      for (int32_t c = 0; c < sw; ++c)
+        meta[sbase + (int64_t)r * sw + c] =
+            (int32_t)(0x80000000u | ((uint32_t)r << 16) | 0x8000u | (uint32_t)c);
   }
 
   auto fill_items = [&](int32_t *it, int tile) {
@@ -248,16 +290,18 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, mmdit_plan *plan, void *hos
   std::memcpy(blob + p.off_fwd_blocks, fwd_blocks.data(), 4 * fwd_blocks.size());
   std::memcpy(blob + p.off_bwd_blocks, bwd_blocks.data(), 4 * bwd_blocks.size());
 
-  // RoPE table: angle pos * theta^(-4j/d), j < d/4, in double, rounded once.
+  // RoPE table [rope_rows][d/2] of {cos, sin}(pos * omega_p), in double,
+  // rounded once.
   float *rope = reinterpret_cast<float *>(blob + p.off_rope);
-  const int q4 = (int)(d / 4);
-  for (int pos = 0; pos < rope_rows; ++pos)
-    for (int j = 0; j < q4; ++j) {
-      const double om = std::pow((double)desc->rope_theta, -4.0 * j / (double)d);
+  const int half = (int)(d / 2);
+  for (int pr = 0; pr < half; ++pr) {
+    const double om = rope_omega((double)desc->rope_theta, (int)d, frame_pairs, pr);
+    for (int pos = 0; pos < rope_rows; ++pos) {
       const double a = (double)pos * om;
-      rope[2 * (pos * q4 + j) + 0] = (float)std::cos(a);
-      rope[2 * (pos * q4 + j) + 1] = (float)std::sin(a);
+      rope[2 * ((int64_t)pos * half + pr) + 0] = (float)std::cos(a);
+      rope[2 * ((int64_t)pos * half + pr) + 1] = (float)std::sin(a);
     }
+  }
   return MMDIT_OK;
 }
 

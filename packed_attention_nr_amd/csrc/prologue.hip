@@ -56,16 +56,14 @@ struct Vec<float> {
 // Rotate the VEC/2 pairs of this lane (elements e0 .. e0+VEC-1 of a row) by
 // the token's RoPE angles; sign = -1 applies the inverse rotation.
 template <int D, int VEC>
-__device__ __forceinline__ void rope_lane(float *x, const float2 *rope, int e0, int row, int col,
-                                          float sign) {
-  constexpr int Q4 = D / 4;
+__device__ __forceinline__ void rope_lane(float *x, const float2 *rope, int e0, int fp, int row,
+                                          int col, int frame, float sign) {
+  const int re = fp + (D / 2 - fp) / 2;
 #pragma unroll
   for (int j = 0; j < VEC / 2; ++j) {
     const int pair = e0 / 2 + j;                 // pair index in [0, d/2)
-    const int half = pair >= Q4;                 // 0: row axis, 1: column axis
-    const int f = pair - half * Q4;              // frequency index
-    const int pos = half ? col : row;
-    const float2 cs = rope[pos * Q4 + f];
+    const int pos = rope_pos(pair, fp, re, row, col, frame);
+    const float2 cs = rope[pos * (D / 2) + pair];
     const float c = cs.x, s = sign * cs.y;
     const float a = x[2 * j], b = x[2 * j + 1];
     x[2 * j] = a * c - b * s;
@@ -88,8 +86,8 @@ __global__ __launch_bounds__(256) void prologue_fwd_kernel(PlanDev p, PrologueFw
   const int e0 = (threadIdx.x % LPR) * VEC;
   const int t = (int)(r / H), h = (int)(r % H);
   bool img;
-  int row, col;
-  tok_pos(p.tok_meta[t], img, row, col);
+  int row, col, frame;
+  tok_pos(p.tok_meta[t], img, row, col, frame);
 
   float xq[VEC], xk[VEC];
   Vec<T>::load(static_cast<const T *>(a.q) + t * a.q_stride + h * D + e0, xq);
@@ -112,8 +110,8 @@ __global__ __launch_bounds__(256) void prologue_fwd_kernel(PlanDev p, PrologueFw
     xk[i] = xk[i] * rk * gk[i];
   }
   if (img) {
-    rope_lane<D, VEC>(xq, p.rope, e0, row, col, 1.f);
-    rope_lane<D, VEC>(xk, p.rope, e0, row, col, 1.f);
+    rope_lane<D, VEC>(xq, p.rope, e0, p.rope_frame_pairs, row, col, frame, 1.f);
+    rope_lane<D, VEC>(xk, p.rope, e0, p.rope_frame_pairs, row, col, frame, 1.f);
   }
   Vec<T>::store(static_cast<T *>(a.q_hat) + r * D + e0, xq);
   Vec<T>::store(static_cast<T *>(a.k_hat) + r * D + e0, xk);
@@ -180,8 +178,8 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(PlanDev p, PrologueBw
     for (int64_t r = c * TPB * H + grp; r < r_end; r += RPB) {
       const int t = (int)(r / H), h = (int)(r % H);
       bool img;
-      int row, col;
-      tok_pos(p.tok_meta[t], img, row, col);
+      int row, col, frame;
+      tok_pos(p.tok_meta[t], img, row, col, frame);
       const T *xp = static_cast<const T *>(a.x) + t * a.x_stride + h * D + e0;
       const float *dyp = a.dx_hat + r * D + e0;
       float x[VEC], dy[VEC];
@@ -191,7 +189,7 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(PlanDev p, PrologueBw
         float4 v = *reinterpret_cast<const float4 *>(dyp + i);
         dy[i] = v.x; dy[i + 1] = v.y; dy[i + 2] = v.z; dy[i + 3] = v.w;
       }
-      if (img) rope_lane<D, VEC>(dy, p.rope, e0, row, col, -1.f);
+      if (img) rope_lane<D, VEC>(dy, p.rope, e0, p.rope_frame_pairs, row, col, frame, -1.f);
       float rho;
       if (a.rstd) {
         rho = a.rstd[a.which * rows + r];

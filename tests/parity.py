@@ -64,7 +64,8 @@ def run_gpu(inp, backward=True, device="cuda"):
     import packed_attention_nr_amd as pam
     import torch
     pack = pam.Pack(inp.text_len, inp.grid_h, inp.grid_w, inp.heads, inp.head_dim,
-                    inp.dtype, inp.rope_theta, inp.rms_eps, device=device)
+                    inp.dtype, inp.rope_theta, inp.rms_eps, device=device,
+                    src_h=inp.src_h, src_w=inp.src_w)
     t = to_device(inp, device)
     saved = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"])
     out = {k: host(v) for k, v in saved.items()}
@@ -83,8 +84,9 @@ def run_oracle(inp, heads=None, backward=True):
     gradients, which are then summed over that subset only)."""
     hs = slice(None) if heads is None else list(heads)
     q, k, v = inp.q[:, hs], inp.k[:, hs], inp.v[:, hs]
+    lay = oracle.layout(inp.text_len, inp.grid_h, inp.grid_w, inp.src_h, inp.src_w)
     f = oracle.forward(inp.text_len, inp.grid_h, inp.grid_w, q, k, v, inp.gains,
-                       inp.rms_eps, inp.rope_theta)
+                       inp.rms_eps, inp.rope_theta, lay=lay)
     out = dict(q_hat=f["q_hat"], k_hat=f["k_hat"], o=f["o"], lse=f["lse"],
                rstd_q=f["rstd_q"], rstd_k=f["rstd_k"])
     if backward and inp.dout is not None:
@@ -115,8 +117,9 @@ def subset_samples(inp, order):
     off = sample_offsets(inp)
     rows = np.concatenate([np.arange(off[i], off[i + 1]) for i in order])
     pick = lambda a: None if a is None else np.ascontiguousarray(a[rows])
-    sel = lambda a: np.asarray(a)[list(order)]
+    sel = lambda a: None if a is None else np.asarray(a)[list(order)]
     return dataclasses.replace(inp, text_len=sel(inp.text_len), grid_h=sel(inp.grid_h),
-                               grid_w=sel(inp.grid_w), q=pick(inp.q), k=pick(inp.k), v=pick(inp.v),
+                               grid_w=sel(inp.grid_w), src_h=sel(inp.src_h), src_w=sel(inp.src_w),
+                               q=pick(inp.q), k=pick(inp.k), v=pick(inp.v),
                                dout=pick(inp.dout)), rows
 

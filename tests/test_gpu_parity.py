@@ -92,7 +92,8 @@ def test_tiny_fp32_workload():
 # gradients (sums over all heads) from a second GPU run on just those heads,
 # whose per-head outputs must equal the full run's bit for bit
 # ---------------------------------------------------------------------------
-FULL = [("gen1024", [0, 11, 23]), ("mixed6", [0, 13]), ("gen2048", [5]), ("small64", [0, 23])]
+FULL = [("gen1024", [0, 11, 23]), ("mixed6", [0, 13]), ("gen2048", [5]), ("small64", [0, 23]),
+        ("edit1024", [0, 17])]
 
 
 @pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])

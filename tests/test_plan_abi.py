@@ -29,7 +29,7 @@ def test_exports_every_header_symbol(L):
     assert {"mmdit_pack_plan", "mmdit_attn_fwd", "mmdit_attn_bwd"} <= names
     for n in sorted(names):
         assert hasattr(L, n), n
-    assert pam.mmdit_abi_version() == 1
+    assert pam.mmdit_abi_version() == pam.ABI_VERSION == 2
     assert pam.mmdit_status_str(0) == "ok"
 
 
@@ -39,8 +39,12 @@ def _blob_section(blob, off, n, dtype):
 
 def _check_plan(inp, dtype_code):
     H, d = inp.heads, inp.head_dim
-    plan, blob = pam.mmdit_pack_plan(inp.text_len, inp.grid_h, inp.grid_w, H, d, dtype_code)
-    lay = oracle.layout(inp.text_len, inp.grid_h, inp.grid_w)
+    if inp.edit:
+        plan, blob = pam.mmdit_pack_plan_edit(inp.text_len, inp.grid_h, inp.grid_w, inp.src_h,
+                                              inp.src_w, H, d, dtype_code)
+    else:
+        plan, blob = pam.mmdit_pack_plan(inp.text_len, inp.grid_h, inp.grid_w, H, d, dtype_code)
+    lay = oracle.layout(inp.text_len, inp.grid_h, inp.grid_w, inp.src_h, inp.src_w)
     N, S = lay.num_tokens, len(inp.text_len)
     assert plan.total_tokens == N and plan.num_samples == S and plan.num_heads == H
     assert plan.max_seqlen == int(np.diff(lay.cu_seqlens).max())
@@ -50,7 +54,8 @@ def _check_plan(inp, dtype_code):
     um = meta.view(np.uint32)
     assert np.array_equal((um >> 31).astype(bool), lay.is_image)
     assert np.array_equal(((um >> 16) & 0x7FFF).astype(np.int64), lay.row)
-    assert np.array_equal((um & 0xFFFF).astype(np.int64), lay.col)
+    assert np.array_equal((um & 0x7FFF).astype(np.int64), lay.col)
+    assert np.array_equal(((um >> 15) & 1).astype(np.int64), lay.frame)
     # work lists: every tile of every sample once, longest segment first
     for n_items, off, tile in ((plan.num_fwd_items, plan.off_fwd_items, plan.q_tile),
                                (plan.num_bwd_items, plan.off_bwd_items, plan.kv_tile)):
@@ -87,12 +92,22 @@ def _check_plan(inp, dtype_code):
             assert last_pos.get(key, (-1, -1))[0] < b   # tiles in order
             assert it[i, 2] > last_pos.get(key, (-1, -1))[1]
             last_pos[key] = (b, int(it[i, 2]))
-    # RoPE table: cos/sin of pos * theta^(-4j/d), rounded once to fp32
-    rope = _blob_section(blob, plan.off_rope, plan.rope_rows * (d // 4) * 2, np.float32)
-    rope = rope.reshape(plan.rope_rows, d // 4, 2)
-    assert plan.rope_rows == max(1, int(max(inp.grid_h.max(), inp.grid_w.max())))
+    # RoPE table [rope_rows][d/2]: cos/sin of pos * omega_p, rounded once to
+    # fp32, omega_p the frequency of pair p in the oracle's schedule (read off
+    # its angles for a token at position 1 on every axis)
+    rope = _blob_section(blob, plan.off_rope, plan.rope_rows * (d // 2) * 2, np.float32)
+    rope = rope.reshape(plan.rope_rows, d // 2, 2)
+    sides = [inp.grid_h.max(), inp.grid_w.max()]
+    if inp.edit:
+        sides += [inp.src_h.max(), inp.src_w.max(), 2]
+    assert plan.rope_rows == max(1, int(max(sides)))
+    assert plan.rope_frame_pairs == (d // 8 if inp.edit else 0)
+    unit = oracle.Layout(np.array([0, 1]), np.zeros(1, np.int64), np.ones(1, bool),
+                         np.ones(1, np.int64), np.ones(1, np.int64), np.ones(1, np.int64),
+                         inp.edit)
+    om = oracle.rope_angles(unit, d)[0]
     pos = np.arange(plan.rope_rows)[:, None].astype(np.float64)
-    ang = pos * oracle.rope_frequencies(d)[None, :]
+    ang = pos * om[None, :]
     assert np.array_equal(rope[..., 0], np.cos(ang).astype(np.float32))
     assert np.array_equal(rope[..., 1], np.sin(ang).astype(np.float32))
     return plan
@@ -106,11 +121,14 @@ def test_plan_matches_oracle_layout_on_workloads(L, name):
         text = rng.integers(w.text_range[0], w.text_range[1] + 1, len(w.grids))
     else:
         text = np.array(w.text)
+    src = (None, None) if w.src is None else tuple(np.array([g[i] for g in w.src], np.int32)
+                                                   for i in (0, 1))
     inp = workloads.Inputs(np.asarray(text, np.int32), np.array([g[0] for g in w.grids], np.int32),
                            np.array([g[1] for g in w.grids], np.int32), None, None, None, None,
-                           None, w.heads, w.head_dim, w.dtype)
+                           None, w.heads, w.head_dim, w.dtype, src_h=src[0], src_w=src[1])
     plan = _check_plan(inp, 1 if w.dtype == "bf16" else 0)
-    expect_n = {"tiny_fp32": 440, "gen1024": 4608, "mixed6": 20436, "gen2048": 16896, "small64": 74894}
+    expect_n = {"tiny_fp32": 440, "gen1024": 4608, "mixed6": 20436, "gen2048": 16896,
+                "small64": 74894, "edit1024": 8704}
     assert plan.total_tokens == expect_n[name]
 
 
@@ -119,6 +137,59 @@ def test_plan_matches_oracle_layout_random(L, seed):
     inp = workloads.random_pack(seed, max_samples=9, max_text=300, max_side=40,
                                 heads=3, head_dim=64, backward=False)
     _check_plan(inp, 0)
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("d", [64, 128])
+def test_edit_plan_matches_oracle_layout_random(L, seed, d):
+    inp = workloads.random_pack(100 + seed, max_samples=7, max_text=200, max_side=33,
+                                heads=2, head_dim=d, backward=False, edit=True)
+    _check_plan(inp, 1)
+
+
+def test_edit_plan_one_pixel_grids(L):
+    """1 x 1 target and source grids: rope_rows still covers frame 1."""
+    inp = workloads.random_pack(0, heads=1, head_dim=64, backward=False, text=[2, 0],
+                                grids=[(1, 1), (1, 1)], src=[(1, 1), (0, 0)])
+    plan = _check_plan(inp, 1)
+    assert plan.rope_rows == 2 and plan.total_tokens == 5
+
+
+def _edit_call(text, gh, gw, sh, sw, budget=0):
+    t, h, w, a, b = (np.ascontiguousarray(x, np.int32) for x in (text, gh, gw, sh, sw))
+    P = C.POINTER(C.c_int32)
+    desc = pam.PackDesc(len(t), t.ctypes.data_as(P), h.ctypes.data_as(P), w.ctypes.data_as(P),
+                        2, 64, 1, 1e4, 1e-6, budget)
+    plan = pam.Plan()
+    return pam.lib().mmdit_pack_plan_edit(C.byref(desc), a.ctypes.data_as(P), b.ctypes.data_as(P),
+                                          C.byref(plan), None, 0), plan
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(sh=[2], sw=[0]), 1),              # source h without w
+    (dict(sh=[-1], sw=[-1]), 1),            # negative source grid
+    (dict(sh=[40000], sw=[1]), 1),          # source side too large
+    (dict(gh=[0], gw=[0], sh=[2], sw=[2]), 1),   # source without a target
+    (dict(budget=15), 4),                   # 3 + 4 + 9 = 16 tokens
+])
+def test_edit_plan_rejects(L, case, code):
+    args = dict(text=[3], gh=[2], gw=[2], sh=[3], sw=[3])
+    args.update(case)
+    st, _ = _edit_call(**args)
+    assert st == code, pam.mmdit_last_error()
+    assert pam.mmdit_last_error()
+
+
+def test_edit_plan_null_arrays_and_budget(L):
+    t = np.array([3], np.int32)
+    P = C.POINTER(C.c_int32)
+    desc = pam.PackDesc(1, t.ctypes.data_as(P), t.ctypes.data_as(P), t.ctypes.data_as(P),
+                        2, 64, 1, 1e4, 1e-6, 0)
+    plan = pam.Plan()
+    assert pam.lib().mmdit_pack_plan_edit(C.byref(desc), None, t.ctypes.data_as(P),
+                                          C.byref(plan), None, 0) == 1
+    st, plan = _edit_call([3], [2], [2], [3], [3], budget=16)
+    assert st == 0 and plan.total_tokens == 16 and plan.rope_frame_pairs == 8
 
 
 def _desc_call(text, gh, gw, H=2, d=64, dtype=1, theta=1e4, eps=1e-6, budget=0, blob_bytes=None):

@@ -46,6 +46,7 @@ class Workload:
     backward: bool
     rope_theta: float = 10000.0
     rms_eps: float = 1e-6
+    src: Optional[Tuple[Tuple[int, int], ...]] = None   # editing: source grid per sample
 
 
 def _rep(x, n):
@@ -79,10 +80,17 @@ WORKLOADS = {
         "small64", "many-small-segments pack, bf16 (64 x (32x32 + text 32..256), 74,894 tokens, H=24, d=128)",
         grids=_rep((32, 32), 64), text=None, text_range=(32, 256),
         heads=24, head_dim=128, dtype="bf16", backward=True),
+    # One 1024x1024 editing step: 512 text + 64x64 target latents + 64x64
+    # source latents on a second RoPE frame.
+    "edit1024": Workload(
+        "edit1024", "1024^2 editing step, bf16 (512 text + 64x64 target + 64x64 source = 8,704 tokens, "
+        "H=24, d=128)",
+        grids=((64, 64),), text=(512,), text_range=None,
+        heads=24, head_dim=128, dtype="bf16", backward=True, src=((64, 64),)),
 }
 
-# The five workloads in their canonical order.
-ORDER = ["tiny_fp32", "gen1024", "mixed6", "gen2048", "small64"]
+# The workloads in their canonical order.
+ORDER = ["tiny_fp32", "gen1024", "mixed6", "gen2048", "small64", "edit1024"]
 
 
 def get(name: str) -> Workload:
@@ -120,21 +128,35 @@ class Inputs:
     dtype: str
     rope_theta: float = 10000.0
     rms_eps: float = 1e-6
+    src_h: Optional[np.ndarray] = None   # int32 [S]: source grids of an editing pack
+    src_w: Optional[np.ndarray] = None
 
     @property
     def num_tokens(self) -> int:
         return int(self.q.shape[0])
 
+    @property
+    def edit(self) -> bool:
+        return self.src_h is not None
+
     def seqlens(self) -> np.ndarray:
-        return (self.text_len.astype(np.int64)
-                + self.grid_h.astype(np.int64) * self.grid_w.astype(np.int64))
+        L = (self.text_len.astype(np.int64)
+             + self.grid_h.astype(np.int64) * self.grid_w.astype(np.int64))
+        if self.edit:
+            L = L + self.src_h.astype(np.int64) * self.src_w.astype(np.int64)
+        return L
 
 
-def _finish(rng, text, hs, ws, H, d, dtype, backward, theta, eps) -> Inputs:
+def _finish(rng, text, hs, ws, H, d, dtype, backward, theta, eps, src=None) -> Inputs:
     text = np.asarray(text, dtype=np.int32)
     hs = np.asarray(hs, dtype=np.int32)
     ws = np.asarray(ws, dtype=np.int32)
     N = int((text.astype(np.int64) + hs.astype(np.int64) * ws.astype(np.int64)).sum())
+    sh = sw = None
+    if src is not None:
+        sh = np.asarray([g[0] for g in src], dtype=np.int32)
+        sw = np.asarray([g[1] for g in src], dtype=np.int32)
+        N += int((sh.astype(np.int64) * sw.astype(np.int64)).sum())
     gains = (1.0 + 0.1 * rng.standard_normal((4, d))).astype(np.float32)
     tens = []
     for _ in range(4 if backward else 3):
@@ -143,7 +165,7 @@ def _finish(rng, text, hs, ws, H, d, dtype, backward, theta, eps) -> Inputs:
         tens = [bf16_round(t) for t in tens]
     q, k, v = tens[:3]
     dout = tens[3] if backward else None
-    return Inputs(text, hs, ws, gains, q, k, v, dout, H, d, dtype, theta, eps)
+    return Inputs(text, hs, ws, gains, q, k, v, dout, H, d, dtype, theta, eps, sh, sw)
 
 
 def draw(w: Workload | str, seed: int = 0, backward: Optional[bool] = None) -> Inputs:
@@ -161,7 +183,7 @@ def draw(w: Workload | str, seed: int = 0, backward: Optional[bool] = None) -> I
     ws = [g[1] for g in w.grids]
     bw = w.backward if backward is None else backward
     return _finish(rng, text, hs, ws, w.heads, w.head_dim, w.dtype, bw,
-                   w.rope_theta, w.rms_eps)
+                   w.rope_theta, w.rms_eps, w.src)
 
 
 def random_pack(seed: int, *, max_samples: int = 4, max_text: int = 40,
@@ -169,10 +191,15 @@ def random_pack(seed: int, *, max_samples: int = 4, max_text: int = 40,
                 dtype: str = "f32", backward: bool = True,
                 allow_empty_text: bool = True, allow_empty_image: bool = True,
                 text: Optional[Sequence[int]] = None,
-                grids: Optional[Sequence[Tuple[int, int]]] = None) -> Inputs:
+                grids: Optional[Sequence[Tuple[int, int]]] = None,
+                edit: bool = False,
+                src: Optional[Sequence[Tuple[int, int]]] = None) -> Inputs:
     """A small random pack for property tests: random sample count, text
     lengths and grids (each sample keeps at least one token). ``text`` and
-    ``grids`` override the random geometry."""
+    ``grids`` override the random geometry. ``edit`` makes an editing pack:
+    each sample with a target grid gets a source grid (a fifth of them none,
+    i.e. generation samples in the editing pack), drawn after everything
+    else; ``src`` gives the source grids instead."""
     rng = np.random.default_rng(seed)
     if text is None or grids is None:
         S = int(rng.integers(1, max_samples + 1))
@@ -192,4 +219,11 @@ def random_pack(seed: int, *, max_samples: int = 4, max_text: int = 40,
         tl = list(text)
         hs = [g[0] for g in grids]
         ws = [g[1] for g in grids]
-    return _finish(rng, tl, hs, ws, heads, head_dim, dtype, backward, 10000.0, 1e-6)
+    if edit and src is None:
+        src = []
+        for h in hs:
+            if h == 0 or rng.random() < 0.2:
+                src.append((0, 0))
+            else:
+                src.append((int(rng.integers(1, max_side + 1)), int(rng.integers(1, max_side + 1))))
+    return _finish(rng, tl, hs, ws, heads, head_dim, dtype, backward, 10000.0, 1e-6, src)
