@@ -5,7 +5,10 @@
 // flattened latent grid are concatenated into one contiguous batch with
 // per-sample cumulative offsets, under a fixed token budget (picx.dev summary,
 // section "Native-Resolution MMDiT (NR-MMDiT)", bullet "Native-resolution
-// packing"; findtube.ai transcript at [00:03:16] and [00:04:03]).
+// packing"; findtube.ai transcript at [00:03:16] and [00:04:03]). Editing
+// samples append the source image's latent grid after the target grid, told
+// apart by the frame axis of a 3D RoPE (picx.dev, same section, conditioning
+// bullet).
 // Work lists and their longest-first order are this library's own scheduling
 // choice (attention cost of a tile grows with its segment's length).
 #include <algorithm>
