@@ -213,8 +213,8 @@ def main():
                     help="also run one plain 256 MiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the work would shard).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(samples and heads are independent, so each GPU would run its own pack).", file=sys.stderr)
         sys.exit(2)
 
     import torch

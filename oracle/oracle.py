@@ -31,7 +31,7 @@ Mage-Flow pages describe it:
 The method (variable-length flash attention) reaches exactly this definition up
 to rounding, so the oracle is the definition written out in float64 with
 numpy; matrix products use numpy's BLAS matmul. Readings taken where the pages
-are silent (each also listed in the design doc):
+are silent:
 
 * token order inside a sample: text first, then the image grid row-major;
 * RMSNorm: over the d elements of one (token, head); eps inside the square
@@ -47,7 +47,9 @@ are silent (each also listed in the design doc):
   frame, the next 3d/16 by the row and the last 3d/16 by the column; pair j of
   a section of n pairs turns by pos * theta^(-j/n) (which for n = d/4 is the
   2D rule);
-* softmax scale 1/sqrt(d), no causal mask, no dropout, natural-log lse.
+* softmax scale 1/sqrt(d), no causal mask, no dropout, natural-log lse;
+* the adaptive-LayerNorm modulation and gated residual around the attention
+  (see ``adaln_forward``).
 
 Parity status of each function (how it is pinned by tests other than itself):
 ``layout`` (pure-Python enumeration, token counts, editing order),
@@ -57,7 +59,10 @@ values of the 2D and 3D schedules, 3D relative-position property, frame-0
 tokens unrotated on the frame pairs), ``attention_forward`` (pure-Python brute force,
 torch fp64 library attention, closed forms, packing invariants),
 ``attention_backward`` / ``rope_backward`` / ``rms_norm_backward``
-(central finite differences, torch fp64 autograd, closed forms).
+(central finite differences, torch fp64 autograd, closed forms),
+``adaln_forward`` (hand values, torch fp64 ``layer_norm``, per-sample and
+per-stream selection), ``adaln_backward`` (central finite differences, torch
+fp64 autograd, closed forms).
 The RoPE pair layout, frequency schedule, position origin and the 3D split
 themselves are readings, not statements of the pages: against the pages they are parity
 unpinned; the code is pinned only against that written reading.
@@ -74,7 +79,7 @@ __all__ = [
     "rope_angles", "rope_apply",
     "rope_backward", "rms_norm", "rms_norm_backward", "token_gains",
     "prologue", "attention_forward", "attention_backward", "forward",
-    "backward",
+    "backward", "modulation_index", "adaln_forward", "adaln_backward",
 ]
 
 QUERY_BLOCK = 2048  # rows of the score matrix formed at once (memory bound only)
@@ -360,3 +365,78 @@ def backward(text_len, grid_h, grid_w, q, k, v, gains, dout, eps=1e-6,
         dgk[~img].sum(axis=(0, 1)), dgk[img].sum(axis=(0, 1)),
     ])
     return dict(dq=dq, dk=dk, dv=dv, dgains=dgains, dq_hat=dqh, dk_hat=dkh)
+
+
+# --------------------------------------------------------------------------
+# Adaptive LayerNorm modulation and gated residual (the memory-bound chains
+# on either side of the attention core)
+# --------------------------------------------------------------------------
+# picx.dev, section "Training Infrastructure": adaptive normalisation and
+# gating of the NR-MMDiT are fused into custom kernels; transcript [00:04:20]:
+# normalisation and residual chains fused so that intermediates stay on chip.
+# The pages give no formula. Readings:
+# * the DiT/MMDiT adaLN: LayerNorm over the model width D without affine
+#   parameters, eps inside the root, then h = x_hat * (1 + scale) + shift;
+# * one (shift, scale, gate) per sample and per stream (text or image): the
+#   modulation comes from each sample's own conditioning, and MMDiT keeps
+#   separate parameters per modality; all image tokens of a sample (an editing
+#   sample's target and source alike) use the image stream's;
+# * gated residual: z = x + gate * y, y being the output projection of the
+#   attention; the LayerNorm that follows is fused, so the op's outputs are
+#   z and h = adaLN(z). Without y the op is the plain adaLN of x (z = x).
+def modulation_index(lay: Layout) -> np.ndarray:
+    """Row of the [S, 2] modulation table of each token: (sample, stream),
+    stream 0 text and 1 image, flattened to 2 * sample + stream."""
+    return 2 * lay.segment + lay.is_image.astype(np.int64)
+
+
+def _per_token(table: np.ndarray, lay: Layout) -> np.ndarray:
+    t = np.asarray(table, dtype=np.float64)
+    return t.reshape(-1, t.shape[-1])[modulation_index(lay)]
+
+
+def _segment_sum(vals: np.ndarray, lay: Layout, S: int) -> np.ndarray:
+    """Sum of the rows of vals [N, D] over each (sample, stream): [S, 2, D]."""
+    out = np.zeros((2 * S, vals.shape[-1]))
+    np.add.at(out, modulation_index(lay), vals)
+    return out.reshape(S, 2, -1)
+
+
+def adaln_forward(lay: Layout, x, shift, scale, eps: float = 1e-6, y=None, gate=None):
+    """z = x (+ gate * y); mu, var = mean and biased variance of z over its D
+    elements; rstd = (var + eps)^(-1/2); h = (z - mu) * rstd * (1 + scale) +
+    shift. x, y: [N, D]; shift, scale, gate: [S, 2, D]. Returns dict with z,
+    h, mean and rstd (float64)."""
+    z = np.asarray(x, dtype=np.float64)
+    if y is not None:
+        z = z + _per_token(gate, lay) * np.asarray(y, dtype=np.float64)
+    mu = np.mean(z, axis=-1)
+    var = np.mean((z - mu[:, None]) ** 2, axis=-1)
+    rstd = 1.0 / np.sqrt(var + eps)
+    zh = (z - mu[:, None]) * rstd[:, None]
+    h = zh * (1.0 + _per_token(scale, lay)) + _per_token(shift, lay)
+    return dict(z=z, h=h, mean=mu, rstd=rstd)
+
+
+def adaln_backward(lay: Layout, x, shift, scale, dh, eps: float = 1e-6, y=None, gate=None,
+                   dz=None):
+    """Gradients of sum(dh * h) + sum(dz * z) for ``adaln_forward``.
+
+    g = dh * (1 + scale); dz_total = dz + rstd * (g - mean(g) - z_hat * mean(g * z_hat)),
+    the means over the D elements of a row; dx = dz_total; dy = gate * dz_total;
+    dshift, dscale, dgate [S, 2, D] = sums over each (sample, stream) of dh,
+    dh * z_hat and dz_total * y."""
+    S = len(lay.cu_seqlens) - 1
+    f = adaln_forward(lay, x, shift, scale, eps, y, gate)
+    dh = np.asarray(dh, dtype=np.float64)
+    zh = (f["z"] - f["mean"][:, None]) * f["rstd"][:, None]
+    g = dh * (1.0 + _per_token(scale, lay))
+    dzt = f["rstd"][:, None] * (g - np.mean(g, -1, keepdims=True)
+                                - zh * np.mean(g * zh, -1, keepdims=True))
+    if dz is not None:
+        dzt = dzt + np.asarray(dz, dtype=np.float64)
+    out = dict(dx=dzt, dshift=_segment_sum(dh, lay, S), dscale=_segment_sum(dh * zh, lay, S))
+    if y is not None:
+        out["dy"] = _per_token(gate, lay) * dzt
+        out["dgate"] = _segment_sum(dzt * np.asarray(y, dtype=np.float64), lay, S)
+    return out

@@ -490,12 +490,159 @@ def pin_backward_closed_forms():
         _close(b[key], -2.5 * a[key], 1e-13)
 
 
+# --------------------------------------------------------------------------
+# adaLN modulation and gated residual
+# --------------------------------------------------------------------------
+def _adaln_pack(seed, D, edit=False):
+    rng = np.random.default_rng(seed)
+    if edit:
+        lay = oracle.layout([3, 0, 2], [2, 1, 0], [2, 3, 0], [1, 2, 0], [3, 2, 0])
+    else:
+        lay = oracle.layout([3, 0, 2], [2, 1, 0], [2, 3, 0])
+    S, N = 3, lay.num_tokens
+    t = lambda *sh: rng.standard_normal(sh)
+    return lay, dict(x=t(N, D) * 2 + 0.5, y=t(N, D), shift=0.3 * t(S, 2, D), scale=0.3 * t(S, 2, D),
+                     gate=t(S, 2, D), dh=t(N, D), dz=t(N, D))
+
+
+def pin_adaln_closed_forms():
+    lay = oracle.layout([1], [0], [0])
+    z0 = np.zeros((1, 2, 4))
+    # (1, 2, 3, 4): mean 2.5, biased variance 1.25, eps = 0
+    f = oracle.adaln_forward(lay, np.array([[1.0, 2.0, 3.0, 4.0]]), z0, z0, eps=0.0)
+    _close(f["h"][0], [-1.3416407864998738, -0.4472135954999579, 0.4472135954999579,
+                       1.3416407864998738], 1e-15)
+    _close(f["mean"], [2.5], 0.0)
+    _close(f["rstd"], [1 / math.sqrt(1.25)], 1e-15)
+    # (1 + scale) = 2, shift = 0.5; text stream of sample 0
+    sc = np.zeros((1, 2, 4)); sc[0, 0] = 1.0
+    sh = np.zeros((1, 2, 4)); sh[0, 0] = 0.5
+    f2 = oracle.adaln_forward(lay, np.array([[1.0, 2.0, 3.0, 4.0]]), sh, sc, eps=0.0)
+    _close(f2["h"], 2 * f["h"] + 0.5, 1e-15)
+    # a constant row normalises to zero: h = shift
+    f3 = oracle.adaln_forward(lay, np.full((1, 4), 7.0), sh, sc, eps=1e-6)
+    _close(f3["h"][0], [0.5] * 4, 0.0)
+    # residual: gate 0 gives z = x, gate 1 gives z = x + y
+    rng = np.random.default_rng(30)
+    x, y = rng.standard_normal((1, 4)), rng.standard_normal((1, 4))
+    _close(oracle.adaln_forward(lay, x, z0, z0, 1e-6, y, np.zeros((1, 2, 4)))["z"], x, 0.0)
+    _close(oracle.adaln_forward(lay, x, z0, z0, 1e-6, y, np.ones((1, 2, 4)))["z"], x + y, 0.0)
+    # unit modulation: mean 0 and mean square var / (var + eps) per row
+    x = rng.standard_normal((1, 64)) * 3 + 1
+    f4 = oracle.adaln_forward(lay, x, np.zeros((1, 2, 64)), np.zeros((1, 2, 64)), 1e-3)
+    var = np.var(x)
+    assert abs(np.mean(f4["h"])) < 1e-14
+    assert abs(np.mean(f4["h"] ** 2) - var / (var + 1e-3)) < 1e-13
+
+
+def pin_adaln_library():
+    """Per (sample, stream), the op is torch's layer_norm with weight 1 + scale
+    and bias shift, applied to x + gate * y."""
+    for edit in (False, True):
+        lay, a = _adaln_pack(31, 16, edit)
+        f = oracle.adaln_forward(lay, a["x"], a["shift"], a["scale"], 1e-5, a["y"], a["gate"])
+        for i in range(len(lay.cu_seqlens) - 1):
+            for m in (0, 1):
+                rows = (lay.segment == i) & (lay.is_image == bool(m))
+                if not rows.any():
+                    continue
+                z = torch.as_tensor(a["x"][rows] + a["gate"][i, m] * a["y"][rows])
+                ref = torch.nn.functional.layer_norm(
+                    z, (16,), torch.as_tensor(1 + a["scale"][i, m]), torch.as_tensor(a["shift"][i, m]),
+                    eps=1e-5)
+                _close(f["h"][rows], ref.numpy(), 1e-13)
+                _close(f["z"][rows], z.numpy(), 0.0)
+
+
+def pin_adaln_selection():
+    """Changing one (sample, stream) modulation row changes exactly that
+    sample's tokens of that stream; an editing sample's target and source
+    share the image stream's row."""
+    for edit in (False, True):
+        lay, a = _adaln_pack(32, 8, edit)
+        base = oracle.adaln_forward(lay, a["x"], a["shift"], a["scale"], 1e-6, a["y"], a["gate"])
+        for key in ("shift", "scale", "gate"):
+            for i in range(3):
+                for m in (0, 1):
+                    b = {k: v.copy() for k, v in a.items()}
+                    b[key][i, m] += 0.7
+                    f = oracle.adaln_forward(lay, b["x"], b["shift"], b["scale"], 1e-6, b["y"], b["gate"])
+                    changed = np.any(f["h"] != base["h"], axis=1)
+                    rows = (lay.segment == i) & (lay.is_image == bool(m))
+                    assert np.array_equal(changed, rows), (edit, key, i, m)
+        if edit:
+            img1 = (lay.segment == 1) & lay.is_image
+            assert set(lay.frame[img1].tolist()) == {0, 1}
+
+
+def _adaln_loss(lay, a, eps=1e-6):
+    f = oracle.adaln_forward(lay, a["x"], a["shift"], a["scale"], eps, a["y"], a["gate"])
+    return float(np.sum(a["dh"] * f["h"]) + np.sum(a["dz"] * f["z"]))
+
+
+def pin_adaln_backward_finite_differences():
+    lay, a = _adaln_pack(33, 6, edit=True)
+    g = oracle.adaln_backward(lay, a["x"], a["shift"], a["scale"], a["dh"], 1e-6, a["y"], a["gate"],
+                              a["dz"])
+    names = {"x": "dx", "y": "dy", "shift": "dshift", "scale": "dscale", "gate": "dgate"}
+    rng = np.random.default_rng(34)
+    for key, gk in names.items():
+        flat = a[key].reshape(-1)
+        for idx in rng.choice(flat.size, size=min(flat.size, 12), replace=False):
+            h = 1e-6
+            old = flat[idx]
+            flat[idx] = old + h; lp = _adaln_loss(lay, a)
+            flat[idx] = old - h; lm = _adaln_loss(lay, a)
+            flat[idx] = old
+            num = (lp - lm) / (2 * h)
+            got = g[gk].reshape(-1)[idx]
+            assert abs(num - got) < 1e-6 * max(1.0, abs(num)), (key, idx, num, got)
+
+
+def pin_adaln_backward_autograd():
+    lay, a = _adaln_pack(35, 12, edit=False)
+    g = oracle.adaln_backward(lay, a["x"], a["shift"], a["scale"], a["dh"], 1e-6, a["y"], a["gate"],
+                              a["dz"])
+    T = {k: torch.tensor(v, requires_grad=k in ("x", "y", "shift", "scale", "gate"))
+         for k, v in a.items()}
+    seg = torch.as_tensor(lay.segment)
+    st = torch.as_tensor(lay.is_image.astype(np.int64))
+    z = T["x"] + T["gate"][seg, st] * T["y"]
+    h = torch.nn.functional.layer_norm(z, (12,), eps=1e-6) * (1 + T["scale"][seg, st]) + T["shift"][seg, st]
+    (torch.sum(T["dh"] * h) + torch.sum(T["dz"] * z)).backward()
+    for key, gk in (("x", "dx"), ("y", "dy"), ("shift", "dshift"), ("scale", "dscale"), ("gate", "dgate")):
+        _close(g[gk], T[key].grad.numpy(), 1e-12)
+
+
+def pin_adaln_backward_closed_forms():
+    lay, a = _adaln_pack(36, 8)
+    zero = np.zeros_like(a["dh"])
+    g = oracle.adaln_backward(lay, a["x"], a["shift"], a["scale"], zero, 1e-6, a["y"], a["gate"])
+    for k in ("dx", "dy", "dshift", "dscale", "dgate"):
+        _close(g[k], np.zeros_like(g[k]), 0.0)
+    # dh = c on every row and scale = 0: sum(h) does not depend on z (the
+    # normalised row sums to zero), so dx = 0; dshift = c * (tokens per stream)
+    sc0 = np.zeros_like(a["scale"])
+    g = oracle.adaln_backward(lay, a["x"], a["shift"], sc0, np.full_like(a["dh"], 0.25), 1e-6)
+    assert np.max(np.abs(g["dx"])) < 1e-14
+    counts = np.zeros((3, 2))
+    for i, m in zip(lay.segment, lay.is_image):
+        counts[i, int(m)] += 1
+    _close(g["dshift"], 0.25 * counts[:, :, None] * np.ones((1, 1, 8)), 1e-15)
+    # without y the op has no dy / dgate, and dz passes straight through
+    g1 = oracle.adaln_backward(lay, a["x"], a["shift"], a["scale"], zero, 1e-6, dz=a["dz"])
+    assert "dy" not in g1
+    _close(g1["dx"], a["dz"], 0.0)
+
+
 PINS = [pin_layout_golden, pin_layout_enumeration, pin_layout_edit_enumeration,
         pin_rmsnorm_closed_forms, pin_modality_separation, pin_rope_golden,
         pin_rope_properties, pin_rope3d_golden, pin_rope3d_properties,
         pin_attention_bruteforce, pin_attention_library, pin_attention_closed_forms,
         pin_packing_invariants, pin_backward_finite_differences,
-        pin_backward_autograd, pin_backward_closed_forms]
+        pin_backward_autograd, pin_backward_closed_forms, pin_adaln_closed_forms,
+        pin_adaln_library, pin_adaln_selection, pin_adaln_backward_finite_differences,
+        pin_adaln_backward_autograd, pin_adaln_backward_closed_forms]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -581,6 +728,48 @@ def _mut_layout_source_first(text_len, grid_h, grid_w, src_h=None, src_w=None):
     return lay
 
 
+def _mut_adaln_variant(kind):
+    def fwd(lay, x, shift, scale, eps=1e-6, y=None, gate=None):
+        z = np.asarray(x, dtype=np.float64)
+        if y is not None:
+            gt = om._per_token(gate, lay)
+            z = gt * z + y if kind == "gate_on_x" else z + gt * y
+        mu = z.mean(-1)
+        var = z.var(-1, ddof=1 if kind == "unbiased" else 0)
+        rstd = 1 / (np.sqrt(var) + eps) if kind == "eps_out" else 1 / np.sqrt(var + eps)
+        zh = (z - mu[:, None]) * rstd[:, None]
+        mult = om._per_token(scale, lay) + (0.0 if kind == "no_one" else 1.0)
+        return dict(z=z, h=zh * mult + om._per_token(shift, lay), mean=mu, rstd=rstd)
+    return fwd
+
+
+def _mut_modulation_stream_swap(lay):
+    return 2 * lay.segment + 1 - lay.is_image.astype(np.int64)
+
+
+def _mut_modulation_sample_shift(lay):
+    S = len(lay.cu_seqlens) - 1
+    return 2 * ((lay.segment + 1) % S) + lay.is_image.astype(np.int64)
+
+
+def _mut_adaln_bwd(kind):
+    def bwd(lay, x, shift, scale, dh, eps=1e-6, y=None, gate=None, dz=None):
+        out = om.__dict__["_orig_adaln_backward"](lay, x, shift, scale, dh, eps, y, gate, dz)
+        f = om.adaln_forward(lay, x, shift, scale, eps, y, gate)
+        zh = (f["z"] - f["mean"][:, None]) * f["rstd"][:, None]
+        g = np.asarray(dh) * (1 + om._per_token(scale, lay))
+        S = len(lay.cu_seqlens) - 1
+        if kind == "no_proj_term":
+            dzt = f["rstd"][:, None] * (g - g.mean(-1, keepdims=True))
+            out["dx"] = dzt + (0 if dz is None else dz)
+        elif kind == "dscale_no_zhat":
+            out["dscale"] = om._segment_sum(np.asarray(dh, np.float64), lay, S)
+        elif kind == "dy_no_gate" and y is not None:
+            out["dy"] = out["dx"].copy()
+        return out
+    return bwd
+
+
 def _mut_rms_eps_out(x, g_tok, eps):
     rho = 1.0 / (np.sqrt(np.mean(x * x, -1)) + eps)
     return x * rho[..., None] * g_tok[:, None, :], rho
@@ -652,6 +841,15 @@ MUTANTS = {
     "rope3d_even_split": ("rope_sections", _mut_3d_even_split),
     "layout_edit_frames_swapped": ("layout", _mut_layout_frames_swapped),
     "layout_edit_source_first": ("layout", _mut_layout_source_first),
+    "adaln_eps_outside_sqrt": ("adaln_forward", _mut_adaln_variant("eps_out")),
+    "adaln_unbiased_variance": ("adaln_forward", _mut_adaln_variant("unbiased")),
+    "adaln_scale_without_one": ("adaln_forward", _mut_adaln_variant("no_one")),
+    "adaln_gate_on_residual_input": ("adaln_forward", _mut_adaln_variant("gate_on_x")),
+    "adaln_streams_swapped": ("modulation_index", _mut_modulation_stream_swap),
+    "adaln_wrong_sample": ("modulation_index", _mut_modulation_sample_shift),
+    "adaln_bwd_projection_term_dropped": ("adaln_backward", _mut_adaln_bwd("no_proj_term")),
+    "adaln_bwd_dscale_without_zhat": ("adaln_backward", _mut_adaln_bwd("dscale_no_zhat")),
+    "adaln_bwd_dy_without_gate": ("adaln_backward", _mut_adaln_bwd("dy_no_gate")),
     "rms_eps_outside_sqrt": ("rms_norm", _mut_rms_eps_out),
     "rms_sum_not_mean": ("rms_norm", _mut_rms_sum),
     "gains_modality_swapped": ("token_gains", _mut_gain_swap),
