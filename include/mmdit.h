@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MMDIT_ABI_VERSION 2
+#define MMDIT_ABI_VERSION 3
 
 /* Largest accepted token stride, in elements (2^24). */
 #define MMDIT_MAX_ROW_STRIDE (1ll << 24)
@@ -107,6 +107,10 @@ typedef struct {
  *               the GPU's 8 XCDs in longest-first order so that each sample's
  *               K/V stay in one XCD's L2 (workgroup b runs on XCD b % 8).
  *   bwd_blocks  int32 [num_bwd_blocks][2], the same for the key-tile kernel
+ *   mod_chunks  int32 [num_mod_chunks][4] = {row_start, row_end, 2*sample + stream, 0}:
+ *               each (sample, stream) token range (stream 0 = text, 1 = image)
+ *               cut into pieces of at most mod_chunk_rows rows, ranges in order
+ *   mod_ranges  int32 [2S+1]: chunks of range r are [mod_ranges[r], mod_ranges[r+1])
  *   rope        fp32  [rope_rows][d/2][2] = {cos, sin}(pos * omega_p) for
  *               each of the d/2 pairs p (the frequency of its section, see
  *               the RoPE conventions above), computed in double precision and
@@ -122,6 +126,10 @@ typedef struct {
   uint64_t off_fwd_blocks, off_bwd_blocks;
   uint64_t fwd_workspace_bytes;  /* needed by mmdit_attn_fwd when q_hat/k_hat are NULL */
   uint64_t bwd_workspace_bytes;  /* needed by mmdit_attn_bwd */
+  uint64_t off_mod_chunks, off_mod_ranges;
+  int32_t num_mod_chunks;        /* adaLN workgroups; mmdit_adaln_bwd needs a workspace of
+                                    num_mod_chunks * 3 * model_dim * 4 bytes */
+  int32_t mod_chunk_rows;        /* rows per adaLN chunk (32) */
   uint64_t fingerprint;          /* hash of every field above; checked on each call */
 } mmdit_plan;
 
@@ -224,6 +232,65 @@ typedef struct {
 mmdit_status mmdit_attn_bwd(const mmdit_plan *plan, const void *plan_blob_dev,
                             const mmdit_bwd_args *args, void *workspace,
                             uint64_t workspace_bytes, void *hip_stream);
+
+/* Adaptive LayerNorm modulation with the fused gated residual, the memory-
+ * bound chains on either side of the attention core of an NR-MMDiT block
+ * (picx.dev "Mage-Flow ...", section "Training Infrastructure": adaptive
+ * normalisation and gating fused into kernels; video page at [00:04:20]:
+ * normalisation and residual chains fused so that intermediates stay on
+ * chip). The pages give no formula; this library computes the DiT-style adaLN
+ *   z = x + gate * y                 (only when y is given: the gated residual
+ *                                     of the attention's output projection y)
+ *   h = (z - mean(z)) * (var(z) + eps)^(-1/2) * (1 + scale) + shift
+ * over the model width D of each token (biased variance, eps inside the
+ * root), where shift, scale and gate are fp32 tables [S][2][D] holding one row
+ * per sample and stream (row 2*sample + stream; stream 0 = text tokens,
+ * 1 = image tokens, an editing sample's target and source alike). Token
+ * rows x, y, dh, dz: [N][D] of the plan's dtype with a token stride (>= D, a
+ * multiple of 4, 16-byte aligned base); z, h, dx, dy: dense [N][D]. The plan
+ * is any plan of the pack (its heads, head_dim and RoPE are not used). D is a
+ * multiple of 4 in [4, 8192] (else UNSUPPORTED). Same ownership, validation,
+ * aliasing and error rules as the attention calls; deterministic. */
+typedef struct {
+  const void *x;                      /* [N][D] */
+  const void *y;                      /* [N][D] or NULL (no residual: z = x, not written) */
+  int64_t x_stride, y_stride;
+  const float *shift, *scale;         /* [S][2][D] fp32 */
+  const float *gate;                  /* [S][2][D] fp32; with y only, else NULL */
+  int32_t model_dim;                  /* D */
+  float eps;                          /* >= 0, e.g. 1e-6 */
+  void *z;                            /* [N][D] out: x + gate * y; with y only, else NULL */
+  void *h;                            /* [N][D] out */
+  float *stats;                       /* [N][2] out: {mean, rstd} of z per token, or NULL */
+} mmdit_adaln_fwd_args;
+
+mmdit_status mmdit_adaln_fwd(const mmdit_plan *plan, const void *plan_blob_dev,
+                             const mmdit_adaln_fwd_args *args, void *hip_stream);
+
+/* Backward of mmdit_adaln_fwd for the loss sum(dh * h) + sum(dz * z):
+ *   g = dh * (1 + scale), z_hat = (z - mean) * rstd,
+ *   dz_total = dz + rstd * (g - mean(g) - z_hat * mean(g * z_hat)),
+ *   dx = dz_total, dy = gate * dz_total,
+ *   dshift / dscale / dgate = sums over each (sample, stream) of dh,
+ *   dh * z_hat and dz_total * y (fixed-order sums; rows with no tokens get 0).
+ * workspace_bytes >= plan->num_mod_chunks * 3 * D * 4. */
+typedef struct {
+  const void *x, *y;                  /* the forward's inputs (y NULL: no residual) */
+  int64_t x_stride, y_stride;
+  const float *scale, *gate;          /* [S][2][D]; gate with y only */
+  int32_t model_dim;
+  float eps;
+  const float *stats;                 /* [N][2] from the forward, or NULL = recompute */
+  const void *dh;                     /* [N][D] gradient of h */
+  const void *dz;                     /* [N][D] gradient arriving at z directly, or NULL */
+  int64_t dh_stride, dz_stride;
+  void *dx, *dy;                      /* [N][D] out; dy with y only */
+  float *dshift, *dscale, *dgate;     /* [S][2][D] fp32 out (overwritten); dgate with y only */
+} mmdit_adaln_bwd_args;
+
+mmdit_status mmdit_adaln_bwd(const mmdit_plan *plan, const void *plan_blob_dev,
+                             const mmdit_adaln_bwd_args *args, void *workspace,
+                             uint64_t workspace_bytes, void *hip_stream);
 
 const char *mmdit_status_str(mmdit_status s);
 const char *mmdit_last_error(void);   /* detail of this thread's last non-OK return */

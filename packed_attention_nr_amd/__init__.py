@@ -19,12 +19,13 @@ import numpy as np
 
 __all__ = [
     "MmditError", "lib", "mmdit_pack_plan", "mmdit_pack_plan_edit", "mmdit_attn_fwd",
-    "mmdit_attn_bwd", "mmdit_cfg_pack_desc",
+    "mmdit_attn_bwd", "mmdit_cfg_pack_desc", "mmdit_adaln_fwd", "mmdit_adaln_bwd",
+    "adaln_forward", "adaln_backward",
     "mmdit_status_str", "mmdit_last_error", "mmdit_abi_version", "Pack",
     "forward", "backward", "FWD_STAGES", "BWD_STAGES", "LIB_PATH",
 ]
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmmdit.so")
 
 MMDIT_F32, MMDIT_BF16 = 0, 1
@@ -49,7 +50,8 @@ class Plan(C.Structure):
         ("rope_theta", C.c_float), ("rms_eps", C.c_float)] + [(n, C.c_uint64) for n in (
         "blob_bytes", "off_cu_seqlens", "off_tok_meta", "off_fwd_items", "off_bwd_items",
         "off_rope", "off_fwd_blocks", "off_bwd_blocks", "fwd_workspace_bytes",
-        "bwd_workspace_bytes", "fingerprint")]
+        "bwd_workspace_bytes", "off_mod_chunks", "off_mod_ranges")] + [
+        ("num_mod_chunks", C.c_int32), ("mod_chunk_rows", C.c_int32), ("fingerprint", C.c_uint64)]
 
 
 class FwdArgs(C.Structure):
@@ -69,6 +71,22 @@ class BwdArgs(C.Structure):
                 ("gains", C.c_void_p), ("lse", C.c_void_p), ("rstd", C.c_void_p),
                 ("dq", C.c_void_p), ("dk", C.c_void_p), ("dv", C.c_void_p),
                 ("dgains", C.c_void_p), ("stages", C.c_uint32)]
+
+
+class AdalnFwdArgs(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("y", C.c_void_p), ("x_stride", C.c_int64),
+                ("y_stride", C.c_int64), ("shift", C.c_void_p), ("scale", C.c_void_p),
+                ("gate", C.c_void_p), ("model_dim", C.c_int32), ("eps", C.c_float),
+                ("z", C.c_void_p), ("h", C.c_void_p), ("stats", C.c_void_p)]
+
+
+class AdalnBwdArgs(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("y", C.c_void_p), ("x_stride", C.c_int64),
+                ("y_stride", C.c_int64), ("scale", C.c_void_p), ("gate", C.c_void_p),
+                ("model_dim", C.c_int32), ("eps", C.c_float), ("stats", C.c_void_p),
+                ("dh", C.c_void_p), ("dz", C.c_void_p), ("dh_stride", C.c_int64),
+                ("dz_stride", C.c_int64), ("dx", C.c_void_p), ("dy", C.c_void_p),
+                ("dshift", C.c_void_p), ("dscale", C.c_void_p), ("dgate", C.c_void_p)]
 
 
 class MmditError(RuntimeError):
@@ -108,6 +126,12 @@ def lib():
         L.mmdit_attn_bwd.restype = C.c_int
         L.mmdit_attn_bwd.argtypes = [C.POINTER(Plan), C.c_void_p, C.POINTER(BwdArgs), C.c_void_p,
                                      C.c_uint64, C.c_void_p]
+        L.mmdit_adaln_fwd.restype = C.c_int
+        L.mmdit_adaln_fwd.argtypes = [C.POINTER(Plan), C.c_void_p, C.POINTER(AdalnFwdArgs),
+                                      C.c_void_p]
+        L.mmdit_adaln_bwd.restype = C.c_int
+        L.mmdit_adaln_bwd.argtypes = [C.POINTER(Plan), C.c_void_p, C.POINTER(AdalnBwdArgs),
+                                      C.c_void_p, C.c_uint64, C.c_void_p]
         L.mmdit_status_str.restype = C.c_char_p
         L.mmdit_status_str.argtypes = [C.c_int]
         L.mmdit_last_error.restype = C.c_char_p
@@ -243,6 +267,28 @@ def mmdit_attn_bwd(plan: Plan, blob_dev, *, q=None, k=None, v=None, q_hat=None, 
                                 ws_bytes, _stream(stream)))
 
 
+def mmdit_adaln_fwd(plan: Plan, blob_dev, *, x=None, y=None, x_stride=0, y_stride=0, shift=None,
+                    scale=None, gate=None, model_dim=0, eps=1e-6, z=None, h=None, stats=None,
+                    stream=None):
+    """Run mmdit_adaln_fwd with torch tensors (device pointers taken from them)."""
+    a = AdalnFwdArgs(_ptr(x), _ptr(y), int(x_stride), int(y_stride), _ptr(shift), _ptr(scale),
+                     _ptr(gate), int(model_dim), float(eps), _ptr(z), _ptr(h), _ptr(stats))
+    _check(lib().mmdit_adaln_fwd(C.byref(plan), _ptr(blob_dev), C.byref(a), _stream(stream)))
+
+
+def mmdit_adaln_bwd(plan: Plan, blob_dev, *, x=None, y=None, x_stride=0, y_stride=0, scale=None,
+                    gate=None, model_dim=0, eps=1e-6, stats=None, dh=None, dz=None, dh_stride=0,
+                    dz_stride=0, dx=None, dy=None, dshift=None, dscale=None, dgate=None,
+                    workspace=None, stream=None):
+    """Run mmdit_adaln_bwd with torch tensors (device pointers taken from them)."""
+    a = AdalnBwdArgs(_ptr(x), _ptr(y), int(x_stride), int(y_stride), _ptr(scale), _ptr(gate),
+                     int(model_dim), float(eps), _ptr(stats), _ptr(dh), _ptr(dz), int(dh_stride),
+                     int(dz_stride), _ptr(dx), _ptr(dy), _ptr(dshift), _ptr(dscale), _ptr(dgate))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mmdit_adaln_bwd(C.byref(plan), _ptr(blob_dev), C.byref(a), _ptr(workspace),
+                                 ws_bytes, _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # Conveniences: a pack with its device blob; forward / backward with torch-
 # allocated outputs.
@@ -285,9 +331,14 @@ class Pack:
         self.device = device
         self.torch_dtype = _torch_dtype(self.dtype_code)
 
-    def workspace(self, kind: str):
+    def workspace(self, kind: str, model_dim: int = 0):
+        """Workspace of the attention forward ("fwd"), backward ("bwd") or
+        the adaLN backward ("adaln", for model width model_dim)."""
         import torch
-        n = self.plan.fwd_workspace_bytes if kind == "fwd" else self.plan.bwd_workspace_bytes
+        if kind == "adaln":
+            n = self.plan.num_mod_chunks * 3 * int(model_dim) * 4
+        else:
+            n = self.plan.fwd_workspace_bytes if kind == "fwd" else self.plan.bwd_workspace_bytes
         return torch.empty(max(int(n), 16), dtype=torch.uint8, device=self.device)
 
 
@@ -344,3 +395,55 @@ def backward(pack: Pack, q, k, v, gains, saved: dict, dout, *, workspace=None, s
                    rstd=saved.get("rstd"), dq=dq, dk=dk, dv=dv, dgains=dgains, workspace=ws,
                    stream=stream)
     return dict(dq=dq, dk=dk, dv=dv, dgains=dgains, workspace=ws)
+
+
+def _rows_stride(t, N, name):
+    if t.dim() != 2 or t.shape[0] != N or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a [N={N}, D] tensor with unit column stride")
+    return t.stride(0)
+
+
+def adaln_forward(pack: Pack, x, shift, scale, *, y=None, gate=None, eps: float = 1e-6,
+                  save_stats: bool = True, stream=None):
+    """h = adaLN(z) with z = x (+ gate * y); returns dict with h, z (with y)
+    and stats ([N, 2] mean and rstd, when saved)."""
+    import torch
+    N, D = pack.N, int(x.shape[-1])
+    xs = _rows_stride(x, N, "x")
+    ys = 0 if y is None else _rows_stride(y, N, "y")
+    h = torch.empty((N, D), dtype=pack.torch_dtype, device=x.device)
+    z = None if y is None else torch.empty_like(h)
+    stats = torch.empty((N, 2), dtype=torch.float32, device=x.device) if save_stats else None
+    mmdit_adaln_fwd(pack.plan, pack.blob_dev, x=x, y=y, x_stride=xs, y_stride=ys, shift=shift,
+                    scale=scale, gate=gate, model_dim=D, eps=eps, z=z, h=h, stats=stats,
+                    stream=stream)
+    out = dict(h=h)
+    if z is not None:
+        out["z"] = z
+    if stats is not None:
+        out["stats"] = stats
+    return out
+
+
+def adaln_backward(pack: Pack, x, scale, dh, *, y=None, gate=None, dz=None, stats=None,
+                   eps: float = 1e-6, workspace=None, stream=None):
+    """dx (= dz_total), dy, dshift, dscale, dgate of ``adaln_forward``."""
+    import torch
+    N, D = pack.N, int(x.shape[-1])
+    S = pack.plan.num_samples
+    dx = torch.empty((N, D), dtype=pack.torch_dtype, device=x.device)
+    dy = None if y is None else torch.empty_like(dx)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dshift, dscale = torch.empty((S, 2, D), **f32), torch.empty((S, 2, D), **f32)
+    dgate = None if y is None else torch.empty((S, 2, D), **f32)
+    ws = pack.workspace("adaln", D) if workspace is None else workspace
+    mmdit_adaln_bwd(pack.plan, pack.blob_dev, x=x, y=y, x_stride=_rows_stride(x, N, "x"),
+                    y_stride=0 if y is None else _rows_stride(y, N, "y"), scale=scale, gate=gate,
+                    model_dim=D, eps=eps, stats=stats, dh=dh, dz=dz,
+                    dh_stride=_rows_stride(dh, N, "dh"),
+                    dz_stride=0 if dz is None else _rows_stride(dz, N, "dz"), dx=dx, dy=dy,
+                    dshift=dshift, dscale=dscale, dgate=dgate, workspace=ws, stream=stream)
+    out = dict(dx=dx, dshift=dshift, dscale=dscale)
+    if y is not None:
+        out.update(dy=dy, dgate=dgate)
+    return out

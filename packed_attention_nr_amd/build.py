@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmmdit.so")
 
-SOURCES = ["plan.cpp", "api.cpp", "prologue.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_f32.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "prologue.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_f32.hip",
+           "adaln.hip"]
 ARCH = "gfx950"
 
 

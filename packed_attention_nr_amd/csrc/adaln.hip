@@ -1,0 +1,407 @@
+// Adaptive LayerNorm modulation of the NR-MMDiT block, with the gated
+// residual of the attention output fused in front of it:
+//   z = x + gate * y        (y: the attention's output projection; optional)
+//   h = (z - mean(z)) * rstd(z) * (1 + scale) + shift,  rstd = (var + eps)^(-1/2)
+// with (shift, scale, gate) one fp32 row of the model width D per sample and
+// per stream (text or image). The pages credit fused adaptive-normalisation
+// and gating kernels in the NR-MMDiT (picx.dev summary "Mage-Flow: An
+// Efficient Native-Resolution Foundation Model ...", section "Training
+// Infrastructure"; findtube.ai transcript at [00:04:20]: normalisation and
+// residual chains fused so that intermediates stay on chip); the formula is
+// the DiT-style adaLN, which the pages do not print.
+//
+// Work split: one workgroup (4 waves) per plan chunk of <= 32 rows of one
+// (sample, stream) range, so the whole workgroup uses one modulation row.
+// Thread t owns the column groups {4g .. 4g+3 : g = t + 256 j}: each load
+// instruction of the workgroup covers one contiguous 2 KB (bf16) or 4 KB
+// (fp32) stretch of a row. Rows are processed RB at a time; the row sums
+// (mean, then the squared deviations, from registers) are reduced with DPP
+// inside a wave and over the 4 waves through LDS in a fixed order, so every
+// thread holds the same bits. The backward keeps per-thread column sums of
+// dshift, dscale and dgate over its chunk and writes one partial row each; a
+// second kernel adds each range's partials in chunk order (no atomics: the
+// results are deterministic).
+#include "device.h"
+#include "internal.h"
+
+namespace mmdit {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+struct Quad;
+template <>
+struct Quad<bf16> {
+  __device__ static void load(const bf16 *p, float (&x)[4]) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (float)v[i];
+  }
+  __device__ static void store(bf16 *p, const float (&x)[4]) {
+    const bf16x2 a = pack2(x[0], x[1]), b = pack2(x[2], x[3]);
+    const bf16x4 v = {a[0], a[1], b[0], b[1]};
+    *reinterpret_cast<bf16x4 *>(p) = v;
+  }
+};
+template <>
+struct Quad<float> {
+  __device__ static void load(const float *p, float (&x)[4]) {
+    const float4 v = *reinterpret_cast<const float4 *>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+  __device__ static void store(float *p, const float (&x)[4]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+};
+
+__device__ __forceinline__ void zero4(float (&x)[4]) { x[0] = x[1] = x[2] = x[3] = 0.f; }
+
+// Sums of v[0 .. NV) over the workgroup; every thread gets the same bits.
+// buf: LDS [NV][4]. Consecutive calls must alternate between two buffers.
+template <int NV>
+__device__ __forceinline__ void block_sums(float (&v)[NV], float *buf, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = group_sum<64>(v[i]);
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) buf[4 * i + wave] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = (buf[4 * i] + buf[4 * i + 1]) + (buf[4 * i + 2] + buf[4 * i + 3]);
+}
+
+// z of RB rows (rows past the chunk and columns past D read as 0).
+template <typename T, int G, int RB, bool RES>
+__device__ __forceinline__ void load_z(float (&z)[RB][G][4], const T *x, int64_t xs,
+                                       const T *y, int64_t ys, const float (&gt)[G][4], int r0, int r1,
+                                       const int (&col)[G], const bool (&ok)[G]) {
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) {
+    const int row = r0 + rr;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (row < r1 && ok[j]) {
+        Quad<T>::load(x + (int64_t)row * xs + col[j], z[rr][j]);
+        if constexpr (RES) {
+          float yv[4];
+          Quad<T>::load(y + (int64_t)row * ys + col[j], yv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[rr][j][i] = fmaf(gt[j][i], yv[i], z[rr][j][i]);
+        }
+      } else {
+        zero4(z[rr][j]);
+      }
+    }
+  }
+}
+
+// Mean and rstd of RB rows held in registers (two fixed-order passes).
+template <int G, int RB>
+__device__ __forceinline__ void row_stats(const float (&z)[RB][G][4], const bool (&ok)[G], float inv_d,
+                                          float eps, float (&mean)[RB], float (&rstd)[RB], float (*red)[64],
+                                          int &nb, int wave, int lane) {
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s += z[rr][j][i];
+    mean[rr] = s;
+  }
+  block_sums<RB>(mean, red[nb++ & 1], wave, lane);
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) {
+    mean[rr] *= inv_d;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (ok[j])
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float c = z[rr][j][i] - mean[rr];
+          s = fmaf(c, c, s);
+        }
+    rstd[rr] = s;
+  }
+  block_sums<RB>(rstd, red[nb++ & 1], wave, lane);
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) rstd[rr] = rsqrtf(rstd[rr] * inv_d + eps);
+}
+
+template <typename T, int G, bool RES>
+__global__ __launch_bounds__(kThreads) void adaln_fwd_kernel(PlanDev p, AdalnFwdArgs a) {
+  constexpr int RB = 4;
+  __shared__ float red[2][64];
+  const int4 ch = p.mod_chunks[blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int D = a.dim;
+  const int64_t mrow = (int64_t)ch.z * D;
+  float sh[G][4], sc[G][4], gt[G][4];
+  int col[G];
+  bool ok[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    col[j] = 4 * (tid + kThreads * j);
+    ok[j] = col[j] < D;
+    zero4(sh[j]);
+    zero4(sc[j]);
+    zero4(gt[j]);
+    if (ok[j]) {
+      Quad<float>::load(a.shift + mrow + col[j], sh[j]);
+      Quad<float>::load(a.scale + mrow + col[j], sc[j]);
+      if constexpr (RES) Quad<float>::load(a.gate + mrow + col[j], gt[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[j][i] += 1.f;
+  }
+  const T *x = static_cast<const T *>(a.x);
+  const T *y = static_cast<const T *>(a.y);
+  T *zo = static_cast<T *>(a.z);
+  T *ho = static_cast<T *>(a.h);
+  const float inv_d = 1.f / (float)D;
+  int nb = 0;
+  for (int r0 = ch.x; r0 < ch.y; r0 += RB) {
+    float z[RB][G][4], mean[RB], rstd[RB];
+    load_z<T, G, RB, RES>(z, x, a.x_stride, y, a.y_stride, gt, r0, ch.y, col, ok);
+    row_stats<G, RB>(z, ok, inv_d, a.eps, mean, rstd, red, nb, wave, lane);
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int row = r0 + rr;
+      if (row >= ch.y) break;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (!ok[j]) continue;
+        const int64_t o = (int64_t)row * D + col[j];
+        if constexpr (RES) Quad<T>::store(zo + o, z[rr][j]);
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = fmaf((z[rr][j][i] - mean[rr]) * rstd[rr], sc[j][i], sh[j][i]);
+        Quad<T>::store(ho + o, hv);
+      }
+      if (a.stats && tid == 0) a.stats[row] = make_float2(mean[rr], rstd[rr]);
+    }
+  }
+}
+
+template <typename T, int G, bool RES>
+__global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwdArgs a) {
+  constexpr int RB = G <= 4 ? 4 : 2;
+  __shared__ float red[2][64];
+  const int4 ch = p.mod_chunks[blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int D = a.dim;
+  const int64_t mrow = (int64_t)ch.z * D;
+  float sc[G][4], gt[G][4], ash[G][4], asc[G][4], agt[G][4];
+  int col[G];
+  bool ok[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    col[j] = 4 * (tid + kThreads * j);
+    ok[j] = col[j] < D;
+    zero4(sc[j]);
+    zero4(gt[j]);
+    zero4(ash[j]);
+    zero4(asc[j]);
+    zero4(agt[j]);
+    if (ok[j]) {
+      Quad<float>::load(a.scale + mrow + col[j], sc[j]);
+      if constexpr (RES) Quad<float>::load(a.gate + mrow + col[j], gt[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[j][i] += 1.f;
+  }
+  const T *x = static_cast<const T *>(a.x);
+  const T *y = static_cast<const T *>(a.y);
+  const T *dh = static_cast<const T *>(a.dh);
+  const T *dz = static_cast<const T *>(a.dz);
+  T *dxo = static_cast<T *>(a.dx);
+  T *dyo = static_cast<T *>(a.dy);
+  const float inv_d = 1.f / (float)D;
+  int nb = 0;
+  for (int r0 = ch.x; r0 < ch.y; r0 += RB) {
+    float z[RB][G][4], g[RB][G][4], mean[RB], rstd[RB];
+    load_z<T, G, RB, RES>(z, x, a.x_stride, y, a.y_stride, gt, r0, ch.y, col, ok);
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int row = r0 + rr;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (row < ch.y && ok[j])
+          Quad<T>::load(dh + (int64_t)row * a.dh_stride + col[j], g[rr][j]);
+        else
+          zero4(g[rr][j]);
+      }
+    }
+    if (a.stats) {
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const int row = r0 + rr < ch.y ? r0 + rr : ch.y - 1;
+        const float2 st = a.stats[row];
+        mean[rr] = st.x;
+        rstd[rr] = st.y;
+      }
+    } else {
+      row_stats<G, RB>(z, ok, inv_d, a.eps, mean, rstd, red, nb, wave, lane);
+    }
+    // z <- z_hat; column sums; g <- dh * (1 + scale); the two row sums.
+    float s[2 * RB];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      float sg = 0.f, sgz = 0.f;
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float zh = ok[j] ? (z[rr][j][i] - mean[rr]) * rstd[rr] : 0.f;
+          const float d = g[rr][j][i];
+          ash[j][i] += d;
+          asc[j][i] = fmaf(d, zh, asc[j][i]);
+          const float gg = d * sc[j][i];
+          z[rr][j][i] = zh;
+          g[rr][j][i] = gg;
+          sg += gg;
+          sgz = fmaf(gg, zh, sgz);
+        }
+      s[2 * rr] = sg;
+      s[2 * rr + 1] = sgz;
+    }
+    block_sums<2 * RB>(s, red[nb++ & 1], wave, lane);
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int row = r0 + rr;
+      if (row >= ch.y) break;
+      const float mg = s[2 * rr] * inv_d, mgz = s[2 * rr + 1] * inv_d;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (!ok[j]) continue;
+        float d[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] = rstd[rr] * (g[rr][j][i] - mg - z[rr][j][i] * mgz);
+        if (dz) {
+          float e[4];
+          Quad<T>::load(dz + (int64_t)row * a.dz_stride + col[j], e);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d[i] += e[i];
+        }
+        const int64_t o = (int64_t)row * D + col[j];
+        Quad<T>::store(dxo + o, d);
+        if constexpr (RES) {
+          float yv[4], dyv[4];
+          Quad<T>::load(y + (int64_t)row * a.y_stride + col[j], yv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            agt[j][i] = fmaf(d[i], yv[i], agt[j][i]);
+            dyv[i] = gt[j][i] * d[i];
+          }
+          Quad<T>::store(dyo + o, dyv);
+        }
+      }
+    }
+  }
+  float *part = a.partials + (int64_t)blockIdx.x * 3 * D;
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    if (!ok[j]) continue;
+    Quad<float>::store(part + col[j], ash[j]);
+    Quad<float>::store(part + D + col[j], asc[j]);
+    if constexpr (RES) Quad<float>::store(part + 2 * D + col[j], agt[j]);
+  }
+}
+
+// Grid: x = (range, 256-column block), y = which sum (0 dshift, 1 dscale, 2 dgate).
+__global__ __launch_bounds__(256) void adaln_reduce_kernel(const int32_t *ranges, const float *part, int D,
+                                                           float *o0, float *o1, float *o2) {
+  const int nxb = (D + 255) / 256;
+  const int r = blockIdx.x / nxb, k = blockIdx.y;
+  const int c = (blockIdx.x % nxb) * 256 + threadIdx.x;
+  if (c >= D) return;
+  float *out = k == 0 ? o0 : (k == 1 ? o1 : o2);
+  const int c0 = ranges[r], c1 = ranges[r + 1];
+  const float *src = part + (int64_t)k * D + c;
+  const int64_t step = 3 * (int64_t)D;
+  float s = 0.f;
+  int q = c0;
+  for (; q + 8 <= c1; q += 8) {  // eight loads in flight, added in chunk order
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = src[(int64_t)(q + u) * step];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += t[u];
+  }
+  for (; q < c1; ++q) s += src[(int64_t)q * step];
+  out[(int64_t)r * D + c] = s;
+}
+
+// Column groups per thread: ceil(D / 1024) rounded up to an instantiated size.
+int groups_for(int D) {
+  const int g = (D + 4 * kThreads - 1) / (4 * kThreads);
+  return g <= 4 ? g : (g <= 6 ? 6 : 8);
+}
+
+template <typename T, int G>
+hipError_t fwd_g(const PlanDev &p, const AdalnFwdArgs &a, hipStream_t s) {
+  if (a.y)
+    hipLaunchKernelGGL((adaln_fwd_kernel<T, G, true>), dim3(p.num_mod_chunks), dim3(kThreads), 0, s, p, a);
+  else
+    hipLaunchKernelGGL((adaln_fwd_kernel<T, G, false>), dim3(p.num_mod_chunks), dim3(kThreads), 0, s, p, a);
+  return hipGetLastError();
+}
+
+template <typename T, int G>
+hipError_t bwd_g(const PlanDev &p, const AdalnBwdArgs &a, hipStream_t s) {
+  if (a.y)
+    hipLaunchKernelGGL((adaln_bwd_kernel<T, G, true>), dim3(p.num_mod_chunks), dim3(kThreads), 0, s, p, a);
+  else
+    hipLaunchKernelGGL((adaln_bwd_kernel<T, G, false>), dim3(p.num_mod_chunks), dim3(kThreads), 0, s, p, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t fwd_t(const PlanDev &p, const AdalnFwdArgs &a, hipStream_t s) {
+  switch (groups_for(a.dim)) {
+    case 1: return fwd_g<T, 1>(p, a, s);
+    case 2: return fwd_g<T, 2>(p, a, s);
+    case 3: return fwd_g<T, 3>(p, a, s);
+    case 4: return fwd_g<T, 4>(p, a, s);
+    case 6: return fwd_g<T, 6>(p, a, s);
+    case 8: return fwd_g<T, 8>(p, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t bwd_t(const PlanDev &p, const AdalnBwdArgs &a, hipStream_t s) {
+  switch (groups_for(a.dim)) {
+    case 1: return bwd_g<T, 1>(p, a, s);
+    case 2: return bwd_g<T, 2>(p, a, s);
+    case 3: return bwd_g<T, 3>(p, a, s);
+    case 4: return bwd_g<T, 4>(p, a, s);
+    case 6: return bwd_g<T, 6>(p, a, s);
+    case 8: return bwd_g<T, 8>(p, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_adaln_fwd(int dtype, const PlanDev &p, const AdalnFwdArgs &a, hipStream_t stream) {
+  if (a.dim < 4 || a.dim > kAdalnMaxDim || a.dim % 4) return hipErrorInvalidValue;
+  return dtype == MMDIT_BF16 ? fwd_t<bf16>(p, a, stream) : fwd_t<float>(p, a, stream);
+}
+
+hipError_t launch_adaln_bwd(int dtype, const PlanDev &p, const AdalnBwdArgs &a, hipStream_t stream) {
+  if (a.dim < 4 || a.dim > kAdalnMaxDim || a.dim % 4) return hipErrorInvalidValue;
+  return dtype == MMDIT_BF16 ? bwd_t<bf16>(p, a, stream) : bwd_t<float>(p, a, stream);
+}
+
+hipError_t launch_adaln_reduce(const PlanDev &p, const float *partials, int dim, float *out0, float *out1,
+                               float *out2, hipStream_t stream) {
+  const dim3 grid((unsigned)((dim + 255) / 256) * 2u * (unsigned)p.num_samples, out2 ? 3 : 2);
+  hipLaunchKernelGGL(adaln_reduce_kernel, grid, dim3(256), 0, stream, p.mod_ranges, partials, dim, out0, out1,
+                     out2);
+  return hipGetLastError();
+}
+
+}  // namespace mmdit

@@ -98,6 +98,9 @@ static PlanDev plan_dev(const mmdit_plan &p, const void *blob) {
   d.num_bwd_blocks = p.num_bwd_blocks;
   d.rope_rows = p.rope_rows;
   d.rope_frame_pairs = p.rope_frame_pairs;
+  d.mod_chunks = reinterpret_cast<const int4 *>(b + p.off_mod_chunks);
+  d.mod_ranges = reinterpret_cast<const int32_t *>(b + p.off_mod_ranges);
+  d.num_mod_chunks = p.num_mod_chunks;
   d.rms_eps = p.rms_eps;
   return d;
 }
@@ -277,6 +280,123 @@ static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmd
   return MMDIT_OK;
 }
 
+// Rows of the adaLN op: D elements per row, `stride` elements between rows.
+static mmdit_status check_rows(const char *name, const void *p, int64_t stride, int64_t D) {
+  if (!p) return fail(MMDIT_ERR_INVALID_ARG, "%s must not be NULL", name);
+  if (!aligned16(p)) return fail(MMDIT_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  if (stride < D || stride % 4 != 0 || stride > MMDIT_MAX_ROW_STRIDE)
+    return fail(MMDIT_ERR_INVALID_ARG, "%s stride %lld must be >= model_dim (%lld), <= %lld and a multiple of 4",
+                name, (long long)stride, (long long)D, (long long)MMDIT_MAX_ROW_STRIDE);
+  return MMDIT_OK;
+}
+
+static mmdit_status check_dim_eps(int32_t D, float eps) {
+  if (D < 4 || D > kAdalnMaxDim || D % 4 != 0)
+    return fail(MMDIT_ERR_UNSUPPORTED, "model_dim %d must be a multiple of 4 in [4, %d]", D, kAdalnMaxDim);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MMDIT_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  return MMDIT_OK;
+}
+
+static mmdit_status adaln_fwd(const mmdit_plan *plan, const void *blob, const mmdit_adaln_fwd_args *a,
+                              void *stream) {
+  mmdit_status st = check_plan(plan, blob);
+  if (st) return st;
+  if (!a) return fail(MMDIT_ERR_INVALID_ARG, "args must not be NULL");
+  if ((st = check_dim_eps(a->model_dim, a->eps))) return st;
+  const int64_t N = plan->total_tokens, S = plan->num_samples, D = a->model_dim;
+  const int elt = plan->dtype == MMDIT_BF16 ? 2 : 4;
+  const bool res = a->y != nullptr;
+  std::vector<Span> spans;
+  if ((st = check_rows("x", a->x, a->x_stride, D)) || (st = check_ptr("shift", a->shift)) ||
+      (st = check_ptr("scale", a->scale)) || (st = check_ptr("h", a->h)))
+    return st;
+  spans.push_back(span("x", a->x, N, a->x_stride, D, elt, false));
+  spans.push_back(span("shift", a->shift, 2 * S, D, D, 4, false));
+  spans.push_back(span("scale", a->scale, 2 * S, D, D, 4, false));
+  spans.push_back(span("h", a->h, N, D, D, elt, true));
+  if (res) {
+    if ((st = check_rows("y", a->y, a->y_stride, D)) || (st = check_ptr("gate", a->gate)) ||
+        (st = check_ptr("z", a->z)))
+      return st;
+    spans.push_back(span("y", a->y, N, a->y_stride, D, elt, false));
+    spans.push_back(span("gate", a->gate, 2 * S, D, D, 4, false));
+    spans.push_back(span("z", a->z, N, D, D, elt, true));
+  } else if (a->gate || a->z) {
+    return fail(MMDIT_ERR_INVALID_ARG, "gate and z are only taken with y (the gated residual)");
+  }
+  if (a->stats) {
+    if ((st = check_ptr("stats", a->stats))) return st;
+    spans.push_back(span("stats", a->stats, N, 2, 2, 4, true));
+  }
+  if ((st = check_aliasing(spans))) return st;
+  const PlanDev pd = plan_dev(*plan, blob);
+  AdalnFwdArgs fa{a->x, a->y, a->x_stride, a->y_stride, a->shift, a->scale, a->gate, a->z, a->h,
+                  reinterpret_cast<float2 *>(a->stats), a->model_dim, a->eps};
+  hipError_t e = launch_adaln_fwd(plan->dtype, pd, fa, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("adaLN forward", e);
+  return MMDIT_OK;
+}
+
+static mmdit_status adaln_bwd(const mmdit_plan *plan, const void *blob, const mmdit_adaln_bwd_args *a, void *ws,
+                              uint64_t ws_bytes, void *stream) {
+  mmdit_status st = check_plan(plan, blob);
+  if (st) return st;
+  if (!a) return fail(MMDIT_ERR_INVALID_ARG, "args must not be NULL");
+  if ((st = check_dim_eps(a->model_dim, a->eps))) return st;
+  const int64_t N = plan->total_tokens, S = plan->num_samples, D = a->model_dim;
+  const int elt = plan->dtype == MMDIT_BF16 ? 2 : 4;
+  const bool res = a->y != nullptr;
+  const uint64_t need = (uint64_t)plan->num_mod_chunks * 3 * (uint64_t)D * 4;
+  if (!ws || !aligned16(ws))
+    return fail(MMDIT_ERR_INVALID_ARG, "workspace must be a non-NULL 16-byte aligned device pointer");
+  if (ws_bytes < need)
+    return fail(MMDIT_ERR_BUFFER_TOO_SMALL, "adaLN backward workspace needs %llu bytes, got %llu",
+                (unsigned long long)need, (unsigned long long)ws_bytes);
+  std::vector<Span> spans;
+  if ((st = check_rows("x", a->x, a->x_stride, D)) || (st = check_rows("dh", a->dh, a->dh_stride, D)) ||
+      (st = check_ptr("scale", a->scale)) || (st = check_ptr("dx", a->dx)) ||
+      (st = check_ptr("dshift", a->dshift)) || (st = check_ptr("dscale", a->dscale)))
+    return st;
+  spans.push_back(span("workspace", ws, 1, (int64_t)need, (int64_t)need, 1, true));
+  spans.push_back(span("x", a->x, N, a->x_stride, D, elt, false));
+  spans.push_back(span("dh", a->dh, N, a->dh_stride, D, elt, false));
+  spans.push_back(span("scale", a->scale, 2 * S, D, D, 4, false));
+  spans.push_back(span("dx", a->dx, N, D, D, elt, true));
+  spans.push_back(span("dshift", a->dshift, 2 * S, D, D, 4, true));
+  spans.push_back(span("dscale", a->dscale, 2 * S, D, D, 4, true));
+  if (res) {
+    if ((st = check_rows("y", a->y, a->y_stride, D)) || (st = check_ptr("gate", a->gate)) ||
+        (st = check_ptr("dy", a->dy)) || (st = check_ptr("dgate", a->dgate)))
+      return st;
+    spans.push_back(span("y", a->y, N, a->y_stride, D, elt, false));
+    spans.push_back(span("gate", a->gate, 2 * S, D, D, 4, false));
+    spans.push_back(span("dy", a->dy, N, D, D, elt, true));
+    spans.push_back(span("dgate", a->dgate, 2 * S, D, D, 4, true));
+  } else if (a->gate || a->dy || a->dgate) {
+    return fail(MMDIT_ERR_INVALID_ARG, "gate, dy and dgate are only taken with y (the gated residual)");
+  }
+  if (a->dz) {
+    if ((st = check_rows("dz", a->dz, a->dz_stride, D))) return st;
+    spans.push_back(span("dz", a->dz, N, a->dz_stride, D, elt, false));
+  }
+  if (a->stats) {
+    if ((st = check_ptr("stats", a->stats))) return st;
+    spans.push_back(span("stats", a->stats, N, 2, 2, 4, false));
+  }
+  if ((st = check_aliasing(spans))) return st;
+  const PlanDev pd = plan_dev(*plan, blob);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *part = static_cast<float *>(ws);
+  AdalnBwdArgs ba{a->x, a->y, a->dh, a->dz, a->x_stride, a->y_stride, a->dh_stride, a->dz_stride,
+                  a->scale, a->gate, reinterpret_cast<const float2 *>(a->stats), a->dx, a->dy, part,
+                  a->model_dim, a->eps};
+  hipError_t e = launch_adaln_bwd(plan->dtype, pd, ba, s);
+  if (e != hipSuccess) return hip_fail("adaLN backward", e);
+  e = launch_adaln_reduce(pd, part, a->model_dim, a->dshift, a->dscale, res ? a->dgate : nullptr, s);
+  if (e != hipSuccess) return hip_fail("adaLN modulation-gradient reduction", e);
+  return MMDIT_OK;
+}
+
 }  // namespace mmdit
 
 extern "C" {
@@ -326,6 +446,27 @@ mmdit_status mmdit_attn_bwd(const mmdit_plan *plan, const void *plan_blob_dev, c
     return mmdit::attn_bwd(plan, plan_blob_dev, args, workspace, workspace_bytes, hip_stream);
   } catch (...) {
     return mmdit::fail(MMDIT_ERR_INVALID_ARG, "backward failed on the host");
+  }
+}
+
+mmdit_status mmdit_adaln_fwd(const mmdit_plan *plan, const void *plan_blob_dev,
+                             const mmdit_adaln_fwd_args *args, void *hip_stream) {
+  mmdit::clear_error();
+  try {
+    return mmdit::adaln_fwd(plan, plan_blob_dev, args, hip_stream);
+  } catch (...) {
+    return mmdit::fail(MMDIT_ERR_INVALID_ARG, "adaLN forward failed on the host");
+  }
+}
+
+mmdit_status mmdit_adaln_bwd(const mmdit_plan *plan, const void *plan_blob_dev,
+                             const mmdit_adaln_bwd_args *args, void *workspace, uint64_t workspace_bytes,
+                             void *hip_stream) {
+  mmdit::clear_error();
+  try {
+    return mmdit::adaln_bwd(plan, plan_blob_dev, args, workspace, workspace_bytes, hip_stream);
+  } catch (...) {
+    return mmdit::fail(MMDIT_ERR_INVALID_ARG, "adaLN backward failed on the host");
   }
 }
 

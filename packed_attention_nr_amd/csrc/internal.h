@@ -19,6 +19,8 @@ constexpr int kFwdTileBf16 = 256;
 constexpr int kFwdTileF32 = 128;
 constexpr int kBwdTile = 128;
 // Limits checked by the plan.
+constexpr int kModChunkRows = 32;               // rows per adaLN workgroup (one modulation row)
+constexpr int kAdalnMaxDim = 8192;              // largest adaLN model width
 constexpr int kMaxGridSide = 32768;             // row and col fit in 15 bits of tok_meta
 constexpr int64_t kMaxTokens = 1ll << 29;  // byte offsets of [N] fp32 vectors fit 31 bits
 constexpr int64_t kMaxElements = 1ll << 40;     // N*H*d
@@ -77,6 +79,9 @@ struct PlanDev {
   int32_t num_samples, total_tokens, num_heads, head_dim;
   int32_t num_fwd_items, num_bwd_items, num_fwd_blocks, num_bwd_blocks, rope_rows;
   int32_t rope_frame_pairs;    // pairs [0, fp) turn by frame, then row, then column
+  const int4 *mod_chunks;      // [num_mod_chunks] {row_start, row_end, 2*sample + stream, 0}
+  const int32_t *mod_ranges;   // [2S+1] first chunk of each (sample, stream) range
+  int32_t num_mod_chunks;
   float rms_eps;
 };
 
@@ -136,6 +141,29 @@ struct PrologueBwdArgs {
   int32_t num_blocks;
 };
 
+// adaLN modulation (+ fused gated residual). Modulation tables are fp32
+// [S][2][D] (row 2*sample + stream).
+struct AdalnFwdArgs {
+  const void *x, *y;           // [N][D] dtype with strides; y == nullptr: no residual
+  int64_t x_stride, y_stride;
+  const float *shift, *scale, *gate;
+  void *z, *h;                 // dense [N][D] dtype; z only with y
+  float2 *stats;               // [N] {mean, rstd} or nullptr
+  int32_t dim;
+  float eps;
+};
+
+struct AdalnBwdArgs {
+  const void *x, *y, *dh, *dz; // dz == nullptr: no gradient arriving at z directly
+  int64_t x_stride, y_stride, dh_stride, dz_stride;
+  const float *scale, *gate;
+  const float2 *stats;         // from the forward, or nullptr = recompute
+  void *dx, *dy;               // dense [N][D] dtype; dy only with y
+  float *partials;             // [num_mod_chunks][3][D]: dshift, dscale, dgate sums
+  int32_t dim;
+  float eps;
+};
+
 // Launchers: enqueue on `stream`, return the launch status.
 hipError_t launch_prologue_fwd(int dtype, const PlanDev &p, const PrologueFwdArgs &a,
                                hipStream_t stream);
@@ -148,6 +176,12 @@ hipError_t launch_prologue_bwd(int dtype, const PlanDev &p, const PrologueBwdArg
                                hipStream_t stream);
 // dgains[m][e] = fixed-order sums of the gain partials: rows m = 0, 1 from
 // part_q[0..nq), rows m = 2, 3 from part_k[0..nk).
+hipError_t launch_adaln_fwd(int dtype, const PlanDev &p, const AdalnFwdArgs &a, hipStream_t stream);
+hipError_t launch_adaln_bwd(int dtype, const PlanDev &p, const AdalnBwdArgs &a, hipStream_t stream);
+// Fixed-order sums of the partials over each range's chunks -> out_k [S][2][D]
+// for k = 0 (dshift), 1 (dscale), 2 (dgate, skipped when out2 is nullptr).
+hipError_t launch_adaln_reduce(const PlanDev &p, const float *partials, int dim, float *out0,
+                               float *out1, float *out2, hipStream_t stream);
 hipError_t launch_gain_reduce(const float *part_q, int nq, const float *part_k, int nk, int d,
                               float *dgains, hipStream_t stream);
 

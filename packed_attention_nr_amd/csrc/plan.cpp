@@ -197,6 +197,23 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, const int32_t *src_h, const
   block_map(qt, fwd_blocks);
   block_map(kt, bwd_blocks);
 
+  // Row chunks of the adaLN kernels: each (sample, stream) token range (text
+  // [cu, cu + T), image [cu + T, cu + L)) cut into pieces of at most
+  // kModChunkRows rows, so that a workgroup's rows share one modulation row
+  // and its gradient partials belong to one range.
+  std::vector<int32_t> mod_chunks, mod_ranges(2 * S + 1, 0);
+  for (int i = 0; i < S; ++i)
+    for (int m = 0; m < 2; ++m) {
+      const int64_t a = cu[i] + (m ? desc->text_len[i] : 0), b = m ? cu[i + 1] : cu[i] + desc->text_len[i];
+      for (int64_t r = a; r < b; r += kModChunkRows) {
+        mod_chunks.push_back((int32_t)r);
+        mod_chunks.push_back((int32_t)std::min<int64_t>(b, r + kModChunkRows));
+        mod_chunks.push_back(2 * i + m);
+        mod_chunks.push_back(0);
+      }
+      mod_ranges[2 * i + m + 1] = (int32_t)(mod_chunks.size() / 4);
+    }
+
   mmdit_plan p;
   std::memset(&p, 0, sizeof(p));
   p.num_samples = S;
@@ -211,6 +228,8 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, const int32_t *src_h, const
   p.num_bwd_items = (int32_t)n_bwd;
   p.num_fwd_blocks = (int32_t)(fwd_blocks.size() / 2);
   p.num_bwd_blocks = (int32_t)(bwd_blocks.size() / 2);
+  p.num_mod_chunks = (int32_t)(mod_chunks.size() / 4);
+  p.mod_chunk_rows = kModChunkRows;
   p.rope_rows = rope_rows;
   p.rope_frame_pairs = frame_pairs;
   p.rope_theta = desc->rope_theta;
@@ -230,6 +249,10 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, const int32_t *src_h, const
   off = align_up(off + 4ull * bwd_blocks.size(), 256);
   p.off_rope = off;
   off = align_up(off + 8ull * rope_rows * (d / 2), 256);
+  p.off_mod_chunks = off;
+  off = align_up(off + 4ull * mod_chunks.size(), 256);
+  p.off_mod_ranges = off;
+  off = align_up(off + 4ull * mod_ranges.size(), 256);
   p.blob_bytes = off;
 
   const uint64_t elt = desc->dtype == MMDIT_BF16 ? 2 : 4;
@@ -292,6 +315,8 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, const int32_t *src_h, const
 
   std::memcpy(blob + p.off_fwd_blocks, fwd_blocks.data(), 4 * fwd_blocks.size());
   std::memcpy(blob + p.off_bwd_blocks, bwd_blocks.data(), 4 * bwd_blocks.size());
+  std::memcpy(blob + p.off_mod_chunks, mod_chunks.data(), 4 * mod_chunks.size());
+  std::memcpy(blob + p.off_mod_ranges, mod_ranges.data(), 4 * mod_ranges.size());
 
   // RoPE table [rope_rows][d/2] of {cos, sin}(pos * omega_p), in double,
   // rounded once.

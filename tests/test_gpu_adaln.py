@@ -1,0 +1,174 @@
+"""adaLN modulation with the fused gated residual on the GPU, through the C
+ABI, against the fp64 oracle: small packs (generation and editing, every
+instantiated column-group count, with and without the residual, saved or
+recomputed statistics, an extra gradient at z) and the mixed-resolution
+training batch at model width 3072; each sample alone gives the same bits.
+Marked ``gpu``: needs an MI355X and the built library."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import F32_TOL, errors
+
+# bf16 gate of the adaLN outputs: its token tensors reach |v| ~ 10 (x is
+# scaled and offset per row), where storing to bf16 alone moves a value by up
+# to half an ulp, 2^-8 |v|. Errors are therefore taken relative to the
+# tensor's largest magnitude: max|g - r| / max|r| <= 5e-3 (2^-8 = 3.9e-3 plus
+# fp32 arithmetic) and relative L2 <= 5e-3; the modulation gradients (sums
+# over up to thousands of rows) on relative L2 only. fp32: normwise <= 1e-5.
+BF16_NORMWISE = 5e-3
+BF16_REL_L2 = 5e-3
+
+
+def check(name, got, ref, dtype, *, l2_only=False, failures=None):
+    e = errors(got, ref)
+    if dtype == "f32":
+        ok = e["normwise"] <= F32_TOL
+    elif l2_only:
+        ok = e["rel_l2"] <= BF16_REL_L2
+    else:
+        ok = e["normwise"] <= BF16_NORMWISE and e["rel_l2"] <= BF16_REL_L2
+    msg = f"{name}: max_abs={e['max_abs']:.3e} normwise={e['normwise']:.3e} rel_l2={e['rel_l2']:.3e}"
+    if failures is not None and not ok:
+        failures.append(msg)
+    return ok, msg
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import packed_attention_nr_amd as pam
+    pam.lib()  # must load: no fallback
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _geometry(name):
+    if name == "edit":
+        return dict(text=[7, 0, 40], grids=[(5, 9), (6, 6), (0, 0)], src=[(9, 5), (6, 6), (0, 0)])
+    if name == "mixed":
+        return dict(text=[33, 0, 1, 70], grids=[(8, 8), (3, 11), (0, 0), (2, 2)], src=None)
+    raise KeyError(name)
+
+
+def _run(pack, a, residual, dtype, save_stats, with_dz, eps=1e-6):
+    import packed_attention_nr_amd as pam
+    dev = "cuda"
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    up = lambda k: torch.from_numpy(np.ascontiguousarray(a[k])).to(dev, tdt)
+    f32 = lambda k: torch.from_numpy(np.ascontiguousarray(a[k])).to(dev)
+    x, dh = up("x"), up("dh")
+    y = up("y") if residual else None
+    gate = f32("gate") if residual else None
+    dz = up("dz") if with_dz else None
+    fw = pam.adaln_forward(pack, x, f32("shift"), f32("scale"), y=y, gate=gate, eps=eps,
+                           save_stats=save_stats)
+    bw = pam.adaln_backward(pack, x, f32("scale"), dh, y=y, gate=gate, dz=dz,
+                            stats=fw.get("stats"), eps=eps)
+    torch.cuda.synchronize()
+    host = lambda t: t.detach().to(torch.float64).cpu().numpy()
+    out = {k: host(v) for k, v in fw.items()}
+    out.update({k: host(v) for k, v in bw.items()})
+    return out
+
+
+def _oracle(lay, a, residual, with_dz, eps=1e-6):
+    y = a["y"] if residual else None
+    g = a["gate"] if residual else None
+    f = oracle.adaln_forward(lay, a["x"], a["shift"], a["scale"], eps, y, g)
+    b = oracle.adaln_backward(lay, a["x"], a["shift"], a["scale"], a["dh"], eps, y, g,
+                              a["dz"] if with_dz else None)
+    f.update(b)
+    return f
+
+
+def _compare(got, ref, residual, dtype, save_stats):
+    fails = []
+    keys = ["h", "dx", "dshift", "dscale"] + (["z", "dy", "dgate"] if residual else [])
+    for k in keys:
+        _, msg = check(k, got[k], ref[k], dtype, l2_only=k.startswith("ds") or k == "dgate",
+                       failures=fails)
+        _say("   " + msg)
+    if save_stats:
+        for i, k in enumerate(("mean", "rstd")):
+            _, msg = check(k, got["stats"][:, i], ref[k], dtype, failures=fails)
+            _say("   " + msg)
+    assert not fails, fails
+
+
+def _pack(geo, dtype):
+    import packed_attention_nr_amd as pam
+    src = geo["src"]
+    return pam.Pack(geo["text"], [g[0] for g in geo["grids"]], [g[1] for g in geo["grids"]], 1, 64,
+                    dtype, src_h=None if src is None else [g[0] for g in src],
+                    src_w=None if src is None else [g[1] for g in src])
+
+
+def _lay(geo):
+    src = geo["src"]
+    return oracle.layout(geo["text"], [g[0] for g in geo["grids"]], [g[1] for g in geo["grids"]],
+                         None if src is None else [g[0] for g in src],
+                         None if src is None else [g[1] for g in src])
+
+
+# D = 64 .. 8192 covers every column-group count (1, 2, 3, 4, 6, 8 groups of
+# 1024 columns), with partial groups (1000, 5000) and the widest (8192).
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 1000, 2048, 3072, 4096, 5000, 8192])
+@pytest.mark.parametrize("geo", ["mixed", "edit"])
+def test_adaln_small_packs(geo, D, dtype):
+    g = _geometry(geo)
+    lay = _lay(g)
+    S, N = len(g["text"]), lay.num_tokens
+    pack = _pack(g, dtype)
+    for residual, save_stats, with_dz in ((True, True, True), (False, False, False),
+                                          (True, False, False), (False, True, True)):
+        a = workloads.draw_adaln(D + len(geo), N, S, D, dtype, residual=True)
+        _say(f"adaln {geo} D={D} {dtype} N={N} residual={residual} stats={save_stats} dz={with_dz}")
+        got = _run(pack, a, residual, dtype, save_stats, with_dz)
+        _compare(got, _oracle(lay, a, residual, with_dz), residual, dtype, save_stats)
+
+
+def test_adaln_samples_alone_bitwise():
+    """Each sample's rows and its modulation gradients are bitwise those of
+    the sample run as a pack of its own."""
+    g = _geometry("mixed")
+    lay = _lay(g)
+    S, N, D = len(g["text"]), lay.num_tokens, 3072
+    a = workloads.draw_adaln(5, N, S, D, "bf16")
+    full = _run(_pack(g, "bf16"), a, True, "bf16", True, True)
+    off = lay.cu_seqlens
+    for i in range(S):
+        gi = dict(text=[g["text"][i]], grids=[g["grids"][i]], src=None)
+        rows = slice(int(off[i]), int(off[i + 1]))
+        ai = {k: (v[rows] if v.shape[0] == N and v.ndim == 2 else v[i:i + 1]) for k, v in a.items()}
+        alone = _run(_pack(gi, "bf16"), ai, True, "bf16", True, True)
+        bad = [k for k in ("h", "z", "dx", "dy", "stats") if not np.array_equal(full[k][rows], alone[k])]
+        bad += [k for k in ("dshift", "dscale", "dgate") if not np.array_equal(full[k][i:i + 1], alone[k])]
+        _say(f"   sample {i}: {'bitwise equal' if not bad else bad}")
+        assert not bad, (i, bad)
+
+
+def test_adaln_mixed_resolution_batch():
+    """The mixed-resolution training batch (6 samples, 20,436 tokens) at model
+    width 3072 (24 heads x 128), bf16, gated residual, every output."""
+    inp = workloads.draw("mixed6", backward=False)
+    lay = oracle.layout(inp.text_len, inp.grid_h, inp.grid_w)
+    S, N, D = len(inp.text_len), lay.num_tokens, 3072
+    import packed_attention_nr_amd as pam
+    pack = pam.Pack(inp.text_len, inp.grid_h, inp.grid_w, 24, 128, "bf16")
+    a = workloads.draw_adaln(1, N, S, D, "bf16")
+    _say(f"adaln mixed6 N={N} D={D}")
+    got = _run(pack, a, True, "bf16", True, True)
+    _compare(got, _oracle(lay, a, True, True), True, "bf16", True)

@@ -29,7 +29,7 @@ def test_exports_every_header_symbol(L):
     assert {"mmdit_pack_plan", "mmdit_attn_fwd", "mmdit_attn_bwd"} <= names
     for n in sorted(names):
         assert hasattr(L, n), n
-    assert pam.mmdit_abi_version() == pam.ABI_VERSION == 2
+    assert pam.mmdit_abi_version() == pam.ABI_VERSION == 3
     assert pam.mmdit_status_str(0) == "ok"
 
 
@@ -110,6 +110,22 @@ def _check_plan(inp, dtype_code):
     ang = pos * om[None, :]
     assert np.array_equal(rope[..., 0], np.cos(ang).astype(np.float32))
     assert np.array_equal(rope[..., 1], np.sin(ang).astype(np.float32))
+    # adaLN row chunks: each inside one (sample, stream) range, at most
+    # mod_chunk_rows rows, covering every token once, ranges in order
+    C_ = plan.num_mod_chunks
+    ch = _blob_section(blob, plan.off_mod_chunks, 4 * C_, np.int32).reshape(-1, 4)
+    rg = _blob_section(blob, plan.off_mod_ranges, 2 * S + 1, np.int32)
+    assert plan.mod_chunk_rows == 32 and rg[0] == 0 and rg[-1] == C_ and np.all(np.diff(rg) >= 0)
+    midx = oracle.modulation_index(lay)
+    cover = np.zeros(N, np.int64)
+    for c, (r0, r1, r, zero) in enumerate(ch.tolist()):
+        assert zero == 0 and 0 < r1 - r0 <= 32 and rg[r] <= c < rg[r + 1]
+        assert np.all(midx[r0:r1] == r)
+        cover[r0:r1] += 1
+    assert np.all(cover == 1)
+    for r in range(2 * S):   # a range's chunks are consecutive and ordered
+        rows = [x for c in range(rg[r], rg[r + 1]) for x in range(ch[c, 0], ch[c, 1])]
+        assert rows == np.flatnonzero(midx == r).tolist()
     return plan
 
 
@@ -330,6 +346,65 @@ def _bwd(plan, ws_bytes=None, **kw):
 def test_bwd_rejects_invalid_arguments(small_plan, kw, code):
     ws_bytes = kw.pop("ws_bytes", None)
     assert _bwd(small_plan, ws_bytes=ws_bytes, **kw) == code, pam.mmdit_last_error()
+
+
+def _adaln_fwd(plan, **kw):
+    args = dict(x=_p(1), y=_p(2), x_stride=3072, y_stride=3072, shift=_p(3), scale=_p(4),
+                gate=_p(5), model_dim=3072, eps=1e-6, z=_p(6), h=_p(7), stats=_p(8), blob=_p(0))
+    args.update(kw)
+    a = pam.AdalnFwdArgs(*(args[n] for n, _ in pam.AdalnFwdArgs._fields_))
+    return pam.lib().mmdit_adaln_fwd(C.byref(plan), args["blob"], C.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1),
+    (dict(x=_p(1) + 8), 1),               # misaligned
+    (dict(x_stride=3000), 1),             # stride < D
+    (dict(y_stride=3074), 1),             # not a multiple of 4
+    (dict(model_dim=3070), 2),            # D not a multiple of 4
+    (dict(model_dim=8196, x_stride=8196, y_stride=8196), 2),  # D above 8192
+    (dict(model_dim=0), 2),
+    (dict(eps=-1.0), 1),
+    (dict(eps=float("inf")), 1),
+    (dict(shift=None), 1),
+    (dict(h=None), 1),
+    (dict(gate=None), 1),                 # the residual needs its gate
+    (dict(z=None), 1),                    # ... and writes z
+    (dict(y=None), 1),                    # gate and z given without y
+    (dict(h=_p(1) + 4096), 1),            # h overlaps x
+    (dict(stats=_p(7) + 64), 1),          # stats overlaps h
+    (dict(blob=None), 1),
+])
+def test_adaln_fwd_rejects_invalid_arguments(small_plan, kw, code):
+    assert _adaln_fwd(small_plan, **kw) == code, pam.mmdit_last_error()
+
+
+def _adaln_bwd(plan, **kw):
+    args = dict(x=_p(1), y=_p(2), x_stride=1024, y_stride=1024, scale=_p(3), gate=_p(4),
+                model_dim=1024, eps=1e-6, stats=_p(5), dh=_p(6), dz=_p(7), dh_stride=1024,
+                dz_stride=1024, dx=_p(8), dy=_p(9), dshift=_p(10), dscale=_p(11), dgate=_p(12))
+    ws = kw.pop("ws", _p(13))
+    wsb = kw.pop("ws_bytes", plan.num_mod_chunks * 3 * 1024 * 4)
+    args.update(kw)
+    a = pam.AdalnBwdArgs(*(args[n] for n, _ in pam.AdalnBwdArgs._fields_))
+    return pam.lib().mmdit_adaln_bwd(C.byref(plan), _p(0), C.byref(a), ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dh=None), 1),
+    (dict(dx=None), 1),
+    (dict(dscale=None), 1),
+    (dict(dgate=None), 1),                # the residual writes dgate
+    (dict(y=None), 1),                    # gate, dy, dgate given without y
+    (dict(dz_stride=1000), 1),
+    (dict(ws=None), 1),
+    (dict(ws_bytes=1024), 3),
+    (dict(dx=_p(6)), 1),                  # dx overlaps dh
+    (dict(dshift=_p(13)), 1),             # dshift overlaps the workspace
+    (dict(model_dim=1026), 2),
+])
+def test_adaln_bwd_rejects_invalid_arguments(small_plan, kw, code):
+    assert _adaln_bwd(small_plan, **kw) == code, pam.mmdit_last_error()
 
 
 # --------------------------------------------------------------------------

@@ -29,7 +29,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "draw", "bf16_round", "bf16_bits",
-    "random_pack", "Inputs",
+    "random_pack", "Inputs", "draw_adaln",
 ]
 
 
@@ -184,6 +184,32 @@ def draw(w: Workload | str, seed: int = 0, backward: Optional[bool] = None) -> I
     bw = w.backward if backward is None else backward
     return _finish(rng, text, hs, ws, w.heads, w.head_dim, w.dtype, bw,
                    w.rope_theta, w.rms_eps, w.src)
+
+
+def draw_adaln(seed: int, num_tokens: int, num_samples: int, dim: int, dtype: str = "bf16",
+               residual: bool = True) -> dict:
+    """Inputs of the adaLN modulation / gated residual op for a pack of
+    num_tokens tokens and num_samples samples at model width dim, from one
+    ``default_rng(seed)`` stream in this order: per-row offsets N(0,1) and
+    scales U(0.5, 2) of x, then x, y, dh, dz ~ N(0,1) [N, dim] (x scaled and
+    offset per row), then shift, scale ~ 0.3 N(0,1) and gate ~ N(0,1)
+    [S, 2, dim]. Token tensors are rounded to bf16 for bf16 packs; the
+    modulation tables stay fp32."""
+    rng = np.random.default_rng(seed)
+    N, S, D = num_tokens, num_samples, dim
+    off = rng.standard_normal((N, 1)).astype(np.float32)
+    sc = rng.uniform(0.5, 2.0, (N, 1)).astype(np.float32)
+    t = lambda: rng.standard_normal((N, D), dtype=np.float32)
+    x = t() * sc + off
+    y, dh, dz = t(), t(), t()
+    if dtype == "bf16":
+        x, y, dh, dz = (bf16_round(a) for a in (x, y, dh, dz))
+    m = lambda k: (k * rng.standard_normal((S, 2, D))).astype(np.float32)
+    out = dict(x=x, dh=dh, dz=dz, shift=m(0.3), scale=m(0.3))
+    gate = m(1.0)
+    if residual:
+        out.update(y=y, gate=gate)
+    return out
 
 
 def random_pack(seed: int, *, max_samples: int = 4, max_text: int = 40,
