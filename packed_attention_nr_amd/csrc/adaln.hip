@@ -29,33 +29,39 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Four consecutive elements as loaded (bf16x4 or float4) and their fp32 values.
 template <typename T>
 struct Quad;
 template <>
 struct Quad<bf16> {
-  __device__ static void load(const bf16 *p, float (&x)[4]) {
-    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+  typedef bf16x4 raw;
+  __device__ static raw zero() { return raw{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f}; }
+  __device__ static raw load(const bf16 *p) { return *reinterpret_cast<const raw *>(p); }
+  __device__ static void cvt(raw v, float (&x)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (float)v[i];
   }
   __device__ static void store(bf16 *p, const float (&x)[4]) {
     const bf16x2 a = pack2(x[0], x[1]), b = pack2(x[2], x[3]);
-    const bf16x4 v = {a[0], a[1], b[0], b[1]};
-    *reinterpret_cast<bf16x4 *>(p) = v;
+    const raw v = {a[0], a[1], b[0], b[1]};
+    *reinterpret_cast<raw *>(p) = v;
   }
 };
 template <>
 struct Quad<float> {
-  __device__ static void load(const float *p, float (&x)[4]) {
-    const float4 v = *reinterpret_cast<const float4 *>(p);
+  typedef float4 raw;
+  __device__ static raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ static raw load(const float *p) { return *reinterpret_cast<const raw *>(p); }
+  __device__ static void cvt(raw v, float (&x)[4]) {
     x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
   }
   __device__ static void store(float *p, const float (&x)[4]) {
-    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<raw *>(p) = make_float4(x[0], x[1], x[2], x[3]);
   }
 };
 
 __device__ __forceinline__ void zero4(float (&x)[4]) { x[0] = x[1] = x[2] = x[3] = 0.f; }
+__device__ __forceinline__ void ld_mod(const float *p, float (&x)[4]) { Quad<float>::cvt(Quad<float>::load(p), x); }
 
 // Sums of v[0 .. NV) over the workgroup; every thread gets the same bits.
 // buf: LDS [NV][4]. Consecutive calls must alternate between two buffers.
@@ -71,29 +77,17 @@ __device__ __forceinline__ void block_sums(float (&v)[NV], float *buf, int wave,
   for (int i = 0; i < NV; ++i) v[i] = (buf[4 * i] + buf[4 * i + 1]) + (buf[4 * i + 2] + buf[4 * i + 3]);
 }
 
-// z of RB rows (rows past the chunk and columns past D read as 0).
-template <typename T, int G, int RB, bool RES>
-__device__ __forceinline__ void load_z(float (&z)[RB][G][4], const T *x, int64_t xs,
-                                       const T *y, int64_t ys, const float (&gt)[G][4], int r0, int r1,
-                                       const int (&col)[G], const bool (&ok)[G]) {
+// Raw loads of RB rows of one tensor (rows past the chunk and columns past
+// D give zeros).
+template <typename T, int G, int RB>
+__device__ __forceinline__ void load_rows(typename Quad<T>::raw (&r)[RB][G], const T *base, int64_t stride,
+                                          int r0, int r1, const int (&col)[G], const bool (&ok)[G]) {
 #pragma unroll
-  for (int rr = 0; rr < RB; ++rr) {
-    const int row = r0 + rr;
+  for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      if (row < r1 && ok[j]) {
-        Quad<T>::load(x + (int64_t)row * xs + col[j], z[rr][j]);
-        if constexpr (RES) {
-          float yv[4];
-          Quad<T>::load(y + (int64_t)row * ys + col[j], yv);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) z[rr][j][i] = fmaf(gt[j][i], yv[i], z[rr][j][i]);
-        }
-      } else {
-        zero4(z[rr][j]);
-      }
-    }
-  }
+    for (int j = 0; j < G; ++j)
+      r[rr][j] = (r0 + rr < r1 && ok[j]) ? Quad<T>::load(base + (int64_t)(r0 + rr) * stride + col[j])
+                                         : Quad<T>::zero();
 }
 
 // Mean and rstd of RB rows held in registers (two fixed-order passes).
@@ -130,41 +124,65 @@ __device__ __forceinline__ void row_stats(const float (&z)[RB][G][4], const bool
   for (int rr = 0; rr < RB; ++rr) rstd[rr] = rsqrtf(rstd[rr] * inv_d + eps);
 }
 
+// Rows are loaded one batch ahead: the loads of batch k+1 are in flight while
+// batch k is reduced and stored.
 template <typename T, int G, bool RES>
 __global__ __launch_bounds__(kThreads) void adaln_fwd_kernel(PlanDev p, AdalnFwdArgs a) {
   constexpr int RB = 4;
+  typedef typename Quad<T>::raw raw;
   __shared__ float red[2][64];
   const int4 ch = p.mod_chunks[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int D = a.dim;
   const int64_t mrow = (int64_t)ch.z * D;
-  float sh[G][4], sc[G][4], gt[G][4];
+  const T *x = static_cast<const T *>(a.x);
+  const T *y = static_cast<const T *>(a.y);
   int col[G];
   bool ok[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     col[j] = 4 * (tid + kThreads * j);
     ok[j] = col[j] < D;
+  }
+  raw nx[RB][G], ny[RB][G];
+  load_rows<T, G, RB>(nx, x, a.x_stride, ch.x, ch.y, col, ok);
+  if constexpr (RES) load_rows<T, G, RB>(ny, y, a.y_stride, ch.x, ch.y, col, ok);
+  float sh[G][4], sc[G][4], gt[G][4];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
     zero4(sh[j]);
     zero4(sc[j]);
     zero4(gt[j]);
     if (ok[j]) {
-      Quad<float>::load(a.shift + mrow + col[j], sh[j]);
-      Quad<float>::load(a.scale + mrow + col[j], sc[j]);
-      if constexpr (RES) Quad<float>::load(a.gate + mrow + col[j], gt[j]);
+      ld_mod(a.shift + mrow + col[j], sh[j]);
+      ld_mod(a.scale + mrow + col[j], sc[j]);
+      if constexpr (RES) ld_mod(a.gate + mrow + col[j], gt[j]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[j][i] += 1.f;
   }
-  const T *x = static_cast<const T *>(a.x);
-  const T *y = static_cast<const T *>(a.y);
   T *zo = static_cast<T *>(a.z);
   T *ho = static_cast<T *>(a.h);
   const float inv_d = 1.f / (float)D;
   int nb = 0;
   for (int r0 = ch.x; r0 < ch.y; r0 += RB) {
     float z[RB][G][4], mean[RB], rstd[RB];
-    load_z<T, G, RB, RES>(z, x, a.x_stride, y, a.y_stride, gt, r0, ch.y, col, ok);
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        Quad<T>::cvt(nx[rr][j], z[rr][j]);
+        if constexpr (RES) {
+          float yv[4];
+          Quad<T>::cvt(ny[rr][j], yv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[rr][j][i] = fmaf(gt[j][i], yv[i], z[rr][j][i]);
+        }
+      }
+    if (r0 + RB < ch.y) {
+      load_rows<T, G, RB>(nx, x, a.x_stride, r0 + RB, ch.y, col, ok);
+      if constexpr (RES) load_rows<T, G, RB>(ny, y, a.y_stride, r0 + RB, ch.y, col, ok);
+    }
     row_stats<G, RB>(z, ok, inv_d, a.eps, mean, rstd, red, nb, wave, lane);
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
@@ -185,54 +203,75 @@ __global__ __launch_bounds__(kThreads) void adaln_fwd_kernel(PlanDev p, AdalnFwd
   }
 }
 
+// Backward, also one batch ahead (x, y, dh and dz of batch k+1 in flight).
 template <typename T, int G, bool RES>
 __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwdArgs a) {
-  constexpr int RB = G <= 4 ? 4 : 2;
+  constexpr int RB = G <= 2 ? 4 : (G <= 4 ? 2 : 1);
+  typedef typename Quad<T>::raw raw;
   __shared__ float red[2][64];
   const int4 ch = p.mod_chunks[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int D = a.dim;
   const int64_t mrow = (int64_t)ch.z * D;
-  float sc[G][4], gt[G][4], ash[G][4], asc[G][4], agt[G][4];
+  const T *x = static_cast<const T *>(a.x);
+  const T *y = static_cast<const T *>(a.y);
+  const T *dh = static_cast<const T *>(a.dh);
+  const T *dz = static_cast<const T *>(a.dz);
+  const bool has_dz = dz != nullptr;
   int col[G];
   bool ok[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     col[j] = 4 * (tid + kThreads * j);
     ok[j] = col[j] < D;
+  }
+  raw nx[RB][G], ny[RB][G], ng[RB][G], ne[RB][G];
+  load_rows<T, G, RB>(nx, x, a.x_stride, ch.x, ch.y, col, ok);
+  if constexpr (RES) load_rows<T, G, RB>(ny, y, a.y_stride, ch.x, ch.y, col, ok);
+  load_rows<T, G, RB>(ng, dh, a.dh_stride, ch.x, ch.y, col, ok);
+  if (has_dz) load_rows<T, G, RB>(ne, dz, a.dz_stride, ch.x, ch.y, col, ok);
+  float sc[G][4], gt[G][4], ash[G][4], asc[G][4], agt[G][4];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
     zero4(sc[j]);
     zero4(gt[j]);
     zero4(ash[j]);
     zero4(asc[j]);
     zero4(agt[j]);
     if (ok[j]) {
-      Quad<float>::load(a.scale + mrow + col[j], sc[j]);
-      if constexpr (RES) Quad<float>::load(a.gate + mrow + col[j], gt[j]);
+      ld_mod(a.scale + mrow + col[j], sc[j]);
+      if constexpr (RES) ld_mod(a.gate + mrow + col[j], gt[j]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[j][i] += 1.f;
   }
-  const T *x = static_cast<const T *>(a.x);
-  const T *y = static_cast<const T *>(a.y);
-  const T *dh = static_cast<const T *>(a.dh);
-  const T *dz = static_cast<const T *>(a.dz);
   T *dxo = static_cast<T *>(a.dx);
   T *dyo = static_cast<T *>(a.dy);
   const float inv_d = 1.f / (float)D;
   int nb = 0;
   for (int r0 = ch.x; r0 < ch.y; r0 += RB) {
+    raw cy[RB][G], ce[RB][G];
     float z[RB][G][4], g[RB][G][4], mean[RB], rstd[RB];
-    load_z<T, G, RB, RES>(z, x, a.x_stride, y, a.y_stride, gt, r0, ch.y, col, ok);
 #pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const int row = r0 + rr;
+    for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        if (row < ch.y && ok[j])
-          Quad<T>::load(dh + (int64_t)row * a.dh_stride + col[j], g[rr][j]);
-        else
-          zero4(g[rr][j]);
+        Quad<T>::cvt(nx[rr][j], z[rr][j]);
+        Quad<T>::cvt(ng[rr][j], g[rr][j]);
+        if constexpr (RES) {
+          cy[rr][j] = ny[rr][j];
+          float yv[4];
+          Quad<T>::cvt(ny[rr][j], yv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[rr][j][i] = fmaf(gt[j][i], yv[i], z[rr][j][i]);
+        }
+        ce[rr][j] = ne[rr][j];
       }
+    if (r0 + RB < ch.y) {
+      load_rows<T, G, RB>(nx, x, a.x_stride, r0 + RB, ch.y, col, ok);
+      if constexpr (RES) load_rows<T, G, RB>(ny, y, a.y_stride, r0 + RB, ch.y, col, ok);
+      load_rows<T, G, RB>(ng, dh, a.dh_stride, r0 + RB, ch.y, col, ok);
+      if (has_dz) load_rows<T, G, RB>(ne, dz, a.dz_stride, r0 + RB, ch.y, col, ok);
     }
     if (a.stats) {
 #pragma unroll
@@ -245,7 +284,8 @@ __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwd
     } else {
       row_stats<G, RB>(z, ok, inv_d, a.eps, mean, rstd, red, nb, wave, lane);
     }
-    // z <- z_hat; column sums; g <- dh * (1 + scale); the two row sums.
+    // z <- z_hat; column sums of dh and dh * z_hat; g <- dh * (1 + scale);
+    // the row sums of g and g * z_hat.
     float s[2 * RB];
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
@@ -276,20 +316,18 @@ __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwd
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         if (!ok[j]) continue;
-        float d[4];
+        float d[4], e[4];
+        Quad<T>::cvt(ce[rr][j], e);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = rstd[rr] * (g[rr][j][i] - mg - z[rr][j][i] * mgz);
-        if (dz) {
-          float e[4];
-          Quad<T>::load(dz + (int64_t)row * a.dz_stride + col[j], e);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) d[i] += e[i];
+        for (int i = 0; i < 4; ++i) {
+          d[i] = rstd[rr] * (g[rr][j][i] - mg - z[rr][j][i] * mgz);
+          if (has_dz) d[i] += e[i];
         }
         const int64_t o = (int64_t)row * D + col[j];
         Quad<T>::store(dxo + o, d);
         if constexpr (RES) {
           float yv[4], dyv[4];
-          Quad<T>::load(y + (int64_t)row * a.y_stride + col[j], yv);
+          Quad<T>::cvt(cy[rr][j], yv);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             agt[j][i] = fmaf(d[i], yv[i], agt[j][i]);
