@@ -11,7 +11,8 @@
 // the DiT-style adaLN, which the pages do not print.
 //
 // Work split: one workgroup (4 waves) per plan chunk of <= 32 rows of one
-// (sample, stream) range, so the whole workgroup uses one modulation row.
+// (sample, stream) range in the backward, two (one per half) in the forward,
+// so a workgroup uses one modulation row.
 // Thread t owns the column groups {4g .. 4g+3 : g = t + 256 j}: each load
 // instruction of the workgroup covers one contiguous 2 KB (bf16) or 4 KB
 // (fp32) stretch of a row. Rows are processed RB at a time; the row sums
@@ -29,39 +30,67 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Four consecutive elements as loaded (bf16x4 or float4) and their fp32 values.
+// Token rows are moved with raw buffer instructions over the chunk's rows:
+// loads past the chunk or past D read 0 and stores there are dropped, so no
+// access sits behind a branch and the compiler can count the loads in flight
+// exactly (a wait for one batch leaves the next batch's loads outstanding).
+constexpr uint32_t kNoAccess = 0x80000000u;  // voffset beyond every chunk resource
+
+// Four consecutive elements: raw loaded form and fp32 values.
 template <typename T>
 struct Quad;
 template <>
 struct Quad<bf16> {
   typedef bf16x4 raw;
-  __device__ static raw zero() { return raw{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f}; }
-  __device__ static raw load(const bf16 *p) { return *reinterpret_cast<const raw *>(p); }
+  __device__ static raw load(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+  }
   __device__ static void cvt(raw v, float (&x)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (float)v[i];
   }
-  __device__ static void store(bf16 *p, const float (&x)[4]) {
+  __device__ static void store(rsrc_t r, uint32_t off, const float (&x)[4]) {
     const bf16x2 a = pack2(x[0], x[1]), b = pack2(x[2], x[3]);
     const raw v = {a[0], a[1], b[0], b[1]};
-    *reinterpret_cast<raw *>(p) = v;
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, 0);
   }
 };
 template <>
 struct Quad<float> {
-  typedef float4 raw;
-  __device__ static raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
-  __device__ static raw load(const float *p) { return *reinterpret_cast<const raw *>(p); }
-  __device__ static void cvt(raw v, float (&x)[4]) {
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  typedef f32x4 raw;
+  __device__ static raw load(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
   }
-  __device__ static void store(float *p, const float (&x)[4]) {
-    *reinterpret_cast<raw *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  __device__ static void cvt(raw v, float (&x)[4]) {
+    x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+  }
+  __device__ static void store(rsrc_t r, uint32_t off, const float (&x)[4]) {
+    const f32x4 v = {x[0], x[1], x[2], x[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
   }
 };
 
 __device__ __forceinline__ void zero4(float (&x)[4]) { x[0] = x[1] = x[2] = x[3] = 0.f; }
-__device__ __forceinline__ void ld_mod(const float *p, float (&x)[4]) { Quad<float>::cvt(Quad<float>::load(p), x); }
+__device__ __forceinline__ void ld_mod(const float *p, float (&x)[4]) {
+  const float4 v = *reinterpret_cast<const float4 *>(p);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+
+// One token tensor seen by a chunk: resource over its rows [r_begin, r_end)
+// (row stride `stride` elements, D elements read per row) and the row pitch
+// in bytes.
+template <typename T>
+struct Rows {
+  rsrc_t r;
+  uint32_t pitch;
+  __device__ Rows(const void *base, int64_t stride, int r_begin, int r_end, int D) {
+    const T *b = base ? static_cast<const T *>(base) + (int64_t)r_begin * stride : nullptr;
+    const uint32_t bytes = base ? (uint32_t)(((int64_t)(r_end - r_begin - 1) * stride + D) * sizeof(T)) : 0u;
+    r = make_rsrc(b, bytes);
+    pitch = (uint32_t)(stride * sizeof(T));
+  }
+};
 
 // Sums of v[0 .. NV) over the workgroup; every thread gets the same bits.
 // buf: LDS [NV][4]. Consecutive calls must alternate between two buffers.
@@ -72,22 +101,21 @@ __device__ __forceinline__ void block_sums(float (&v)[NV], float *buf, int wave,
   if (lane == 0)
 #pragma unroll
     for (int i = 0; i < NV; ++i) buf[4 * i + wave] = v[i];
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = (buf[4 * i] + buf[4 * i + 1]) + (buf[4 * i + 2] + buf[4 * i + 3]);
 }
 
-// Raw loads of RB rows of one tensor (rows past the chunk and columns past
-// D give zeros).
+// Raw loads of the RB rows starting at chunk-relative row k0 (zeros past the
+// chunk; coff[j] = this thread's column byte offset, or kNoAccess).
 template <typename T, int G, int RB>
-__device__ __forceinline__ void load_rows(typename Quad<T>::raw (&r)[RB][G], const T *base, int64_t stride,
-                                          int r0, int r1, const int (&col)[G], const bool (&ok)[G]) {
+__device__ __forceinline__ void load_rows(typename Quad<T>::raw (&v)[RB][G], const Rows<T> &t, int k0,
+                                          const uint32_t (&coff)[G]) {
 #pragma unroll
   for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
     for (int j = 0; j < G; ++j)
-      r[rr][j] = (r0 + rr < r1 && ok[j]) ? Quad<T>::load(base + (int64_t)(r0 + rr) * stride + col[j])
-                                         : Quad<T>::zero();
+      v[rr][j] = Quad<T>::load(t.r, coff[j] == kNoAccess ? kNoAccess : (uint32_t)(k0 + rr) * t.pitch + coff[j]);
 }
 
 // Mean and rstd of RB rows held in registers (two fixed-order passes).
@@ -111,12 +139,11 @@ __device__ __forceinline__ void row_stats(const float (&z)[RB][G][4], const bool
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < G; ++j)
-      if (ok[j])
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float c = z[rr][j][i] - mean[rr];
-          s = fmaf(c, c, s);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float c = ok[j] ? z[rr][j][i] - mean[rr] : 0.f;
+        s = fmaf(c, c, s);
+      }
     rstd[rr] = s;
   }
   block_sums<RB>(rstd, red[nb++ & 1], wave, lane);
@@ -125,28 +152,38 @@ __device__ __forceinline__ void row_stats(const float (&z)[RB][G][4], const bool
 }
 
 // Rows are loaded one batch ahead: the loads of batch k+1 are in flight while
-// batch k is reduced and stored.
+// batch k is reduced and stored. Two workgroups share each plan chunk (its
+// first and second half): the forward writes no partial sums, so smaller
+// pieces only add workgroups in flight.
 template <typename T, int G, bool RES>
 __global__ __launch_bounds__(kThreads) void adaln_fwd_kernel(PlanDev p, AdalnFwdArgs a) {
-  constexpr int RB = 4;
+  constexpr int RB = 2;
   typedef typename Quad<T>::raw raw;
   __shared__ float red[2][64];
-  const int4 ch = p.mod_chunks[blockIdx.x];
+  int4 ch = p.mod_chunks[blockIdx.x >> 1];
+  {
+    const int mid = ch.x + (ch.y - ch.x + 1) / 2;
+    if (blockIdx.x & 1) ch.x = mid; else ch.y = mid;
+    if (ch.x >= ch.y) return;  // a one-row chunk has no second half
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int D = a.dim;
+  const int D = a.dim, nrows = ch.y - ch.x;
   const int64_t mrow = (int64_t)ch.z * D;
-  const T *x = static_cast<const T *>(a.x);
-  const T *y = static_cast<const T *>(a.y);
+  const Rows<T> tx(a.x, a.x_stride, ch.x, ch.y, D), ty(a.y, a.y_stride, ch.x, ch.y, D);
+  const Rows<T> tz(a.z, D, ch.x, ch.y, D), th(a.h, D, ch.x, ch.y, D);
+  const rsrc_t tstat = make_rsrc(a.stats ? a.stats + ch.x : nullptr, a.stats ? 8u * (uint32_t)(ch.y - ch.x) : 0u);
   int col[G];
   bool ok[G];
+  uint32_t coff[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     col[j] = 4 * (tid + kThreads * j);
     ok[j] = col[j] < D;
+    coff[j] = ok[j] ? (uint32_t)(col[j] * sizeof(T)) : kNoAccess;
   }
   raw nx[RB][G], ny[RB][G];
-  load_rows<T, G, RB>(nx, x, a.x_stride, ch.x, ch.y, col, ok);
-  if constexpr (RES) load_rows<T, G, RB>(ny, y, a.y_stride, ch.x, ch.y, col, ok);
+  load_rows<T, G, RB>(nx, tx, 0, coff);
+  if constexpr (RES) load_rows<T, G, RB>(ny, ty, 0, coff);
   float sh[G][4], sc[G][4], gt[G][4];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -161,11 +198,9 @@ __global__ __launch_bounds__(kThreads) void adaln_fwd_kernel(PlanDev p, AdalnFwd
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[j][i] += 1.f;
   }
-  T *zo = static_cast<T *>(a.z);
-  T *ho = static_cast<T *>(a.h);
   const float inv_d = 1.f / (float)D;
   int nb = 0;
-  for (int r0 = ch.x; r0 < ch.y; r0 += RB) {
+  for (int k0 = 0; k0 < nrows; k0 += RB) {
     float z[RB][G][4], mean[RB], rstd[RB];
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr)
@@ -179,57 +214,58 @@ __global__ __launch_bounds__(kThreads) void adaln_fwd_kernel(PlanDev p, AdalnFwd
           for (int i = 0; i < 4; ++i) z[rr][j][i] = fmaf(gt[j][i], yv[i], z[rr][j][i]);
         }
       }
-    if (r0 + RB < ch.y) {
-      load_rows<T, G, RB>(nx, x, a.x_stride, r0 + RB, ch.y, col, ok);
-      if constexpr (RES) load_rows<T, G, RB>(ny, y, a.y_stride, r0 + RB, ch.y, col, ok);
-    }
+    load_rows<T, G, RB>(nx, tx, k0 + RB, coff);
+    if constexpr (RES) load_rows<T, G, RB>(ny, ty, k0 + RB, coff);
+    __builtin_amdgcn_sched_barrier(0);  // issue the next batch's loads here, not after the stores
     row_stats<G, RB>(z, ok, inv_d, a.eps, mean, rstd, red, nb, wave, lane);
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
-      const int row = r0 + rr;
-      if (row >= ch.y) break;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        if (!ok[j]) continue;
-        const int64_t o = (int64_t)row * D + col[j];
-        if constexpr (RES) Quad<T>::store(zo + o, z[rr][j]);
+        const uint32_t o = coff[j] == kNoAccess ? kNoAccess : (uint32_t)(k0 + rr) * th.pitch + coff[j];
+        if constexpr (RES) Quad<T>::store(tz.r, o, z[rr][j]);
         float hv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) hv[i] = fmaf((z[rr][j][i] - mean[rr]) * rstd[rr], sc[j][i], sh[j][i]);
-        Quad<T>::store(ho + o, hv);
+        Quad<T>::store(th.r, o, hv);
       }
-      if (a.stats && tid == 0) a.stats[row] = make_float2(mean[rr], rstd[rr]);
+      // thread 0 stores the row's {mean, rstd} (dropped past the chunk, or
+      // everywhere when no statistics are wanted)
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 st = {__float_as_uint(mean[rr]), __float_as_uint(rstd[rr])};
+      __builtin_amdgcn_raw_buffer_store_b64(st, tstat, tid == 0 ? (int)(8 * (k0 + rr)) : (int)kNoAccess, 0, 0);
     }
   }
 }
 
-// Backward, also one batch ahead (x, y, dh and dz of batch k+1 in flight).
+// Backward, also one row ahead (x, y, dh and dz of row k+1 in flight).
 template <typename T, int G, bool RES>
 __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwdArgs a) {
-  constexpr int RB = G <= 2 ? 4 : (G <= 4 ? 2 : 1);
+  constexpr int RB = 1;
   typedef typename Quad<T>::raw raw;
   __shared__ float red[2][64];
   const int4 ch = p.mod_chunks[blockIdx.x];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int D = a.dim;
+  const int D = a.dim, nrows = ch.y - ch.x;
   const int64_t mrow = (int64_t)ch.z * D;
-  const T *x = static_cast<const T *>(a.x);
-  const T *y = static_cast<const T *>(a.y);
-  const T *dh = static_cast<const T *>(a.dh);
-  const T *dz = static_cast<const T *>(a.dz);
-  const bool has_dz = dz != nullptr;
+  const Rows<T> tx(a.x, a.x_stride, ch.x, ch.y, D), ty(a.y, a.y_stride, ch.x, ch.y, D);
+  const Rows<T> tg(a.dh, a.dh_stride, ch.x, ch.y, D), te(a.dz, a.dz_stride, ch.x, ch.y, D);
+  const Rows<T> tdx(a.dx, D, ch.x, ch.y, D), tdy(a.dy, D, ch.x, ch.y, D);
+  const bool has_dz = a.dz != nullptr;
   int col[G];
   bool ok[G];
+  uint32_t coff[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     col[j] = 4 * (tid + kThreads * j);
     ok[j] = col[j] < D;
+    coff[j] = ok[j] ? (uint32_t)(col[j] * sizeof(T)) : kNoAccess;
   }
   raw nx[RB][G], ny[RB][G], ng[RB][G], ne[RB][G];
-  load_rows<T, G, RB>(nx, x, a.x_stride, ch.x, ch.y, col, ok);
-  if constexpr (RES) load_rows<T, G, RB>(ny, y, a.y_stride, ch.x, ch.y, col, ok);
-  load_rows<T, G, RB>(ng, dh, a.dh_stride, ch.x, ch.y, col, ok);
-  if (has_dz) load_rows<T, G, RB>(ne, dz, a.dz_stride, ch.x, ch.y, col, ok);
+  load_rows<T, G, RB>(nx, tx, 0, coff);
+  if constexpr (RES) load_rows<T, G, RB>(ny, ty, 0, coff);
+  load_rows<T, G, RB>(ng, tg, 0, coff);
+  load_rows<T, G, RB>(ne, te, 0, coff);  // all zeros when dz is absent
   float sc[G][4], gt[G][4], ash[G][4], asc[G][4], agt[G][4];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -245,11 +281,9 @@ __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwd
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[j][i] += 1.f;
   }
-  T *dxo = static_cast<T *>(a.dx);
-  T *dyo = static_cast<T *>(a.dy);
   const float inv_d = 1.f / (float)D;
   int nb = 0;
-  for (int r0 = ch.x; r0 < ch.y; r0 += RB) {
+  for (int k0 = 0; k0 < nrows; k0 += RB) {
     raw cy[RB][G], ce[RB][G];
     float z[RB][G][4], g[RB][G][4], mean[RB], rstd[RB];
 #pragma unroll
@@ -267,17 +301,15 @@ __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwd
         }
         ce[rr][j] = ne[rr][j];
       }
-    if (r0 + RB < ch.y) {
-      load_rows<T, G, RB>(nx, x, a.x_stride, r0 + RB, ch.y, col, ok);
-      if constexpr (RES) load_rows<T, G, RB>(ny, y, a.y_stride, r0 + RB, ch.y, col, ok);
-      load_rows<T, G, RB>(ng, dh, a.dh_stride, r0 + RB, ch.y, col, ok);
-      if (has_dz) load_rows<T, G, RB>(ne, dz, a.dz_stride, r0 + RB, ch.y, col, ok);
-    }
+    load_rows<T, G, RB>(nx, tx, k0 + RB, coff);
+    if constexpr (RES) load_rows<T, G, RB>(ny, ty, k0 + RB, coff);
+    load_rows<T, G, RB>(ng, tg, k0 + RB, coff);
+    load_rows<T, G, RB>(ne, te, k0 + RB, coff);
+    __builtin_amdgcn_sched_barrier(0);  // issue the next batch's loads here, not after the stores
     if (a.stats) {
 #pragma unroll
       for (int rr = 0; rr < RB; ++rr) {
-        const int row = r0 + rr < ch.y ? r0 + rr : ch.y - 1;
-        const float2 st = a.stats[row];
+        const float2 st = a.stats[ch.x + min(k0 + rr, nrows - 1)];
         mean[rr] = st.x;
         rstd[rr] = st.y;
       }
@@ -310,21 +342,15 @@ __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwd
     block_sums<2 * RB>(s, red[nb++ & 1], wave, lane);
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
-      const int row = r0 + rr;
-      if (row >= ch.y) break;
       const float mg = s[2 * rr] * inv_d, mgz = s[2 * rr + 1] * inv_d;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        if (!ok[j]) continue;
         float d[4], e[4];
         Quad<T>::cvt(ce[rr][j], e);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          d[i] = rstd[rr] * (g[rr][j][i] - mg - z[rr][j][i] * mgz);
-          if (has_dz) d[i] += e[i];
-        }
-        const int64_t o = (int64_t)row * D + col[j];
-        Quad<T>::store(dxo + o, d);
+        for (int i = 0; i < 4; ++i) d[i] = rstd[rr] * (g[rr][j][i] - mg - z[rr][j][i] * mgz) + e[i];
+        const uint32_t o = coff[j] == kNoAccess ? kNoAccess : (uint32_t)(k0 + rr) * tdx.pitch + coff[j];
+        Quad<T>::store(tdx.r, o, d);
         if constexpr (RES) {
           float yv[4], dyv[4];
           Quad<T>::cvt(cy[rr][j], yv);
@@ -333,18 +359,24 @@ __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwd
             agt[j][i] = fmaf(d[i], yv[i], agt[j][i]);
             dyv[i] = gt[j][i] * d[i];
           }
-          Quad<T>::store(dyo + o, dyv);
+          Quad<T>::store(tdy.r, o, dyv);
         }
       }
     }
   }
+  (void)has_dz;
   float *part = a.partials + (int64_t)blockIdx.x * 3 * D;
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     if (!ok[j]) continue;
-    Quad<float>::store(part + col[j], ash[j]);
-    Quad<float>::store(part + D + col[j], asc[j]);
-    if constexpr (RES) Quad<float>::store(part + 2 * D + col[j], agt[j]);
+    const f32x4 v0 = {ash[j][0], ash[j][1], ash[j][2], ash[j][3]};
+    const f32x4 v1 = {asc[j][0], asc[j][1], asc[j][2], asc[j][3]};
+    *reinterpret_cast<f32x4 *>(part + col[j]) = v0;
+    *reinterpret_cast<f32x4 *>(part + D + col[j]) = v1;
+    if constexpr (RES) {
+      const f32x4 v2 = {agt[j][0], agt[j][1], agt[j][2], agt[j][3]};
+      *reinterpret_cast<f32x4 *>(part + 2 * D + col[j]) = v2;
+    }
   }
 }
 
@@ -380,10 +412,11 @@ int groups_for(int D) {
 
 template <typename T, int G>
 hipError_t fwd_g(const PlanDev &p, const AdalnFwdArgs &a, hipStream_t s) {
+  const dim3 grid(2u * (unsigned)p.num_mod_chunks);
   if (a.y)
-    hipLaunchKernelGGL((adaln_fwd_kernel<T, G, true>), dim3(p.num_mod_chunks), dim3(kThreads), 0, s, p, a);
+    hipLaunchKernelGGL((adaln_fwd_kernel<T, G, true>), grid, dim3(kThreads), 0, s, p, a);
   else
-    hipLaunchKernelGGL((adaln_fwd_kernel<T, G, false>), dim3(p.num_mod_chunks), dim3(kThreads), 0, s, p, a);
+    hipLaunchKernelGGL((adaln_fwd_kernel<T, G, false>), grid, dim3(kThreads), 0, s, p, a);
   return hipGetLastError();
 }
 
