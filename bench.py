@@ -178,6 +178,40 @@ def edit_1024(pam, torch, dev):
             "fwd_bwd_ms": round(t_fb, 4), "fwd_bwd_tflops": round(14 * flop1 / t_fb / 1e9, 1)}
 
 
+def adaln_block(pam, torch, dev, inp, D):
+    """adaLN modulation with the fused gated residual on the timed pack at
+    model width D (= H * d): forward (x, y -> z, h, statistics) and backward
+    (x, y, dh, dz -> dx, dy and the modulation gradients), bf16, inputs drawn
+    on the device. HBM roofline: algorithmic bytes = every token tensor once
+    (forward 8*N*D + 8*N, backward 12*N*D + 8*N) over the event-timed call."""
+    N, S = inp.num_tokens, len(inp.text_len)
+    pack = pam.Pack(inp.text_len, inp.grid_h, inp.grid_w, 24, 128, "bf16", device=dev)
+    g = torch.Generator(device=dev).manual_seed(7)
+    x, y, dh, dz = (torch.randn((N, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(4))
+    shift, scale, gate = (0.3 * torch.randn((S, 2, D), generator=g, device=dev) for _ in range(3))
+    h, z = torch.empty_like(x), torch.empty_like(x)
+    stats = torch.empty((N, 2), dtype=torch.float32, device=dev)
+    dx, dy = torch.empty_like(x), torch.empty_like(x)
+    dsh, dsc, dg = (torch.empty((S, 2, D), device=dev) for _ in range(3))
+    ws = pack.workspace("adaln", D)
+
+    def fwd():
+        pam.mmdit_adaln_fwd(pack.plan, pack.blob_dev, x=x, y=y, x_stride=D, y_stride=D, shift=shift,
+                            scale=scale, gate=gate, model_dim=D, z=z, h=h, stats=stats)
+
+    def bwd():
+        pam.mmdit_adaln_bwd(pack.plan, pack.blob_dev, x=x, y=y, x_stride=D, y_stride=D, scale=scale,
+                            gate=gate, model_dim=D, stats=stats, dh=dh, dz=dz, dh_stride=D,
+                            dz_stride=D, dx=dx, dy=dy, dshift=dsh, dscale=dsc, dgate=dg, workspace=ws)
+    out = {"model_dim": D, "tokens": N}
+    for name, fn, nbytes in (("fwd", fwd, 8 * N * D + 8 * N), ("bwd", bwd, 12 * N * D + 8 * N)):
+        ms = time_passes(torch, [fn], 50)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"us": round(ms * 1e3, 1), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def bucket_padding(pam, torch, dev, inp, H, d):
     """The same samples as dense per-bucket batches: one batch per distinct
     latent grid, every text padded to the longest prompt of the workload's
@@ -337,6 +371,7 @@ def main():
 
     cfg = packed_cfg_1024(pam, torch, dev, H, d)
     edit = edit_1024(pam, torch, dev)
+    adaln = adaln_block(pam, torch, dev, inp, H * d)
     bucket = bucket_padding(pam, torch, dev, inp, H, d)
 
     if args.copy_calibration:
@@ -374,6 +409,7 @@ def main():
         "roofline": roof,
         "packed_cfg_1024": cfg,
         "edit_1024": edit,
+        "adaln_gated_residual": adaln,
         "bucket_padding": bucket,
     }
     if not args.no_cpu_baseline:
