@@ -151,6 +151,8 @@ __device__ __forceinline__ void row_stats(const float (&z)[RB][G][4], const bool
   for (int rr = 0; rr < RB; ++rr) rstd[rr] = rsqrtf(rstd[rr] * inv_d + eps);
 }
 
+}  // namespace
+
 // Rows are loaded one batch ahead: the loads of batch k+1 are in flight while
 // batch k is reduced and stored. Two workgroups share each plan chunk (its
 // first and second half): the forward writes no partial sums, so smaller
@@ -403,6 +405,8 @@ __global__ __launch_bounds__(256) void adaln_reduce_kernel(const int32_t *ranges
   for (; q < c1; ++q) s += src[(int64_t)q * step];
   out[(int64_t)r * D + c] = s;
 }
+
+namespace {
 
 // Column groups per thread: ceil(D / 1024) rounded up to an instantiated size.
 int groups_for(int D) {
