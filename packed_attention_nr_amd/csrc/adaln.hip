@@ -382,28 +382,38 @@ __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwd
   }
 }
 
-// Grid: x = (range, 256-column block), y = which sum (0 dshift, 1 dscale, 2 dgate).
+// Grid: x = (range, 64-column block), y = which sum (0 dshift, 1 dscale,
+// 2 dgate). Wave w adds chunks c0 + w, c0 + w + 4, ... of the range for its
+// block's 64 columns; the four wave sums are then added in wave order. The
+// split depends only on the plan, so the result is the same on every run.
 __global__ __launch_bounds__(256) void adaln_reduce_kernel(const int32_t *ranges, const float *part, int D,
                                                            float *o0, float *o1, float *o2) {
-  const int nxb = (D + 255) / 256;
+  __shared__ float red[4][64];
+  const int nxb = (D + 63) / 64;
   const int r = blockIdx.x / nxb, k = blockIdx.y;
-  const int c = (blockIdx.x % nxb) * 256 + threadIdx.x;
-  if (c >= D) return;
-  float *out = k == 0 ? o0 : (k == 1 ? o1 : o2);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = (blockIdx.x % nxb) * 64 + lane;
   const int c0 = ranges[r], c1 = ranges[r + 1];
-  const float *src = part + (int64_t)k * D + c;
-  const int64_t step = 3 * (int64_t)D;
   float s = 0.f;
-  int q = c0;
-  for (; q + 8 <= c1; q += 8) {  // eight loads in flight, added in chunk order
-    float t[8];
+  if (c < D) {
+    const float *src = part + (int64_t)k * D + c;
+    const int64_t step = 3 * (int64_t)D;
+    int q = c0 + w;
+    for (; q + 28 < c1; q += 32) {  // eight loads in flight, added in chunk order
+      float t[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) t[u] = src[(int64_t)(q + u) * step];
+      for (int u = 0; u < 8; ++u) t[u] = src[(int64_t)(q + 4 * u) * step];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += t[u];
+      for (int u = 0; u < 8; ++u) s += t[u];
+    }
+    for (; q < c1; q += 4) s += src[(int64_t)q * step];
   }
-  for (; q < c1; ++q) s += src[(int64_t)q * step];
-  out[(int64_t)r * D + c] = s;
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && c < D) {
+    float *out = k == 0 ? o0 : (k == 1 ? o1 : o2);
+    out[(int64_t)r * D + c] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+  }
 }
 
 namespace {
@@ -473,7 +483,7 @@ hipError_t launch_adaln_bwd(int dtype, const PlanDev &p, const AdalnBwdArgs &a, 
 
 hipError_t launch_adaln_reduce(const PlanDev &p, const float *partials, int dim, float *out0, float *out1,
                                float *out2, hipStream_t stream) {
-  const dim3 grid((unsigned)((dim + 255) / 256) * 2u * (unsigned)p.num_samples, out2 ? 3 : 2);
+  const dim3 grid((unsigned)((dim + 63) / 64) * 2u * (unsigned)p.num_samples, out2 ? 3 : 2);
   hipLaunchKernelGGL(adaln_reduce_kernel, grid, dim3(256), 0, stream, p.mod_ranges, partials, dim, out0, out1,
                      out2);
   return hipGetLastError();
