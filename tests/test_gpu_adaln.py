@@ -140,6 +140,36 @@ def test_adaln_small_packs(geo, D, dtype):
         _compare(got, _oracle(lay, a, residual, with_dz), residual, dtype, save_stats)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_adaln_strided_views(dtype):
+    """x, y, dh and dz as column slices of wider row-major buffers (a fused
+    projection output): the same bits as contiguous copies."""
+    import packed_attention_nr_amd as pam
+    g = _geometry("edit")
+    lay = _lay(g)
+    S, N, D = len(g["text"]), lay.num_tokens, 1000
+    pack = _pack(g, dtype)
+    a = workloads.draw_adaln(77, N, S, D, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    f32 = lambda k: torch.from_numpy(np.ascontiguousarray(a[k])).cuda()
+    dense = {k: torch.from_numpy(np.ascontiguousarray(a[k])).cuda().to(tdt) for k in ("x", "y", "dh", "dz")}
+    wide = {}
+    for i, k in enumerate(("x", "y", "dh", "dz")):
+        buf = torch.full((N, 3 * D + 4 * (i + 1)), float("nan"), dtype=tdt, device="cuda")
+        buf[:, D:2 * D] = dense[k]
+        wide[k] = buf[:, D:2 * D]
+        assert wide[k].stride(0) != D
+    outs = []
+    for t in (dense, wide):
+        fw = pam.adaln_forward(pack, t["x"], f32("shift"), f32("scale"), y=t["y"], gate=f32("gate"))
+        bw = pam.adaln_backward(pack, t["x"], f32("scale"), t["dh"], y=t["y"], gate=f32("gate"),
+                                dz=t["dz"], stats=fw["stats"])
+        torch.cuda.synchronize()
+        outs.append({k: v.detach().cpu() for k, v in list(fw.items()) + list(bw.items())})
+    bad = [k for k in outs[0] if not torch.equal(outs[0][k], outs[1][k])]
+    assert not bad, bad
+
+
 def test_adaln_samples_alone_bitwise():
     """Each sample's rows and its modulation gradients are bitwise those of
     the sample run as a pack of its own."""
