@@ -57,6 +57,8 @@ EDGE_PACKS = {
     "ragged_multi_tile": dict(text=[45, 3, 130], grids=[(13, 11), (2, 5), (7, 19)]),
     "wide_4to1": dict(text=[20], grids=[(8, 32)]),
     "tile_plus_one": dict(text=[1], grids=[(16, 8)]),
+    "single_token_pack": dict(text=[1], grids=[(0, 0)]),
+    "single_pixel_pack": dict(text=[0], grids=[(1, 1)]),
 }
 
 
@@ -78,6 +80,17 @@ def test_random_packs(seed, dtype):
                                 heads=2, head_dim=128 if seed % 2 else 64, dtype=dtype)
     _say(f"random pack seed={seed} {dtype} d={inp.head_dim} N={inp.num_tokens} "
          f"L={inp.seqlens().tolist()}")
+    _compare(inp, run_gpu(inp), run_oracle(inp))
+
+
+def test_largest_grid_sides():
+    """Grid sides of 32,767 (the largest the packing accepts): a 1 x 32767
+    strip after 5 text tokens and a 32767 x 1 column, so row and column
+    indices reach their 15-bit maximum in the token words and the RoPE table
+    has 32,767 rows. One head, d = 64, bf16, forward and backward."""
+    inp = workloads.random_pack(11, heads=1, head_dim=64, dtype="bf16",
+                                text=[5, 0], grids=[(1, 32767), (32767, 1)])
+    _say(f"largest grid sides N={inp.num_tokens} L={inp.seqlens().tolist()}")
     _compare(inp, run_gpu(inp), run_oracle(inp))
 
 
