@@ -340,6 +340,7 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
         s = mfma32(kf, qf[ks], s);
         dp = mfma32(vf, gf[ks], dp);
       }
+      pipeline_mfma_ds<2 * KS, 0, 0, 1, 4>();
       // Keys past the segment end (last tile only): score -inf, so P = dS = 0.
       if (kb0 + kb * 32 + 32 > seg1) {
 #pragma unroll
@@ -362,6 +363,7 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
         const bf16x8 kt = lds_read_tr(Ks, LDK, t * 16, b * 32, lane);
         dq[b] = mfma32(kt, dsf[t], dq[b]);
       }
+    pipeline_mfma_ds<(BN / 16) * DB, (BN / 16) * DB, 2, 0, 4>();
     if (j + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();
   }
