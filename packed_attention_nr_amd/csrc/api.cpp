@@ -347,6 +347,8 @@ static mmdit_status adaln_bwd(const mmdit_plan *plan, const void *blob, const mm
   const int elt = plan->dtype == MMDIT_BF16 ? 2 : 4;
   const bool res = a->y != nullptr;
   const uint64_t need = (uint64_t)plan->num_mod_chunks * 3 * (uint64_t)D * 4;
+  if ((D + 63) / 64 * 2 * S > INT32_MAX)
+    return fail(MMDIT_ERR_UNSUPPORTED, "too many samples (%lld) for the modulation-gradient sums", (long long)S);
   if (!ws || !aligned16(ws))
     return fail(MMDIT_ERR_INVALID_ARG, "workspace must be a non-NULL 16-byte aligned device pointer");
   if (ws_bytes < need)
