@@ -18,7 +18,12 @@
  *     (transcript at [00:03:16]; aiany.app entry, "Key Capabilities");
  *   - joint text+image self-attention confined to each sample (variable-length
  *     attention over the cumulative offsets; picx.dev, same section), and its
- *     backward for training.
+ *     backward for training;
+ *   - around it: packed classifier-free guidance (mmdit_cfg_pack_desc),
+ *     editing packs with a frame axis of a 3D RoPE (mmdit_pack_plan_edit) and
+ *     the adaptive-LayerNorm modulation with the fused gated residual
+ *     (mmdit_adaln_fwd / mmdit_adaln_bwd), each documented at its
+ *     declaration.
  *
  * Conventions fixed by this library where the pages are silent:
  *   - token order inside a sample: text tokens, then the latent grid row-major;

@@ -32,8 +32,11 @@ constexpr int kThreads = 256;
 
 // Token rows are moved with raw buffer instructions over the chunk's rows:
 // loads past the chunk or past D read 0 and stores there are dropped, so no
-// access sits behind a branch and the compiler can count the loads in flight
-// exactly (a wait for one batch leaves the next batch's loads outstanding).
+// access sits behind a branch. (gfx950 counts loads and stores on one
+// counter, so with the previous batch's stores pending the compiler still
+// waits for every outstanding access at the top of a batch; the next batch's
+// loads overlap the current batch's reductions and stores, and further
+// latency is hidden by the other workgroups on the CU.)
 constexpr uint32_t kNoAccess = 0x80000000u;  // voffset beyond every chunk resource
 
 // Four consecutive elements: raw loaded form and fp32 values.
