@@ -94,6 +94,46 @@ def test_largest_grid_sides():
     _compare(inp, run_gpu(inp), run_oracle(inp))
 
 
+INFER_PACKS = [
+    ("ragged_multi_tile", 128, dict(text=[45, 3, 130], grids=[(13, 11), (2, 5), (7, 19)]), None),
+    ("wide_4to1", 64, dict(text=[20], grids=[(8, 32)]), None),
+    ("edit_mixed", 128, dict(text=[20, 0, 64], grids=[(5, 5), (8, 16), (3, 3)]),
+     [(0, 0), (16, 8), (11, 2)]),
+]
+
+
+@pytest.mark.parametrize("name,d,spec,src", INFER_PACKS, ids=[c[0] for c in INFER_PACKS])
+def test_inference_forward_in_workspace(name, d, spec, src):
+    """A bf16 forward that keeps no Q-hat / K-hat (they live in the caller's
+    workspace): O and lse against the oracle, and bit for bit against the
+    forward that stores them."""
+    import packed_attention_nr_amd as pam
+    inp = workloads.random_pack(31, heads=3, head_dim=d, dtype="bf16", backward=False,
+                                text=spec["text"], grids=spec["grids"], src=src)
+    _say(f"inference forward {name} d={d} N={inp.num_tokens}")
+    pack = pam.Pack(inp.text_len, inp.grid_h, inp.grid_w, inp.heads, inp.head_dim, "bf16",
+                    src_h=inp.src_h, src_w=inp.src_w)
+    up = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    gains = torch.from_numpy(inp.gains).cuda()
+    inf = pam.forward(pack, q, k, v, gains, save_for_backward=False)
+    trn = pam.forward(pack, q, k, v, gains, save_for_backward=True)
+    torch.cuda.synchronize()
+    ref = run_oracle(inp, backward=False)
+    fails = []
+    o = inf["o"].double().cpu().numpy()
+    _, msg = check("o (workspace)", o, ref["o"], "bf16", failures=fails)
+    _say("   " + msg)
+    e = float(np.max(np.abs(inf["lse"].double().cpu().numpy().T - ref["lse"])))
+    _say(f"   lse (workspace): max_abs={e:.3e}")
+    if e > 2e-2:
+        fails.append(f"lse {e:.3e}")
+    for key in ("o", "lse"):
+        if not torch.equal(inf[key], trn[key]):
+            fails.append(f"{key} differs between the workspace and the stored forward")
+    assert not fails, fails
+
+
 def test_tiny_fp32_workload():
     inp = workloads.draw("tiny_fp32")
     _say(f"tiny_fp32 N={inp.num_tokens}")
