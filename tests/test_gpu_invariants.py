@@ -122,3 +122,27 @@ def test_fused_qkv_views_match_dense(dtype):
            "dgains": host(g["dgains"])}
     bad = [k for k in got if not np.array_equal(got[k], dense[k])]
     assert not bad, f"strided views differ from dense inputs: {bad}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_side_stream_matches_default_stream(dtype):
+    """Forward and backward enqueued on a side stream (default priority) give
+    the default stream's bits: every launch goes to the caller's stream."""
+    import packed_attention_nr_amd as pam
+    from parity import to_device
+    inp = _pack(15, dtype)
+    _say(f"side stream {dtype} N={inp.num_tokens}")
+    pack = pam.Pack(inp.text_len, inp.grid_h, inp.grid_w, inp.heads, inp.head_dim, dtype)
+    t = to_device(inp)
+    ref_f = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"])
+    ref_b = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], ref_f, t["dout"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        f = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"])
+        b = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], f, t["dout"])
+    side.synchronize()
+    bad = [k for k in f if not torch.equal(f[k], ref_f[k])]
+    bad += [k for k in ("dq", "dk", "dv", "dgains") if not torch.equal(b[k], ref_b[k])]
+    assert not bad, bad
