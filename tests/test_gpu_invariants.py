@@ -146,3 +146,36 @@ def test_side_stream_matches_default_stream(dtype):
     bad = [k for k in f if not torch.equal(f[k], ref_f[k])]
     bad += [k for k in ("dq", "dk", "dv", "dgains") if not torch.equal(b[k], ref_b[k])]
     assert not bad, bad
+
+
+def test_graph_capture_replays_match_eager():
+    """Forward + backward captured in one HIP graph (the library allocates,
+    clears and synchronises nothing, so its launches are capturable) and
+    replayed three times, with eager work and synchronisation between the
+    replays: every replay gives the eager bits."""
+    import packed_attention_nr_amd as pam
+    from parity import to_device
+    inp = _pack(16, "bf16")
+    _say(f"graph capture N={inp.num_tokens}")
+    pack = pam.Pack(inp.text_len, inp.grid_h, inp.grid_w, inp.heads, inp.head_dim, "bf16")
+    t = to_device(inp)
+    eager_f = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"])
+    eager_b = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], eager_f, t["dout"])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        f = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"])
+        b = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], f, t["dout"])
+    for rep in range(3):
+        for k in ("o", "lse"):  # clobber the outputs so each replay must rewrite them
+            f[k].fill_(float("nan"))
+        for k in ("dq", "dk", "dv", "dgains"):
+            b[k].fill_(float("nan"))
+        noise = torch.randn(1 << 20, device="cuda") * 2.0  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        bad = [k for k in ("o", "lse", "q_hat", "k_hat", "rstd") if not torch.equal(f[k], eager_f[k])]
+        bad += [k for k in ("dq", "dk", "dv", "dgains") if not torch.equal(b[k], eager_b[k])]
+        _say(f"   replay {rep}: {'bitwise equal' if not bad else bad} (noise {float(noise.sum()):.1f})")
+        assert not bad, (rep, bad)
