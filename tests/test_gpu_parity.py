@@ -83,6 +83,16 @@ def test_random_packs(seed, dtype):
     _compare(inp, run_gpu(inp), run_oracle(inp))
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_many_heads(dtype, d):
+    """40 heads (token stride 40*d): head-indexed strides, block maps and the
+    gain-gradient sums over more heads than the workloads use."""
+    inp = workloads.random_pack(17, heads=40, head_dim=d, dtype=dtype,
+                                text=[33, 7], grids=[(9, 10), (4, 4)])
+    _say(f"many heads {dtype} d={d} N={inp.num_tokens}")
+    _compare(inp, run_gpu(inp), run_oracle(inp))
+
+
 def test_largest_grid_sides():
     """Grid sides of 32,767 (the largest the packing accepts): a 1 x 32767
     strip after 5 text tokens and a 32767 x 1 column, so row and column
