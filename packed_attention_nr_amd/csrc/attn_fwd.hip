@@ -26,9 +26,12 @@
 //  * K/V tiles of 64 keys go global -> LDS directly (global_load_lds_dwordx4,
 //    no register staging) into a 4-stage ring of unpadded XOR-swizzled tiles;
 //    only the last tile of a segment is masked;
-//  * online softmax in fp32 in the exp2 domain, with the running reference max
-//    only moved when a new score exceeds it by more than 8 (log2 units), so
-//    the O^T rescale is rare and the result is unchanged.
+//  * online softmax in fp32 in the exp2 domain against a running reference
+//    that moves rarely: each tile's P is formed against the current reference
+//    and kept when the lane's sum of P stays within a bound (then no P can
+//    overflow the accumulators), so the row maxima are formed only on the
+//    first tile and on tiles that pass the bound; the result is the same
+//    softmax whichever reference it was formed against.
 #include <type_traits>
 
 #include "device.h"
@@ -42,6 +45,7 @@ constexpr int BM = 32 * NW;        // queries per workgroup (= kFwdTileBf16)
 constexpr int BN = 64;             // keys per tile
 constexpr int NS = 4;              // stages of the K/V ring
 constexpr float kRescaleThreshold = 8.0f;
+constexpr float kSumLimit = 16384.0f;  // per-lane tile sum of P kept without a rescale
 }  // namespace fwd
 
 static_assert(fwd::BM == kFwdTileBf16, "forward tile must match the plan");
@@ -149,6 +153,23 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
       }
   };
   // Phase B piece (vector ALU): online softmax of tile t's scores -> pf.
+  // exp_pack forms P = exp2(S c2 - m_ref) into pf and returns the lane's sum
+  // of P; the fp32 scores stay in s.
+  auto exp_pack = [&]() __attribute__((always_inline)) -> float {
+    float ts = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      f32x16 e;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        e[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -m_ref));
+        ts = (kb == 0 && i == 0) ? e[i] : ts + e[i];
+      }
+      pf[2 * kb] = acc_to_bf16(e, 0);
+      pf[2 * kb + 1] = acc_to_bf16(e, 8);
+    }
+    return ts;
+  };
   auto softmax = [&](int t) __attribute__((always_inline)) {
     const int kb0 = seg0 + t * BN;
     if (kb0 + BN > seg1) {  // keys past the segment end (last tile only)
@@ -158,33 +179,34 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
         for (int i = 0; i < 16; ++i)
           if (kb0 + kb * 32 + acc_row(i, g) >= seg1) s[kb][i] = -INFINITY;
     }
-    float mx = -INFINITY;
+    // P is formed against the current reference first. A lane sum of at most
+    // kSumLimit bounds each of the lane's P by it, which keeps the fp32
+    // accumulators far from overflow, so the reference can stay. Any other
+    // sum (larger, infinite or NaN; always on the first tile, where m_ref is
+    // -inf) takes the exact online-softmax step: the row maxima, a raised
+    // reference when they pass it by kRescaleThreshold, and P formed again.
+    // Either way the result is the same softmax; only the reference differs.
+    float ts = exp_pack();
+    if (__ballot(!(ts <= kSumLimit))) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = half_max(mx) * c2;
-    if (__ballot(mx > m_ref + kRescaleThreshold)) {
-      const float mn = fmaxf(m_ref, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
-      l_part *= alpha;
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = half_max(mx) * c2;
+      if (__ballot(mx > m_ref + kRescaleThreshold)) {
+        const float mn = fmaxf(m_ref, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+        l_part *= alpha;
 #pragma unroll
-      for (int b = 0; b < DB; ++b)
+        for (int b = 0; b < DB; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
-      m_ref = mn;
-    }
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -m_ref));
-        s[kb][i] = e;
-        l_part += e;
+          for (int i = 0; i < 16; ++i) o[b][i] *= alpha;
+        m_ref = mn;
       }
-      pf[2 * kb] = acc_to_bf16(s[kb], 0);
-      pf[2 * kb + 1] = acc_to_bf16(s[kb], 8);
+      ts = exp_pack();
     }
+    l_part += ts;
   };
 
   // Schedule (every wave passes the same number of barriers; group 1 runs one

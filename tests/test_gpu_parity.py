@@ -1,5 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
 same seeded inputs. Marked ``gpu``: needs an MI355X and the built library."""
+import dataclasses
 import sys
 
 import numpy as np
@@ -102,6 +103,76 @@ def test_largest_grid_sides():
                                 text=[5, 0], grids=[(1, 32767), (32767, 1)])
     _say(f"largest grid sides N={inp.num_tokens} L={inp.seqlens().tolist()}")
     _compare(inp, run_gpu(inp), run_oracle(inp))
+
+
+SCORE_PATTERNS = ("jump", "ramp_up", "gentle", "ramp_down", "random")
+
+
+def _score_pattern_pack(d, seed=5):
+    """Text-only samples (no RoPE) of 401 tokens whose scores follow a chosen
+    course along the keys, in one pack: q and k rows are +-1 vectors and all
+    gains equal g, so Q-hat and K-hat are +-g up to a relative 5e-7 (exactly
+    +-g once rounded to bf16) and every score g^2 (d - 2 f) is exact in fp32,
+    f being the number of sign flips between the query and the key. Per head,
+    every query is a base vector u with 0..3 flips; key j of a sample has f_j
+    flips of u:
+      jump      - the first 64 keys are -u, the rest have 0..6 flips: the later
+                  scores exceed the first tile's by ~150 (log2 units), past
+                  the fp32 range of exp2;
+      ramp_up   - f from d down to 0: the maximum rises by ~26 per 64 keys;
+      gentle    - f from d/2 + a down to d/2 - a: a rise of 5..8 over the
+                  sample, so later keys weigh up to ~2^7 against the first;
+      ramp_down - f from 0 up to d: the first keys hold the maximum;
+      random    - f uniform in 0..d.
+    g = 2.25 (d = 128) or 2.75 (d = 64) makes 1 unit of s_int = d - 2f worth
+    0.65 or 1.36 in log2 units."""
+    T = 401
+    S = len(SCORE_PATTERNS)
+    g = 2.25 if d == 128 else 2.75
+    inp = workloads.random_pack(seed, heads=2, head_dim=d, dtype="bf16", backward=False,
+                                text=[T] * S, grids=[(0, 0)] * S)
+    rng = np.random.default_rng(seed + 1000)
+    H = inp.heads
+    j = np.arange(T)
+    a = 3 if d == 128 else 1
+    flips = {
+        "jump": np.where(j < 64, d, rng.integers(0, 7, T)),
+        "ramp_up": np.rint(d * (1 - j / (T - 1))),
+        "gentle": np.rint(d / 2 + a - 2 * a * j / (T - 1)),
+        "ramp_down": np.rint(d * j / (T - 1)),
+        "random": rng.integers(0, d + 1, T),
+    }
+    q = np.empty_like(inp.q)
+    k = np.empty_like(inp.k)
+
+    def flipped(u, f):
+        x = u.copy()
+        x[rng.permutation(d)[:int(f)]] *= -1
+        return x
+
+    for h in range(H):
+        u = rng.choice([-1.0, 1.0], d).astype(np.float32)
+        for i, name in enumerate(SCORE_PATTERNS):
+            for t in range(T):
+                q[i * T + t, h] = flipped(u, rng.integers(0, 4))
+                k[i * T + t, h] = flipped(u, flips[name][t])
+    gains = np.full_like(inp.gains, g)
+    return dataclasses.replace(inp, q=q, k=k, gains=gains)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_score_patterns(d):
+    """The forward's running reference (P formed against the current one, kept
+    while P stays bounded, the reference raised from the row maxima otherwise)
+    on scores that jump past exp2's range, climb steeply or gently, fall, or
+    scatter: Q-hat, K-hat, O and lse against the oracle. Forward only: with
+    these keys a gradient is the small remainder of hundreds of near-parallel
+    terms, and a key that takes the weight of all 401 queries gets a dV near 20
+    whose bf16 rounding alone passes the absolute bar; the backward reads the
+    forward only through the lse checked here."""
+    inp = _score_pattern_pack(d)
+    _say(f"score patterns d={d} N={inp.num_tokens} {SCORE_PATTERNS}")
+    _compare(inp, run_gpu(inp, backward=False), run_oracle(inp, backward=False), backward=False)
 
 
 INFER_PACKS = [
