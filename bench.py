@@ -5,7 +5,8 @@
 One step = one pass of the whole path over one synthetic pack: the host pack
 plan and its upload, the forward (QK-norm + 2D RoPE prologue, var-len
 attention) and the backward (D = rowsum(dO*O), var-len attention backward
-with the prologue backward fused into its epilogues, gain-gradient reduction).
+with the prologue backward fused into its epilogues, gain-gradient reduction;
+--bwd-mode stored_ds forms dQ from the dS that the dK/dV kernel stores).
 HIP events recorded on the launch stream between the stages give each
 kernel's duration inside the timed region.
 Prints one JSON line.
@@ -243,6 +244,9 @@ def main():
     ap.add_argument("--workload", default="mixed6", choices=["mixed6", "gen2048", "small64"])
     ap.add_argument("--cpu-heads", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd-mode", default="recompute", choices=["recompute", "stored_ds"],
+                    help="backward mode of the timed step (stored_ds: dQ from the dS the "
+                         "dK/dV kernel writes; needs ~2*H*sum(L^2) bytes of workspace)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -275,16 +279,29 @@ def main():
     dgains = torch.empty((4, d), dtype=torch.float32, device=dev)
 
     plan0, blob0 = pam.mmdit_pack_plan(inp.text_len, inp.grid_h, inp.grid_w, H, d, pam.MMDIT_BF16)
-    ws = torch.empty(int(plan0.bwd_workspace_bytes), dtype=torch.uint8, device=dev)
+    # The backward in its recompute mode (dQ with D, then dK/dV) or, with
+    # --bwd-mode stored_ds, in its stored-dS mode (D, then dK/dV writing dS,
+    # then dQ from dS); each stage is its own call so that events separate them.
+    B = pam.BWD_STAGES
+    ds_mode = args.bwd_mode == "stored_ds"
+    if ds_mode and not plan0.bwd_ds_workspace_bytes > plan0.bwd_workspace_bytes:
+        raise SystemExit("this pack has no stored-dS backward")
+    if ds_mode:
+        bcalls = [("bwd_d", B["d"] | B["store_ds"]), ("attn_bwd_dkdv", B["dkdv"] | B["store_ds"]),
+                  ("attn_bwd_dq", B["dq"] | B["store_ds"]), ("gain_reduce", B["gains"])]
+    else:
+        bcalls = [("attn_bwd_dq", B["dq"]), ("attn_bwd_dkdv", B["dkdv"]), ("gain_reduce", B["gains"])]
+    names = ["prologue_fwd", "attn_fwd"] + [n for n, _ in bcalls]
+    ws_bytes = plan0.bwd_ds_workspace_bytes if ds_mode else plan0.bwd_workspace_bytes
+    ws = torch.empty(int(ws_bytes), dtype=torch.uint8, device=dev)
     blob_dev = [torch.empty(int(plan0.blob_bytes), dtype=torch.uint8, device=dev) for _ in range(2)]
     pinned = [torch.empty(int(plan0.blob_bytes), dtype=torch.uint8).pin_memory() for _ in range(2)]
     copied = [torch.cuda.Event() for _ in range(2)]
     for e in copied:
         e.record()
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     S = pam.FWD_STAGES
-    B = pam.BWD_STAGES
 
     def step(i, evs=None):
         # a1: host plan + upload of its blob (pinned ring of two buffers)
@@ -306,12 +323,9 @@ def main():
         ba = dict(q=q, k=k, v=v, q_hat=q_hat, k_hat=k_hat, o=o, dout=do, q_stride=H * d,
                   k_stride=H * d, v_stride=H * d, dout_stride=H * d, gains=gains, lse=lse,
                   rstd=rstd, dq=dq, dk=dk, dv=dv, dgains=dgains, workspace=ws)
-        pam.mmdit_attn_bwd(plan, bd, stages=B["dq"], **ba)
-        rec(3)
-        pam.mmdit_attn_bwd(plan, bd, stages=B["dkdv"], **ba)
-        rec(4)
-        pam.mmdit_attn_bwd(plan, bd, stages=B["gains"], **ba)
-        rec(5)
+        for j, (_, st) in enumerate(bcalls):
+            pam.mmdit_attn_bwd(plan, bd, stages=st, **ba)
+            rec(3 + j)
 
     for i in range(args.warmup):
         step(i)
@@ -323,18 +337,20 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
-    names = ["prologue_fwd", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv", "gain_reduce"]
     kt = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
           for j, n in enumerate(names)}
     value = (fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12
-    t_bwd = kt["attn_bwd_dq"] + kt["attn_bwd_dkdv"]
+    t_bwd = kt["attn_bwd_dq"] + kt["attn_bwd_dkdv"] + kt.get("bwd_d", 0.0)
     bwd_tflops = bwd_flop / (t_bwd * 1e-3) / 1e12
     fwd_tflops = fwd_flop / (kt["attn_fwd"] * 1e-3) / 1e12
     # Dominant kernel's roofline. Algorithmic FLOPs per launch: the dK/dV kernel
     # performs 4 of the backward's 5 products (S, dP, dV, dK: 8*H*d*sum L^2);
-    # the dQ kernel adds only dQ (2*H*d*sum L^2) -- its S and dP are recomputed.
-    cand = {"attn_bwd_dkdv": (8.0 * H * d * sl2, "attn_bwd_dkdv_kernel<128>"),
-            "attn_bwd_dq": (2.0 * H * d * sl2, "attn_bwd_dq_kernel<128>"),
+    # the dQ kernel adds only dQ (2*H*d*sum L^2), from the stored dS or with
+    # S and dP recomputed.
+    dkdv_name = "attn_bwd_dkdv_kernel<128, true>" if ds_mode else "attn_bwd_dkdv_kernel<128, false>"
+    dq_name = "attn_bwd_dq_ds_kernel<128>" if ds_mode else "attn_bwd_dq_kernel<128>"
+    cand = {"attn_bwd_dkdv": (8.0 * H * d * sl2, dkdv_name),
+            "attn_bwd_dq": (2.0 * H * d * sl2, dq_name),
             "attn_fwd": (fwd_flop, "attn_fwd_bf16_kernel<128>")}
     dom = max(cand, key=lambda n: kt[n])
     ach = cand[dom][0] / (kt[dom] * 1e-3) / 1e12
@@ -398,6 +414,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {n: round(t, 4) for n, t in kt.items()},
+        "bwd_mode": "stored_ds" if ds_mode else "recompute",
         "attn_fwd_tflops": round(fwd_tflops, 2),
         "attn_fwd_frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
         "attn_bwd_tflops": round(bwd_tflops, 2),

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MMDIT_ABI_VERSION 3
+#define MMDIT_ABI_VERSION 4
 
 /* Largest accepted token stride, in elements (2^24). */
 #define MMDIT_MAX_ROW_STRIDE (1ll << 24)
@@ -116,6 +116,9 @@ typedef struct {
  *               each (sample, stream) token range (stream 0 = text, 1 = image)
  *               cut into pieces of at most mod_chunk_rows rows, ranges in order
  *   mod_ranges  int32 [2S+1]: chunks of range r are [mod_ranges[r], mod_ranges[r+1])
+ *   ds_base     int64 [S+1]: first 1 KiB block of sample s's dS area (all heads) in
+ *               the backward's dS store; sample s with L = seg_end - seg_start
+ *               tokens has ceil(L/32) * 4 * ceil(L/64) blocks per head
  *   rope        fp32  [rope_rows][d/2][2] = {cos, sin}(pos * omega_p) for
  *               each of the d/2 pairs p (the frequency of its section, see
  *               the RoPE conventions above), computed in double precision and
@@ -135,6 +138,11 @@ typedef struct {
   int32_t num_mod_chunks;        /* adaLN workgroups; mmdit_adaln_bwd needs a workspace of
                                     num_mod_chunks * 3 * model_dim * 4 bytes */
   int32_t mod_chunk_rows;        /* rows per adaLN chunk (32) */
+  uint64_t off_ds_base;
+  uint64_t bwd_ds_workspace_bytes; /* a workspace this large lets mmdit_attn_bwd (all of stages
+                                      DQ and DKDV in one call, bf16) store dS and form dQ from it;
+                                      equals bwd_workspace_bytes where that path does not apply
+                                      (fp32 plans, samples over 32,768 tokens) */
   uint64_t fingerprint;          /* hash of every field above; checked on each call */
 } mmdit_plan;
 
@@ -190,6 +198,8 @@ mmdit_status mmdit_cfg_pack_desc(const mmdit_pack_desc *cond, int32_t null_text_
 #define MMDIT_STAGE_BWD_DKDV      2u  /* bwd: dK-hat and dV (reads D), inverse RoPE + RMSNorm
                                          backward -> dk, dv, K gain partials (workspace) */
 #define MMDIT_STAGE_BWD_GAINS     4u  /* bwd: fixed-order sum of the gain partials -> dgains */
+#define MMDIT_STAGE_BWD_D         8u  /* bwd, stored-dS mode only: D = rowsum(dO * O) */
+#define MMDIT_STAGE_BWD_STORE_DS 16u  /* bwd mode flag: the stored-dS backward (see mmdit_attn_bwd) */
 
 typedef struct {
   const void *q, *k, *v;              /* [N][H][d] device, dtype; pre-norm */
@@ -229,11 +239,27 @@ typedef struct {
  * plan->bwd_workspace_bytes. Workspace layout (fp32, each part 256-byte
  * aligned): D [H][N] at offset 0, then the Q and K gain-gradient partials;
  * fp32 plans also keep fp32 dQ-hat and dK-hat [N][H][d] after them. A stage
- * subset may run per call: DQ before DKDV (which reads D), both before GAINS
- * (which reads their partials) on the same workspace. Stage DQ needs o, q,
- * dq; DKDV needs k, dk, dv; both need q_hat, k_hat, v, dout, lse, gains.
- * Deterministic: the same inputs give bitwise the same outputs (no atomics;
- * fixed-order reductions). */
+ * subset may run per call, in the order given below for the mode, on the
+ * same workspace. Stage D needs o and dout; DQ needs q, dq (and o in the
+ * recompute mode); DKDV needs k, dk, dv; both need q_hat, k_hat, v, dout,
+ * lse, gains.
+ * dQ is formed one of two ways, with equal results up to rounding order:
+ *  - recompute: the DQ stage forms D, then S and dP again for each query
+ *    tile, and dQ; stages in the order DQ, DKDV, GAINS;
+ *  - stored dS (bf16 plans with bwd_ds_workspace_bytes > bwd_workspace_bytes,
+ *    workspace_bytes >= plan->bwd_ds_workspace_bytes): stage D forms D, the
+ *    DKDV stage also writes dS (bf16, 2 bytes per score of every sample and
+ *    head) to the workspace past bwd_workspace_bytes (rounded up to 4 KiB),
+ *    and the DQ stage multiplies it by K-hat; stages in the order D, DKDV,
+ *    DQ, GAINS. Faster; the area takes ds_base[S] KiB, about
+ *    2 * H * sum(L_i^2) bytes.
+ * stages = 0 runs everything, in the stored-dS mode when the workspace is
+ * large enough. Stage subsets select the stored-dS mode with
+ * MMDIT_STAGE_BWD_STORE_DS in each call (UNSUPPORTED where the plan has no
+ * such mode, BUFFER_TOO_SMALL without the room); stage D is only valid in
+ * that mode.
+ * Deterministic: the same inputs and the same workspace size give bitwise
+ * the same outputs (no atomics; fixed-order reductions). */
 mmdit_status mmdit_attn_bwd(const mmdit_plan *plan, const void *plan_blob_dev,
                             const mmdit_bwd_args *args, void *workspace,
                             uint64_t workspace_bytes, void *hip_stream);

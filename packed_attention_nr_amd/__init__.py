@@ -25,14 +25,15 @@ __all__ = [
     "forward", "backward", "FWD_STAGES", "BWD_STAGES", "LIB_PATH",
 ]
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmmdit.so")
 
 MMDIT_F32, MMDIT_BF16 = 0, 1
 STAGE_PROLOGUE, STAGE_ATTENTION = 1, 2
-STAGE_BWD_DQ, STAGE_BWD_DKDV, STAGE_BWD_GAINS = 1, 2, 4
+STAGE_BWD_DQ, STAGE_BWD_DKDV, STAGE_BWD_GAINS, STAGE_BWD_D, STAGE_BWD_STORE_DS = 1, 2, 4, 8, 16
 FWD_STAGES = {"prologue": STAGE_PROLOGUE, "attention": STAGE_ATTENTION}
-BWD_STAGES = {"dq": STAGE_BWD_DQ, "dkdv": STAGE_BWD_DKDV, "gains": STAGE_BWD_GAINS}
+BWD_STAGES = {"dq": STAGE_BWD_DQ, "dkdv": STAGE_BWD_DKDV, "gains": STAGE_BWD_GAINS,
+              "d": STAGE_BWD_D, "store_ds": STAGE_BWD_STORE_DS}
 
 
 class PackDesc(C.Structure):
@@ -40,6 +41,10 @@ class PackDesc(C.Structure):
                 ("grid_h", C.POINTER(C.c_int32)), ("grid_w", C.POINTER(C.c_int32)),
                 ("num_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32),
                 ("rope_theta", C.c_float), ("rms_eps", C.c_float), ("token_budget", C.c_int64)]
+
+
+# Largest workspace Pack.workspace("bwd") takes for the stored-dS backward.
+DS_WORKSPACE_LIMIT = 16 << 30
 
 
 class Plan(C.Structure):
@@ -51,7 +56,8 @@ class Plan(C.Structure):
         "blob_bytes", "off_cu_seqlens", "off_tok_meta", "off_fwd_items", "off_bwd_items",
         "off_rope", "off_fwd_blocks", "off_bwd_blocks", "fwd_workspace_bytes",
         "bwd_workspace_bytes", "off_mod_chunks", "off_mod_ranges")] + [
-        ("num_mod_chunks", C.c_int32), ("mod_chunk_rows", C.c_int32), ("fingerprint", C.c_uint64)]
+        ("num_mod_chunks", C.c_int32), ("mod_chunk_rows", C.c_int32), ("off_ds_base", C.c_uint64),
+        ("bwd_ds_workspace_bytes", C.c_uint64), ("fingerprint", C.c_uint64)]
 
 
 class FwdArgs(C.Structure):
@@ -331,14 +337,26 @@ class Pack:
         self.device = device
         self.torch_dtype = _torch_dtype(self.dtype_code)
 
-    def workspace(self, kind: str, model_dim: int = 0):
+    def workspace(self, kind: str, model_dim: int = 0, ds_limit: int = DS_WORKSPACE_LIMIT):
         """Workspace of the attention forward ("fwd"), backward ("bwd") or
-        the adaLN backward ("adaln", for model width model_dim)."""
+        the adaLN backward ("adaln", for model width model_dim). "bwd" (and
+        "bwd_recompute") is the workspace with which the backward forms S and
+        dP again for dQ; "bwd_ds" is large enough for it to store dS and form
+        dQ from it (bf16 plans that offer that mode), when that needs at most
+        ds_limit bytes."""
         import torch
         if kind == "adaln":
             n = self.plan.num_mod_chunks * 3 * int(model_dim) * 4
+        elif kind == "fwd":
+            n = self.plan.fwd_workspace_bytes
+        elif kind in ("bwd", "bwd_recompute"):
+            n = self.plan.bwd_workspace_bytes
+        elif kind == "bwd_ds":
+            n = self.plan.bwd_ds_workspace_bytes
+            if n > ds_limit:
+                raise ValueError(f"the stored-dS workspace needs {n} bytes, over ds_limit={ds_limit}")
         else:
-            n = self.plan.fwd_workspace_bytes if kind == "fwd" else self.plan.bwd_workspace_bytes
+            raise ValueError(f"unknown workspace kind {kind!r}")
         return torch.empty(max(int(n), 16), dtype=torch.uint8, device=self.device)
 
 

@@ -102,6 +102,7 @@ static PlanDev plan_dev(const mmdit_plan &p, const void *blob) {
   d.mod_ranges = reinterpret_cast<const int32_t *>(b + p.off_mod_ranges);
   d.num_mod_chunks = p.num_mod_chunks;
   d.rms_eps = p.rms_eps;
+  d.ds_base = reinterpret_cast<const int64_t *>(b + p.off_ds_base);
   return d;
 }
 
@@ -187,10 +188,8 @@ static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmd
   if (st) return st;
   if (!a) return fail(MMDIT_ERR_INVALID_ARG, "args must not be NULL");
   const uint32_t all = MMDIT_STAGE_BWD_DQ | MMDIT_STAGE_BWD_DKDV | MMDIT_STAGE_BWD_GAINS;
-  const uint32_t stages = a->stages ? a->stages : all;
-  if (stages & ~all) return fail(MMDIT_ERR_INVALID_ARG, "unknown backward stage bits 0x%x", stages);
-  const bool sdq = stages & MMDIT_STAGE_BWD_DQ, skv = stages & MMDIT_STAGE_BWD_DKDV,
-             sgn = stages & MMDIT_STAGE_BWD_GAINS;
+  const uint32_t known = all | MMDIT_STAGE_BWD_D | MMDIT_STAGE_BWD_STORE_DS;
+  if (a->stages & ~known) return fail(MMDIT_ERR_INVALID_ARG, "unknown backward stage bits 0x%x", a->stages);
   const int64_t N = plan->total_tokens, H = plan->num_heads, d = plan->head_dim, HD = H * d;
   const bool f32 = plan->dtype == MMDIT_F32;
   const int elt = f32 ? 4 : 2;
@@ -200,6 +199,25 @@ static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmd
     return fail(MMDIT_ERR_BUFFER_TOO_SMALL, "backward workspace needs %llu bytes, got %llu",
                 (unsigned long long)plan->bwd_workspace_bytes, (unsigned long long)ws_bytes);
   const BwdLayout wl = bwd_layout(*plan);
+  const bool has_ds = wl.ds_total > wl.total;  // the plan offers the stored-dS mode
+  uint32_t stages = a->stages;
+  bool store_ds;
+  if (!stages) {  // everything; stored dS when the workspace has room for it
+    store_ds = has_ds && ws_bytes >= wl.ds_total;
+    stages = all | (store_ds ? MMDIT_STAGE_BWD_D : 0u);
+  } else {
+    store_ds = stages & MMDIT_STAGE_BWD_STORE_DS;
+    if (store_ds && !has_ds)
+      return fail(MMDIT_ERR_UNSUPPORTED, "this plan has no stored-dS backward (fp32, or a sample over %d tokens)",
+                  kDsMaxSeqlen);
+    if (store_ds && ws_bytes < wl.ds_total)
+      return fail(MMDIT_ERR_BUFFER_TOO_SMALL, "stored-dS backward workspace needs %llu bytes, got %llu",
+                  (unsigned long long)wl.ds_total, (unsigned long long)ws_bytes);
+    if ((stages & MMDIT_STAGE_BWD_D) && !store_ds)
+      return fail(MMDIT_ERR_INVALID_ARG, "stage D belongs to the stored-dS backward (the DQ stage forms D otherwise)");
+  }
+  const bool sd = stages & MMDIT_STAGE_BWD_D, sdq = stages & MMDIT_STAGE_BWD_DQ,
+             skv = stages & MMDIT_STAGE_BWD_DKDV, sgn = stages & MMDIT_STAGE_BWD_GAINS;
   char *w = static_cast<char *>(ws);
   float *delta = reinterpret_cast<float *>(w + wl.delta);
   float *part_q = reinterpret_cast<float *>(w + wl.part_q);
@@ -209,10 +227,15 @@ static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmd
 
   std::vector<Span> spans;
   spans.push_back(Span{"workspace", reinterpret_cast<uintptr_t>(ws),
-                       reinterpret_cast<uintptr_t>(ws) + plan->bwd_workspace_bytes, true});
-  if (sdq) {
+                       reinterpret_cast<uintptr_t>(ws) + (store_ds ? wl.ds_total : plan->bwd_workspace_bytes),
+                       true});
+  if ((sdq && !store_ds) || sd) {
     if ((st = check_ptr("o", a->o))) return st;
     spans.push_back(span("o", a->o, N, HD, HD, elt, false));
+  }
+  if (sd && !(sdq || skv)) {
+    if ((st = check_tensor("dout", a->dout, a->dout_stride, HD))) return st;
+    spans.push_back(span("dout", a->dout, N, a->dout_stride, HD, elt, false));
   }
   if (sdq || skv) {
     if ((st = check_ptr("q_hat", a->q_hat)) || (st = check_ptr("k_hat", a->k_hat)) ||
@@ -256,17 +279,27 @@ static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmd
   AttnBwdArgs ba{a->q_hat, a->k_hat, a->v, a->dout, a->o, a->v_stride, a->dout_stride, a->lse,
                  delta, dq_acc, dk_acc, a->dv, (float)(1.4426950408889634 / std::sqrt((double)d)),
                  scale, a->q, a->k, a->q_stride, a->k_stride, a->gains, a->rstd, a->dq, a->dk,
-                 part_q, part_k};
-  if (sdq) {
-    hipError_t e = launch_attn_bwd(plan->dtype, pd, ba, 0, s);
+                 part_q, part_k, store_ds ? static_cast<void *>(w + wl.ds) : nullptr};
+  if (store_ds) {  // D, then dK/dV writing dS, then dQ from dS
+    hipError_t e = hipSuccess;
+    if (sd) {
+      const BwdPreArgs pre{a->o, a->dout, a->dout_stride, delta, nullptr};
+      e = launch_bwd_pre(plan->dtype, pd, pre, s);
+    }
+    if (e == hipSuccess && skv) e = launch_attn_bwd(plan->dtype, pd, ba, kBwdDkdv, s);
+    if (e == hipSuccess && sdq) e = launch_attn_bwd(plan->dtype, pd, ba, kBwdDq, s);
+    if (e != hipSuccess) return hip_fail("attention backward (stored dS)", e);
+  }
+  if (sdq && !store_ds) {
+    hipError_t e = launch_attn_bwd(plan->dtype, pd, ba, kBwdDq, s);
     if (e == hipSuccess && f32) {
       const PrologueBwdArgs pa{a->q, a->q_stride, a->gains, a->rstd, dq_acc, a->dq, part_q, 0, wl.nq};
       e = launch_prologue_bwd(plan->dtype, pd, pa, s);
     }
     if (e != hipSuccess) return hip_fail("attention backward (dQ)", e);
   }
-  if (skv) {
-    hipError_t e = launch_attn_bwd(plan->dtype, pd, ba, 1, s);
+  if (skv && !store_ds) {
+    hipError_t e = launch_attn_bwd(plan->dtype, pd, ba, kBwdDkdv, s);
     if (e == hipSuccess && f32) {
       const PrologueBwdArgs pa{a->k, a->k_stride, a->gains, a->rstd, dk_acc, a->dk, part_k, 1, wl.nk};
       e = launch_prologue_bwd(plan->dtype, pd, pa, s);

@@ -23,12 +23,19 @@
 //    from a ring of LDS tiles filled by direct global->LDS loads.
 // dQ is recomputed rather than accumulated across key tiles: device-wide
 // fp32 atomics from eight XCDs cost far more than the extra S and dP products.
+// Where the caller gives room for it, the dK/dV kernel instead writes dS
+// (bf16, in its register order) and a third kernel forms dQ^T = K^T dS^T by
+// streaming it, which costs 2 bytes of HBM traffic per score instead of the
+// S and dP products (D then comes first, from the backward preprocess).
 #include <type_traits>
 
 #include "device.h"
 #include "internal.h"
 
 namespace mmdit {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 
 namespace bwd {
 constexpr int NWQ = 8;    // waves of a dQ workgroup
@@ -380,6 +387,173 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
 }
 
 // ---------------------------------------------------------------------------
+// dQ-hat from the stored dS for one 256-query tile of one sample and head:
+// dQ^T += K^T dS^T over the sample's keys, 64 per tile. Each wave owns 32
+// queries (two 16-query slices of the stored blocks). Per tile, K-hat (shared
+// by the 8 waves) and each wave's own 4 KiB of dS arrive by direct
+// global->LDS loads into a 3-stage ring; both MFMA operands are read
+// transposed (ds_read_b64_tr_b16): K^T with one d per lane, dS^T with one
+// query per lane. A stored 16-byte piece of dS is lane (g, key) of the
+// writer: queries acc_row(0..7, g) of its slice, i.e. four consecutive
+// queries in each half, so each 8-byte half is one row piece of a
+// transposed read. The epilogue is the dQ kernel's.
+// ---------------------------------------------------------------------------
+namespace bwd {
+constexpr int DQS_TK = 64;                             // keys per tile
+constexpr int DQS_NS = 3;                              // ring stages
+constexpr int DQS_BLK = kDsBlockBytes + 128;           // LDS bytes per stored block
+constexpr int DQS_WAVE = 4 * DQS_BLK;                  // a wave's dS of one tile
+// Cache policy of the dS stream (written once, read once): non-temporal
+// (aux bit 1), which keeps the K/V/Q tiles that other workgroups re-read in
+// L2; measured ~3% faster in the dK/dV kernel than the default policy.
+constexpr int kDsCachePolicy = 2;
+}  // namespace bwd
+
+// dS^T fragment (B operand) of keys 16 t .. 16 t + 15 of the wave's tile
+// from its four LDS blocks [key half kb][query slice u] at sw + (2 kb + u) *
+// DQS_BLK: lane (G, i) supplies row 4 g + i/4 (and + 8), queries 4 (i % 4)..+3
+// of slice u = G % 2, and ends up holding query 16 u + i.
+__device__ __forceinline__ bf16x8 ds_frag(const char *sw, int t, int lane) {
+  using namespace bwd;
+  const int G = lane >> 4, i = lane & 15;
+  const int g = G >> 1, u = G & 1;
+  const int r = 16 * t + 4 * g + (i >> 2);  // key within the 64-key tile
+  const int c4 = i & 3;
+  const char *p0 = sw + (2 * (r >> 5) + u) * DQS_BLK + (2 * (r & 31) + (c4 & 1)) * 16 + (c4 >> 1) * 8;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0 + 2 * 8 * 16));
+  bf16x8 out;
+  out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
+  out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
+  return out;
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_ds_kernel(PlanDev p, AttnBwdArgs a) {
+  using namespace bwd;
+  constexpr int DB = D / 32;
+  constexpr int TK = DQS_TK;
+  using KL = TileLoader<D, SWZ_TRANS, TK, NWQ>;
+  constexpr int PER_TILE = KL::LOADS + 4;  // loads per wave per tile
+  // One LDS object per ring stage and operand (compile-time stage indices
+  // let the compiler see that loads into one stage never alias reads of
+  // another).
+  __shared__ __attribute__((aligned(16))) bf16 k0s[TK * D], k1s[TK * D], k2s[TK * D];
+  __shared__ __attribute__((aligned(16))) char s0s[NWQ * DQS_WAVE], s1s[NWQ * DQS_WAVE], s2s[NWQ * DQS_WAVE];
+  __shared__ __attribute__((aligned(16))) float g_s[2 * D];  // Q gains: text, image
+  static_assert(NWQ * 2 * D * 4 <= NWQ * DQS_WAVE, "gain partials fit a ring stage");
+  auto kst = [&](auto stage) __attribute__((always_inline)) -> bf16 * {
+    constexpr int S = decltype(stage)::value;
+    if constexpr (S == 0) return k0s; else if constexpr (S == 1) return k1s; else return k2s;
+  };
+  auto sst = [&](auto stage) __attribute__((always_inline)) -> char * {
+    constexpr int S = decltype(stage)::value;
+    if constexpr (S == 0) return s0s; else if constexpr (S == 1) return s1s; else return s2s;
+  };
+
+  const int H = p.num_heads;
+  const int2 wb = p.fwd_blocks[blockIdx.x];
+  float *part = a.part_q + (int64_t)blockIdx.x * 2 * D;
+  if (wb.x < 0) {  // idle slot of the block map (whole workgroup): empty partials
+    if (threadIdx.x < 2 * D) part[threadIdx.x] = 0.f;
+    return;
+  }
+  const int h = wb.y;
+  const int4 it = p.fwd_items[wb.x];
+  const int seg0 = it.x, seg1 = it.y, q0 = it.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31;
+  const int64_t HD = (int64_t)H * D;
+
+  const int qi = q0 + wave * 32 + lq;
+  const int qc = min(qi, seg1 - 1);
+  if (tid < 2 * D) g_s[tid] = a.gains[tid];
+  const int32_t meta = p.tok_meta[qc];
+  const float rho0 = a.rstd ? a.rstd[(int64_t)qc * H + h] : -1.f;
+
+  // This sample and head's dS area; blocks past it (keys past the segment
+  // end in the last tile) read as zeros, and slices past the last query tile
+  // only feed queries past the segment end, whose rows are dropped.
+  const int L = seg1 - seg0;
+  const int nq16 = 4 * ((L + BMQ - 1) / BMQ);
+  const int64_t blocks = (int64_t)((L + 31) / 32) * nq16;
+  const rsrc_t ds_rs = make_rsrc(static_cast<const char *>(a.ds) + (p.ds_base[it.w] + h * blocks) * kDsBlockBytes,
+                                 (uint32_t)(blocks * kDsBlockBytes));
+  const int u0 = (q0 - seg0) / 16 + 2 * wave;  // the wave's first query slice
+  KL kload;
+  kload.init(wave, lane, HD);
+  const bf16 *kh = static_cast<const bf16 *>(a.k_hat) + h * D;
+  const int ntiles = (L + TK - 1) / TK;
+  // Tile j: K-hat rows seg0 + 64 j .. (rows past the segment end land as
+  // zeros) and this wave's blocks (2 j + kb, u0 + u), kb, u in {0, 1}.
+  auto issue = [&](auto stage, int j) __attribute__((always_inline)) {
+    if (j >= ntiles) return;
+    kload.issue(kst(stage), kh, seg0 + j * TK, seg1 - 1);
+    char *sw = sst(stage) + wave * DQS_WAVE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t blk = (uint32_t)((2 * j + kb) * nq16 + u0 + u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ds_rs, (__attribute__((address_space(3))) void *)(sw + (2 * kb + u) * DQS_BLK),
+                                                 16, blk * kDsBlockBytes + 16u * lane, 0, 0, kDsCachePolicy);
+      }
+  };
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[b][i] = 0.f;
+
+  // Tile j+2 reuses the stage of tile j-1, which every wave finished reading
+  // before the barrier of step j; each wave waits for its own loads of tile
+  // j before that barrier.
+  auto step = [&](auto stage, int j) __attribute__((always_inline)) {
+    constexpr int SG = decltype(stage)::value;
+    if (j + 1 < ntiles) wait_vmem_le<PER_TILE>();
+    else wait_vmem();
+    lds_barrier();
+    issue(std::integral_constant<int, (SG + 2) % DQS_NS>{}, j + 2);
+    const bf16 *Ks = kst(stage);
+    const char *sw = sst(stage) + wave * DQS_WAVE;
+    bf16x8 bfr[TK / 16];
+#pragma unroll
+    for (int t = 0; t < TK / 16; ++t) bfr[t] = ds_frag(sw, t, lane);
+#pragma unroll
+    for (int t = 0; t < TK / 16; ++t)
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+        dq[b] = mfma32(lds_read_tr_swz<D, SWZ_TRANS>(Ks, t * 16, b * 32, lane), bfr[t], dq[b]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TK / 16), 0);  // the dS fragments first
+    pipeline_mfma_ds<(TK / 16) * DB, 0, 0, 2, 4>();
+  };
+  issue(std::integral_constant<int, 0>{}, 0);
+  issue(std::integral_constant<int, 1>{}, 1);
+  for (int j = 0; j < ntiles; j += DQS_NS) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 >= ntiles) break;
+    step(std::integral_constant<int, 1>{}, j + 1);
+    if (j + 2 >= ntiles) break;
+    step(std::integral_constant<int, 2>{}, j + 2);
+  }
+  wait_vmem();  // no load into LDS may outlive the workgroup
+  __syncthreads();  // the ring is free: stage 0 holds the waves' gain partials
+
+  // dQ-hat row of this lane's query -> dq, and the block's Q gain partials.
+  float *red = reinterpret_cast<float *>(s0s);
+  const bf16 *xg = static_cast<const bf16 *>(a.q) + (int64_t)qc * a.q_stride + h * D;
+  auto xa = [&](int d0) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x4 *>(xg + d0);
+  };
+  prologue_bwd_rows<D>(dq, a.scale, meta, rho0, qi < seg1, xa, g_s, p.rope, p.rope_frame_pairs, p.rms_eps,
+                       static_cast<bf16 *>(a.dq), ((int64_t)qc * H + h) * D, red + wave * 2 * D, lane);
+  __syncthreads();
+  sum_wave_partials<D>(red, NWQ, part, tid);
+}
+
+// ---------------------------------------------------------------------------
 // dK-hat and dV for one 128-key tile of one sample and head.
 //
 // Eight waves in two roles, paired per SIMD (wave w and w+4 share keys
@@ -413,7 +587,7 @@ constexpr int KV_NW = 8;   // waves of a dK/dV workgroup
 constexpr int KV_NS = 4;   // Q-hat / dO ring stages
 }  // namespace bwd
 
-template <int D>
+template <int D, bool DS>
 __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanDev p, AttnBwdArgs a) {
   using namespace bwd;
   constexpr int KS = D / 16;
@@ -456,6 +630,22 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform to the compiler
   const int role = wave >> 2, sub = wave & 3;  // role 0: P/dV, role 1: dS/dK
   const int lq = lane & 31, g = lane >> 5;
+  // Stored dS (DS): 1 KiB block (kb, u) of this sample and head holds keys
+  // 32kb..+31 and queries 16u..+15 (sample-relative), lane (g, key lq) of
+  // the writing wave at 16 bytes (2 lq + g) * 16: its eight dS values for
+  // queries 16u + acc_row(0..7, g). The descriptor ends with the area, so a
+  // wave whose keys all lie past the segment end stores nothing.
+  rsrc_t ds_rs = make_rsrc(a.ds, 0u);
+  uint32_t ds_off = 0;
+  if constexpr (DS) {
+    const int L = seg1 - seg0;
+    const int nq16 = 4 * ((L + BMQ - 1) / BMQ);
+    const int64_t blocks = (int64_t)((L + 31) / 32) * nq16;
+    ds_rs = make_rsrc(static_cast<char *>(a.ds) + (p.ds_base[it.w] + h * blocks) * kDsBlockBytes,
+                      (uint32_t)(blocks * kDsBlockBytes));
+    const int kb = (k0 - seg0) / 32 + sub;
+    ds_off = (uint32_t)kb * (uint32_t)nq16 * kDsBlockBytes + 16u * (2 * lq + g);
+  }
   const int64_t HD = (int64_t)H * D;
   const int64_t gstride = a.dout_stride;
   const bf16 *qh = static_cast<const bf16 *>(a.q_hat) + h * D;
@@ -647,12 +837,29 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
       }
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
-      wait_vmem_le<PER_TILE>();  // this wave's loads of tile t+1
+      // This wave's loads of tile t+1: loads complete in issue order, so at
+      // most PER_TILE outstanding operations (tile t+2's loads) leaves none
+      // of them. Stores (dS, with DS) may complete out of order with respect
+      // to loads, so they are not counted on.
+      wait_vmem_le<PER_TILE>();
       phase_barrier();  // P(t) and tile t+1 visible
-      issue_g(std::integral_constant<int, (SG + 3) % KV_NS>{}, t + 3);
-      if (t < ntq) {
-        dscores(dst(stage));  // dS(t)
-        if (t + 1 == ntq) accumulate(qst(stage));  // last dK
+      if constexpr (DS) {
+        if (t < ntq) {
+          dscores(dst(stage));  // dS(t)
+#pragma unroll
+          for (int u = 0; u < BMQ / 16; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pb[u]), ds_rs,
+                                                   (int)(ds_off + (uint32_t)(4 * t + u) * kDsBlockBytes), 0,
+                                                   bwd::kDsCachePolicy);
+        }
+        issue_g(std::integral_constant<int, (SG + 3) % KV_NS>{}, t + 3);
+        if (t < ntq && t + 1 == ntq) accumulate(qst(stage));  // last dK
+      } else {
+        issue_g(std::integral_constant<int, (SG + 3) % KV_NS>{}, t + 3);
+        if (t < ntq) {
+          dscores(dst(stage));  // dS(t)
+          if (t + 1 == ntq) accumulate(qst(stage));  // last dK
+        }
       }
       phase_barrier();  // P(t) consumed
     };
@@ -705,14 +912,31 @@ static hipError_t bwd_dq(const PlanDev &p, const AttnBwdArgs &a, hipStream_t s) 
 }
 template <int D>
 static hipError_t bwd_dkdv(const PlanDev &p, const AttnBwdArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)p.num_bwd_blocks), dim3(64 * bwd::KV_NW), 0, s, p, a);
+  if (a.ds)
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), dim3((unsigned)p.num_bwd_blocks), dim3(64 * bwd::KV_NW), 0,
+                       s, p, a);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), dim3((unsigned)p.num_bwd_blocks), dim3(64 * bwd::KV_NW), 0,
+                       s, p, a);
   return hipGetLastError();
 }
 
-// which = 0: dQ-hat and D; which = 1: dK-hat and dV (reads D).
+template <int D>
+static hipError_t bwd_dq_ds(const PlanDev &p, const AttnBwdArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(attn_bwd_dq_ds_kernel<D>, dim3((unsigned)p.num_fwd_blocks), dim3(64 * bwd::NWQ), 0, s, p, a);
+  return hipGetLastError();
+}
+
+// which = kBwdDq: dQ-hat and D (a.ds null) or dQ-hat from the stored dS;
+// which = kBwdDkdv: dK-hat and dV (reads D), writing dS when a.ds is set.
 hipError_t launch_attn_bwd(int dtype, const PlanDev &p, const AttnBwdArgs &a, int which,
                            hipStream_t stream) {
   if (dtype == MMDIT_F32) return launch_attn_bwd_f32(p, a, which, stream);
+  if (which == kBwdDq && a.ds) {
+    if (p.head_dim == 64) return bwd_dq_ds<64>(p, a, stream);
+    if (p.head_dim == 128) return bwd_dq_ds<128>(p, a, stream);
+    return hipErrorInvalidValue;
+  }
   if (p.head_dim == 64) return which == 0 ? bwd_dq<64>(p, a, stream) : bwd_dkdv<64>(p, a, stream);
   if (p.head_dim == 128) return which == 0 ? bwd_dq<128>(p, a, stream) : bwd_dkdv<128>(p, a, stream);
   return hipErrorInvalidValue;

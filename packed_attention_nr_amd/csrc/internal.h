@@ -29,6 +29,12 @@ constexpr int kPbwdTokensPerBlock = 64;
 constexpr int kPbwdMaxBlocks = 1024;
 // XCDs (each with its own L2) of the target GPU; workgroup b runs on XCD b % kXcds.
 constexpr int kXcds = 8;
+// Stored dS of the bf16 backward: 1 KiB blocks, each 32 keys x 16 queries of
+// one (sample, head) in the dK/dV kernel's register order; samples up to
+// kDsMaxSeqlen tokens (one sample-head area stays under 4 GiB).
+constexpr int kDsBlockBytes = 1024;
+constexpr int kDsMaxSeqlen = 32768;
+inline int64_t ds_blocks_per_head(int64_t L) { return (L + 31) / 32 * 4 * ((L + 63) / 64); }
 
 constexpr uint32_t kBlobMagic = 0x50444D4Du;    // "MMDP"
 constexpr uint64_t kBlobHeaderBytes = 64;
@@ -58,9 +64,11 @@ uint64_t bwd_partial_blocks(int64_t n_tokens);
 
 // Backward workspace layout (byte offsets, each 256-byte aligned): D [H][N],
 // Q gain partials [nq][2][d], K gain partials [nk][2][d], then for fp32 plans
-// the dQ-hat and dK-hat accumulators [N][H][d].
+// the dQ-hat and dK-hat accumulators [N][H][d]; `total` bytes in all. The
+// stored-dS path (bf16) adds the dS area at `ds` (4 KiB aligned), ds_total
+// bytes in all (ds_total = total where the path does not apply).
 struct BwdLayout {
-  uint64_t delta, part_q, part_k, dq_acc, dk_acc, total;
+  uint64_t delta, part_q, part_k, dq_acc, dk_acc, total, ds, ds_total;
   int32_t nq, nk;
 };
 BwdLayout bwd_layout(const mmdit_plan &p);
@@ -83,6 +91,7 @@ struct PlanDev {
   const int32_t *mod_ranges;   // [2S+1] first chunk of each (sample, stream) range
   int32_t num_mod_chunks;
   float rms_eps;
+  const int64_t *ds_base;      // [S+1] first dS block of each sample (all heads)
 };
 
 struct PrologueFwdArgs {
@@ -105,7 +114,7 @@ struct BwdPreArgs {
   const void *o, *dout;
   int64_t dout_stride;
   float *delta;                // [H][N]
-  float *dq_acc;               // [N][H][d] fp32, zeroed here
+  float *dq_acc;               // [N][H][d] fp32, zeroed here; nullptr: D only
 };
 
 struct AttnBwdArgs {
@@ -125,6 +134,7 @@ struct AttnBwdArgs {
   const float *rstd;           // [2][N][H] or nullptr = recompute
   void *dq, *dk;               // [N][H][d] dtype, dense
   float *part_q, *part_k;      // [grid blocks][2][d] gain-gradient partials (text, image)
+  void *ds;                    // stored-dS area (bf16 path) or nullptr
 };
 
 // fp32 path: prologue backward of Q (which = 0) or K (which = 1) from the
@@ -169,7 +179,10 @@ hipError_t launch_prologue_fwd(int dtype, const PlanDev &p, const PrologueFwdArg
                                hipStream_t stream);
 hipError_t launch_attn_fwd(int dtype, const PlanDev &p, const AttnFwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd_pre(int dtype, const PlanDev &p, const BwdPreArgs &a, hipStream_t stream);
-// which = 0: dQ-hat and D; which = 1: dK-hat and dV (needs D).
+// which = kBwdDq: dQ-hat (and D, unless a.ds is set: then dQ-hat from the
+// stored dS); which = kBwdDkdv: dK-hat and dV (needs D; writes dS to a.ds
+// when set).
+constexpr int kBwdDq = 0, kBwdDkdv = 1;
 hipError_t launch_attn_bwd(int dtype, const PlanDev &p, const AttnBwdArgs &a, int which,
                            hipStream_t stream);
 hipError_t launch_prologue_bwd(int dtype, const PlanDev &p, const PrologueBwdArgs &a,

@@ -70,6 +70,8 @@ BwdLayout bwd_layout(const mmdit_plan &p) {
     off = align_up(off + N * H * d * 4, 256);
   }
   w.total = off;
+  w.ds = align_up(off, 4096);
+  w.ds_total = p.bwd_ds_workspace_bytes > off ? p.bwd_ds_workspace_bytes : off;
   return w;
 }
 
@@ -253,12 +255,21 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, const int32_t *src_h, const
   off = align_up(off + 4ull * mod_chunks.size(), 256);
   p.off_mod_ranges = off;
   off = align_up(off + 4ull * mod_ranges.size(), 256);
+  p.off_ds_base = off;
+  off = align_up(off + 8ull * (S + 1), 256);
   p.blob_bytes = off;
 
   const uint64_t elt = desc->dtype == MMDIT_BF16 ? 2 : 4;
   const uint64_t nhd = (uint64_t)N * H * d;
   p.fwd_workspace_bytes = 2 * align_up(nhd * elt, 256);
   p.bwd_workspace_bytes = bwd_layout(p).total;
+  // Stored-dS backward: per sample and head ceil(L/32) * 4 * ceil(L/64)
+  // blocks of 1 KiB, samples in pack order, heads inside a sample.
+  std::vector<int64_t> ds_base(S + 1, 0);
+  for (int i = 0; i < S; ++i) ds_base[i + 1] = ds_base[i] + (int64_t)H * ds_blocks_per_head(cu[i + 1] - cu[i]);
+  p.bwd_ds_workspace_bytes = p.bwd_workspace_bytes;
+  if (desc->dtype == MMDIT_BF16 && max_len <= kDsMaxSeqlen)
+    p.bwd_ds_workspace_bytes = bwd_layout(p).ds + (uint64_t)ds_base[S] * kDsBlockBytes;
   p.fingerprint = plan_fingerprint(p);
   *plan = p;
 
@@ -317,6 +328,7 @@ mmdit_status build_plan(const mmdit_pack_desc *desc, const int32_t *src_h, const
   std::memcpy(blob + p.off_bwd_blocks, bwd_blocks.data(), 4 * bwd_blocks.size());
   std::memcpy(blob + p.off_mod_chunks, mod_chunks.data(), 4 * mod_chunks.size());
   std::memcpy(blob + p.off_mod_ranges, mod_ranges.data(), 4 * mod_ranges.size());
+  std::memcpy(blob + p.off_ds_base, ds_base.data(), 8 * ds_base.size());
 
   // RoPE table [rope_rows][d/2] of {cos, sin}(pos * omega_p), in double,
   // rounded once.

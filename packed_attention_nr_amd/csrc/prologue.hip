@@ -122,7 +122,8 @@ __global__ __launch_bounds__(256) void prologue_fwd_kernel(PlanDev p, PrologueFw
 }
 
 // ---------------------------------------------------------------------------
-// Backward preprocess: D = rowsum(dO * O); clear dQ-hat accumulator.
+// Backward preprocess: D = rowsum(dO * O); clear the fp32 dQ-hat
+// accumulator when there is one.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(PlanDev p, BwdPreArgs a) {
@@ -144,6 +145,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PlanDev p, BwdPreArgs a) {
   for (int i = 0; i < VEC; ++i) s += o[i] * g[i];
   s = group_sum<LPR>(s);
   if (e0 == 0) a.delta[(int64_t)h * N + t] = s;
+  if (!a.dq_acc) return;
   float *z = a.dq_acc + r * D + e0;
 #pragma unroll
   for (int i = 0; i < VEC; i += 4) *reinterpret_cast<float4 *>(z + i) = make_float4(0.f, 0.f, 0.f, 0.f);

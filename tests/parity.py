@@ -59,8 +59,11 @@ def host(t):
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def run_gpu(inp, backward=True, device="cuda"):
-    """Forward (and backward) through the binding. Returns numpy fp64 arrays."""
+def run_gpu(inp, backward=True, device="cuda", bwd_workspace="bwd"):
+    """Forward (and backward) through the binding. Returns numpy fp64 arrays.
+    bwd_workspace: a Pack.workspace kind: "bwd" (the default choice),
+    "bwd_ds" (dQ from the stored dS) or "bwd_recompute" (dQ with S and dP
+    recomputed)."""
     import packed_attention_nr_amd as pam
     import torch
     pack = pam.Pack(inp.text_len, inp.grid_h, inp.grid_w, inp.heads, inp.head_dim,
@@ -70,7 +73,8 @@ def run_gpu(inp, backward=True, device="cuda"):
     saved = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"])
     out = {k: host(v) for k, v in saved.items()}
     if backward and inp.dout is not None:
-        g = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], saved, t["dout"])
+        g = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], saved, t["dout"],
+                         workspace=pack.workspace(bwd_workspace))
         out.update({k: host(v) for k, v in g.items() if k != "workspace"})
     torch.cuda.synchronize()
     out["lse"] = out["lse"].T            # [N, H] like the oracle

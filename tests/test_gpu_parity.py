@@ -74,6 +74,49 @@ def test_edge_packs(case, d, dtype):
     _compare(inp, run_gpu(inp), run_oracle(inp))
 
 
+@pytest.mark.parametrize("mode", ["bwd_recompute", "bwd_ds"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", ["one_token_samples", "exact_tiles", "ragged_multi_tile", "wide_4to1"])
+def test_backward_modes(case, d, mode):
+    """Both bf16 backward modes at both head sizes: dQ with S and dP formed
+    again per query tile (a workspace too small for dS), and dQ from the dS
+    that the dK/dV kernel stores. (The other cases take the default
+    workspace: recompute.)"""
+    spec = EDGE_PACKS[case]
+    inp = workloads.random_pack(40 + sorted(EDGE_PACKS).index(case), heads=3, head_dim=d, dtype="bf16",
+                                text=spec["text"], grids=spec["grids"])
+    _say(f"backward {mode} {case} d={d} N={inp.num_tokens}")
+    _compare(inp, run_gpu(inp, bwd_workspace=mode), run_oracle(inp))
+
+
+def test_stored_ds_stage_calls_match_one_call():
+    """The stored-dS backward as separate stage calls (D, dK/dV, dQ, gains,
+    each with the mode flag) gives bitwise the results of one call."""
+    import packed_attention_nr_amd as pam
+    from parity import to_device
+    inp = workloads.random_pack(23, heads=2, head_dim=128, dtype="bf16",
+                                text=[45, 3, 130], grids=[(13, 11), (2, 5), (7, 19)])
+    _say(f"stored-dS stage calls N={inp.num_tokens}")
+    pack = pam.Pack(inp.text_len, inp.grid_h, inp.grid_w, inp.heads, inp.head_dim, "bf16")
+    assert pack.plan.bwd_ds_workspace_bytes > pack.plan.bwd_workspace_bytes
+    t = to_device(inp)
+    saved = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"])
+    one = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], saved, t["dout"],
+                       workspace=pack.workspace("bwd_ds"))
+    N, H, d = pack.N, pack.H, pack.d
+    out = {n: torch.empty_like(one[n]) for n in ("dq", "dk", "dv", "dgains")}
+    ws = pack.workspace("bwd_ds")
+    B = pam.BWD_STAGES
+    for st in (B["d"] | B["store_ds"], B["dkdv"] | B["store_ds"], B["dq"] | B["store_ds"], B["gains"]):
+        pam.mmdit_attn_bwd(pack.plan, pack.blob_dev, q=t["q"], k=t["k"], v=t["v"], q_hat=saved["q_hat"],
+                           k_hat=saved["k_hat"], o=saved["o"], dout=t["dout"], q_stride=H * d,
+                           k_stride=H * d, v_stride=H * d, dout_stride=H * d, gains=t["gains"],
+                           lse=saved["lse"], rstd=saved["rstd"], workspace=ws, stages=st, **out)
+    torch.cuda.synchronize()
+    for n in out:
+        assert torch.equal(out[n], one[n]), n
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("seed", range(6))
 def test_random_packs(seed, dtype):

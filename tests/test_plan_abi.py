@@ -29,7 +29,7 @@ def test_exports_every_header_symbol(L):
     assert {"mmdit_pack_plan", "mmdit_attn_fwd", "mmdit_attn_bwd"} <= names
     for n in sorted(names):
         assert hasattr(L, n), n
-    assert pam.mmdit_abi_version() == pam.ABI_VERSION == 3
+    assert pam.mmdit_abi_version() == pam.ABI_VERSION == 4
     assert pam.mmdit_status_str(0) == "ok"
 
 
@@ -135,6 +135,18 @@ def _check_plan(inp, dtype_code):
     for r in range(2 * S):   # a range's chunks are consecutive and ordered
         rows = [x for c in range(rg[r], rg[r + 1]) for x in range(ch[c, 0], ch[c, 1])]
         assert rows == np.flatnonzero(midx == r).tolist()
+    # stored-dS areas: per sample and head ceil(L/32) * 4 * ceil(L/64) blocks
+    # of 1 KiB, samples in pack order; the area follows the backward's
+    # workspace at the next 4 KiB (bf16 packs whose samples have at most
+    # 32,768 tokens; else no larger workspace is offered)
+    Ls = np.diff(lay.cu_seqlens)
+    per = (Ls + 31) // 32 * 4 * ((Ls + 63) // 64)
+    base = _blob_section(blob, plan.off_ds_base, S + 1, np.int64)
+    assert np.array_equal(base, np.concatenate([[0], np.cumsum(H * per)]))
+    if dtype_code == 1 and Ls.max() <= 32768:
+        assert plan.bwd_ds_workspace_bytes == (plan.bwd_workspace_bytes + 4095) // 4096 * 4096 + 1024 * int(base[-1])
+    else:
+        assert plan.bwd_ds_workspace_bytes == plan.bwd_workspace_bytes
     return plan
 
 
@@ -353,7 +365,11 @@ def _bwd(plan, ws_bytes=None, **kw):
     (dict(dout_stride=64), 1),
     (dict(dout_stride=(1 << 24) + 8), 1),
     (dict(ws=None), 1),
-    (dict(stages=16), 1),
+    (dict(stages=32), 1),                 # unknown stage bit
+    (dict(stages=8), 1),                  # stage D only in the stored-dS mode
+    (dict(stages=8 | 16), 3),             # stored-dS mode without room for dS
+    (dict(stages=8 | 16, o=None, ws_bytes=1 << 20), 1),     # stage D reads o
+    (dict(stages=8 | 16, dout=None, ws_bytes=1 << 20), 1),  # ... and dout
     (dict(ws_bytes=64), 3),
     (dict(stages=1, q=None), 1),          # the dQ stage writes dq from q
     (dict(stages=1, o=None), 1),          # ... and forms D from o
@@ -366,6 +382,14 @@ def _bwd(plan, ws_bytes=None, **kw):
 def test_bwd_rejects_invalid_arguments(small_plan, kw, code):
     ws_bytes = kw.pop("ws_bytes", None)
     assert _bwd(small_plan, ws_bytes=ws_bytes, **kw) == code, pam.mmdit_last_error()
+
+
+def test_bwd_stored_ds_mode_needs_a_bf16_plan(L):
+    """fp32 plans (and samples over 32,768 tokens) have no stored-dS mode."""
+    plan, _ = pam.mmdit_pack_plan([5, 3], [2, 3], [3, 2], 2, 64, 0)
+    assert plan.bwd_ds_workspace_bytes == plan.bwd_workspace_bytes
+    assert _bwd(plan, ws_bytes=1 << 20, stages=2 | 16) == 2, pam.mmdit_last_error()
+    assert "stored-dS" in pam.mmdit_last_error()
 
 
 def _adaln_fwd(plan, **kw):
