@@ -139,9 +139,8 @@ typedef struct {
                                     num_mod_chunks * 3 * model_dim * 4 bytes */
   int32_t mod_chunk_rows;        /* rows per adaLN chunk (32) */
   uint64_t off_ds_base;
-  uint64_t bwd_ds_workspace_bytes; /* a workspace this large lets mmdit_attn_bwd (all of stages
-                                      DQ and DKDV in one call, bf16) store dS and form dQ from it;
-                                      equals bwd_workspace_bytes where that path does not apply
+  uint64_t bwd_ds_workspace_bytes; /* workspace of the stored-dS backward (see mmdit_attn_bwd);
+                                      equals bwd_workspace_bytes where the plan has no such mode
                                       (fp32 plans, samples over 32,768 tokens) */
   uint64_t fingerprint;          /* hash of every field above; checked on each call */
 } mmdit_plan;
