@@ -273,6 +273,22 @@ FULL = [("gen1024", [0, 11, 23]), ("mixed6", [0, 13]), ("gen2048", [5]), ("small
         ("edit1024", [0, 17])]
 
 
+@pytest.mark.parametrize("name,heads", [("mixed6", [5, 19]), ("edit1024", [7])], ids=["mixed6", "edit1024"])
+def test_full_workload_stored_ds(name, heads):
+    """The stored-dS backward at full size (the mixed-resolution training
+    pack: 3.6 GiB of dS), against the oracle on sampled heads, and the
+    recompute backward's dV bit for bit (dV does not depend on D, which the two
+    modes sum in different orders; the kernel differs only in also storing
+    dS)."""
+    inp = workloads.draw(name)
+    _say(f"{name} stored dS: N={inp.num_tokens} H={inp.heads} heads checked={heads}")
+    gpu = run_gpu(inp, bwd_workspace="bwd_ds")
+    ref = run_oracle(inp, heads=heads)
+    _compare(inp, gpu, ref, heads=heads)
+    rec = run_gpu(inp, bwd_workspace="bwd_recompute")
+    assert np.array_equal(gpu["dv"], rec["dv"])
+
+
 @pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])
 def test_full_workload(name, heads):
     w = workloads.get(name)
