@@ -484,3 +484,20 @@ def test_cfg_pack_desc_rejects(L):
     assert st == 0 and out.num_samples == 4 and out.token_budget == 20
     plan = pam.Plan()                                    # 6 + 10 + 6 + 9 = 31 tokens > 20
     assert pam.lib().mmdit_pack_plan(C.byref(out), C.byref(plan), None, 0) == 4
+
+
+def test_pack_workspace_kinds(L):
+    """Pack.workspace sizes: "bwd" and "bwd_recompute" take the plan's
+    backward workspace, "bwd_ds" the stored-dS one (refused over ds_limit),
+    "fwd" the inference forward's; unknown kinds are refused."""
+    pack = pam.Pack([5, 3], [2, 3], [3, 2], 2, 64, "bf16", device="cpu")
+    p = pack.plan
+    assert p.bwd_ds_workspace_bytes > p.bwd_workspace_bytes
+    assert pack.workspace("bwd").numel() == p.bwd_workspace_bytes
+    assert pack.workspace("bwd_recompute").numel() == p.bwd_workspace_bytes
+    assert pack.workspace("bwd_ds").numel() == p.bwd_ds_workspace_bytes
+    assert pack.workspace("fwd").numel() == p.fwd_workspace_bytes
+    with pytest.raises(ValueError):
+        pack.workspace("bwd_ds", ds_limit=p.bwd_ds_workspace_bytes - 1)
+    with pytest.raises(ValueError):
+        pack.workspace("bwd_dS")
