@@ -263,6 +263,30 @@ mmdit_status mmdit_attn_bwd(const mmdit_plan *plan, const void *plan_blob_dev,
                             const mmdit_bwd_args *args, void *workspace,
                             uint64_t workspace_bytes, void *hip_stream);
 
+/* Size of the per-GPU device array that mmdit_attn_bwd_noalloc uses as its
+ * workspace (64 MiB): packs whose plan->bwd_workspace_bytes exceed it are
+ * refused by that entry point. */
+#define MMDIT_NOALLOC_WORKSPACE_BYTES (64ull << 20)
+
+/* mmdit_attn_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same backward in its recompute mode, with the workspace taken from a
+ * device array that the library owns (one per GPU, held until the process
+ * ends) instead of a caller buffer. The caller still passes every input and
+ * output, as for mmdit_attn_bwd; stage subsets run as there, and the array
+ * keeps what the last call on that GPU left in it (a DKDV-only call reads the
+ * D of the DQ call before it). The stream (NULL = default) must belong to the
+ * current device. Calls that overlap on one GPU (different streams or
+ * threads without ordering) share the array and race. Errors: those of
+ * mmdit_attn_bwd; BUFFER_TOO_SMALL when plan->bwd_workspace_bytes >
+ * MMDIT_NOALLOC_WORKSPACE_BYTES; UNSUPPORTED with MMDIT_STAGE_BWD_STORE_DS;
+ * INVALID_ARG when the stream is on another device; HIP when the array's
+ * device address cannot be looked up. Allocates, frees and synchronises
+ * nothing. Deterministic, with results bitwise equal to mmdit_attn_bwd's
+ * recompute mode. */
+mmdit_status mmdit_attn_bwd_noalloc(const mmdit_plan *plan, const void *plan_blob_dev,
+                                    const mmdit_bwd_args *args, void *hip_stream);
+
 /* Adaptive LayerNorm modulation with the fused gated residual, the memory-
  * bound chains on either side of the attention core of an NR-MMDiT block
  * (picx.dev "Mage-Flow ...", section "Training Infrastructure": adaptive

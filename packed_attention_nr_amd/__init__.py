@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "MmditError", "lib", "mmdit_pack_plan", "mmdit_pack_plan_edit", "mmdit_attn_fwd",
-    "mmdit_attn_bwd", "mmdit_cfg_pack_desc", "mmdit_adaln_fwd", "mmdit_adaln_bwd",
+    "mmdit_attn_bwd", "mmdit_attn_bwd_noalloc", "mmdit_cfg_pack_desc", "mmdit_adaln_fwd", "mmdit_adaln_bwd",
     "adaln_forward", "adaln_backward",
     "mmdit_status_str", "mmdit_last_error", "mmdit_abi_version", "Pack",
     "forward", "backward", "FWD_STAGES", "BWD_STAGES", "LIB_PATH",
@@ -132,6 +132,9 @@ def lib():
         L.mmdit_attn_bwd.restype = C.c_int
         L.mmdit_attn_bwd.argtypes = [C.POINTER(Plan), C.c_void_p, C.POINTER(BwdArgs), C.c_void_p,
                                      C.c_uint64, C.c_void_p]
+        L.mmdit_attn_bwd_noalloc.restype = C.c_int
+        L.mmdit_attn_bwd_noalloc.argtypes = [C.POINTER(Plan), C.c_void_p, C.POINTER(BwdArgs),
+                                             C.c_void_p]
         L.mmdit_adaln_fwd.restype = C.c_int
         L.mmdit_adaln_fwd.argtypes = [C.POINTER(Plan), C.c_void_p, C.POINTER(AdalnFwdArgs),
                                       C.c_void_p]
@@ -271,6 +274,19 @@ def mmdit_attn_bwd(plan: Plan, blob_dev, *, q=None, k=None, v=None, q_hat=None, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().mmdit_attn_bwd(C.byref(plan), _ptr(blob_dev), C.byref(a), _ptr(workspace),
                                 ws_bytes, _stream(stream)))
+
+
+def mmdit_attn_bwd_noalloc(plan: Plan, blob_dev, *, q=None, k=None, v=None, q_hat=None,
+                           k_hat=None, o=None, dout=None, q_stride=0, k_stride=0, v_stride=0,
+                           dout_stride=0, gains=None, lse=None, rstd=None, dq=None, dk=None,
+                           dv=None, dgains=None, stages: int = 0, stream=None):
+    """Run mmdit_attn_bwd_noalloc (the recompute backward with the library's
+    own per-GPU workspace; no workspace argument)."""
+    a = BwdArgs(_ptr(q), _ptr(k), _ptr(v), _ptr(q_hat), _ptr(k_hat), _ptr(o), _ptr(dout),
+                int(q_stride), int(k_stride), int(v_stride), int(dout_stride), _ptr(gains),
+                _ptr(lse), _ptr(rstd), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgains), int(stages))
+    _check(lib().mmdit_attn_bwd_noalloc(C.byref(plan), _ptr(blob_dev), C.byref(a),
+                                        _stream(stream)))
 
 
 def mmdit_adaln_fwd(plan: Plan, blob_dev, *, x=None, y=None, x_stride=0, y_stride=0, shift=None,

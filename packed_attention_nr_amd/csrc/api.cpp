@@ -182,8 +182,8 @@ static mmdit_status attn_fwd(const mmdit_plan *plan, const void *blob, const mmd
   return MMDIT_OK;
 }
 
-static mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmdit_bwd_args *a,
-                             void *ws, uint64_t ws_bytes, void *stream) {
+mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmdit_bwd_args *a,
+                      void *ws, uint64_t ws_bytes, void *stream) {
   mmdit_status st = check_plan(plan, blob);
   if (st) return st;
   if (!a) return fail(MMDIT_ERR_INVALID_ARG, "args must not be NULL");

@@ -73,6 +73,11 @@ struct BwdLayout {
 };
 BwdLayout bwd_layout(const mmdit_plan &p);
 
+// The backward behind mmdit_attn_bwd (validation, then launches); also used
+// by the entry point that brings its own workspace.
+mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmdit_bwd_args *a, void *ws,
+                      uint64_t ws_bytes, void *stream);
+
 // ---------------------------------------------------------------------------
 // Kernel launch arguments (device pointers; plain data passed by value).
 // ---------------------------------------------------------------------------

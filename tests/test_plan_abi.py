@@ -501,3 +501,28 @@ def test_pack_workspace_kinds(L):
         pack.workspace("bwd_ds", ds_limit=p.bwd_ds_workspace_bytes - 1)
     with pytest.raises(ValueError):
         pack.workspace("bwd_dS")
+
+
+def _noalloc(plan, **kw):
+    names = ("q", "k", "v", "q_hat", "k_hat", "o", "dout")
+    args = {n: _p(i + 1) for i, n in enumerate(names)}
+    args.update(gains=_p(8), lse=_p(9), rstd=_p(10), dq=_p(11), dk=_p(12), dv=_p(13), dgains=_p(14))
+    args.update(kw)
+    a = pam.BwdArgs(*(args[n] for n in names), 128, 128, 128, 128, args["gains"], args["lse"],
+                    args["rstd"], args["dq"], args["dk"], args["dv"], args["dgains"],
+                    args.get("stages", 0))
+    return pam.lib().mmdit_attn_bwd_noalloc(None if plan is None else C.byref(plan), _p(0),
+                                            C.byref(a), None)
+
+
+def test_noalloc_refuses_before_touching_a_device(L):
+    """The allocation-free backward refuses, on the host and before any HIP
+    call, the stored-dS mode and packs whose workspace exceeds its array."""
+    plan, _ = pam.mmdit_pack_plan([5, 3], [2, 3], [3, 2], 1, 128, 1)
+    assert _noalloc(plan, stages=2 | 16) == 2, pam.mmdit_last_error()
+    assert "recompute" in pam.mmdit_last_error()
+    big, _ = pam.mmdit_pack_plan([0], [512], [512], 24, 128, 1)
+    assert big.bwd_workspace_bytes > 64 << 20
+    assert _noalloc(big) == 3, pam.mmdit_last_error()
+    assert "exceeds" in pam.mmdit_last_error()
+    assert _noalloc(None) == 1
