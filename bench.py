@@ -4,16 +4,32 @@
 
 One step = one pass of the whole path over one synthetic pack: the host pack
 plan and its upload, the forward (QK-norm + 2D RoPE prologue, var-len
-attention) and the backward (D = rowsum(dO*O), var-len attention backward
-with the prologue backward fused into its epilogues, gain-gradient reduction;
+attention) and the backward (var-len attention backward with D = rowsum(dO*O)
+and the prologue backward fused into its kernels, gain-gradient reduction;
 --bwd-mode stored_ds forms dQ from the dS that the dK/dV kernel stores).
 HIP events recorded on the launch stream between the stages give each
-kernel's duration inside the timed region.
-Prints one JSON line.
+kernel's duration inside the timed region. Prints one JSON line.
 
-metric: bf16 forward+backward attention throughput in TFLOP/s, counting
-4*H*d*sum(L_i^2) for the forward and 10*H*d*sum(L_i^2) for the backward,
-divided by the whole step time (plan, prologues and preprocess included).
+metric (`value`): bf16 forward+backward attention throughput in TFLOP/s,
+counting 4*H*d*sum(L_i^2) for the forward and 10*H*d*sum(L_i^2) for the
+backward, divided by the whole step time (plan, prologues and gain reduction
+included), on the mixed-resolution training pack.
+
+Also in the line:
+  per_config     every configuration's pack (1024^2 generation forward,
+                 mixed-resolution pack, 2048^2 sample, 64 small segments):
+                 median HIP-event time per stage; the prologue and the whole
+                 forward call after writing a 512 MiB buffer (Infinity Cache
+                 flushed), the attention kernels back to back; TFLOP/s and
+                 fraction of the bf16 spec peak, prologue GB/s and fraction
+                 of HBM; the reported core clock sampled meanwhile;
+  measured_peaks a dense matrix-instruction loop (achievable bf16 throughput
+                 and the core clock under it) and a 1 GiB copy;
+  roofline       the dominant kernel of the step against the bf16 peak;
+  cpu_baseline   the fp64 oracle timed on the host cores, forward and
+                 backward separately per configuration, on head subsets;
+  next-row fields: packed CFG at 1024^2, the 1024^2 editing step, adaLN with
+                 the gated residual, the bucket-padding comparison.
 """
 from __future__ import annotations
 
@@ -71,26 +87,316 @@ def measured_traffic(kernel: str):
     return None if k is None else k["hbm_bytes"]
 
 
-def cpu_baseline(inp, heads):
-    """Time the fp64 oracle (fwd+bwd) on a subset of heads; report TFLOP/s of
-    the same algorithmic count, scaled to the metric's unit."""
-    import oracle
+def host_info():
+    """Host cores, CPU model and BLAS of the oracle's numpy (read without
+    starting any program)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = " ".join(str(b.get(k, "")) for k in ("name", "version")).strip() or None
+    except Exception:  # pragma: no cover - older numpy
+        pass
+    threads = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            threads = max(int(i.get("num_threads", 1)) for i in info)
+            blas = blas or info[0].get("internal_api")
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    hs = list(range(heads))
-    q, k, v, do = (x[:, hs] for x in (inp.q, inp.k, inp.v, inp.dout))
+        pass
+    return {"cpu_model": model, "blas": blas, "threads": threads,
+            "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def oracle_timing(name, heads, seed=0):
+    """Time the fp64 oracle's forward and backward, separately, on `heads`
+    heads of the workload's pack geometry (inputs drawn like the workload's,
+    with that head count; input generation not timed)."""
+    import oracle
+    w = workloads.get(name)
+    text, grids, src = workloads.geometry(name)
+    inp = workloads.random_pack(seed, heads=heads, head_dim=w.head_dim, dtype=w.dtype,
+                                backward=w.backward, text=text, grids=grids, src=src)
+    sl2 = sum_l2(inp)
     t0 = time.perf_counter()
-    f = oracle.forward(inp.text_len, inp.grid_h, inp.grid_w, q, k, v, inp.gains)
-    oracle.backward(inp.text_len, inp.grid_h, inp.grid_w, q, k, v, inp.gains, do, lay=f["layout"])
-    dt = time.perf_counter() - t0
-    flops = 14.0 * heads * inp.head_dim * sum_l2(inp)
-    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(threads),
+    f = oracle.forward(inp.text_len, inp.grid_h, inp.grid_w, inp.q, inp.k, inp.v, inp.gains)
+    t1 = time.perf_counter()
+    out = {"heads": heads, "fwd_s": round(t1 - t0, 3),
+           "fwd_gflops": round(4.0 * heads * w.head_dim * sl2 / (t1 - t0) / 1e9, 2)}
+    if w.backward:
+        oracle.backward(inp.text_len, inp.grid_h, inp.grid_w, inp.q, inp.k, inp.v, inp.gains,
+                        inp.dout, lay=f["layout"])
+        t2 = time.perf_counter()
+        out.update(bwd_s=round(t2 - t1, 3),
+                   bwd_gflops=round(10.0 * heads * w.head_dim * sl2 / (t2 - t1) / 1e9, 2))
+    return out
+
+
+def cpu_baseline(headline, heads):
+    """The oracle as it stands, timed on the host cores: forward and backward
+    separately on a head subset of every configuration's pack; the headline
+    value is the headline workload's forward+backward throughput."""
+    info = host_info()
+    per = {}
+    for name, h in (("gen1024", 1), ("mixed6", heads), ("gen2048", 1), ("small64", 1)):
+        per[name] = oracle_timing(name, h)
+    hl = per.get(headline) or oracle_timing(headline, heads)
+    w = workloads.get(headline)
+    text, grids, src = workloads.geometry(headline)
+    L = np.asarray(text, np.int64) + np.asarray([g[0] * g[1] for g in grids], np.int64)
+    sl2 = int((L * L).sum())
+    t = hl["fwd_s"] + hl.get("bwd_s", 0.0)
+    flops = 14.0 * hl["heads"] * w.head_dim * sl2
+    total_s = sum(v["fwd_s"] + v.get("bwd_s", 0.0) for v in per.values())
+    return dict(value=round(flops / t / 1e12, 6), unit="TFLOP/s", cores=int(info["threads"]),
                 kind="oracle",
-                sample=f"fp64 numpy oracle forward+backward of {heads} of {inp.heads} heads "
-                       f"of the same pack ({dt:.1f} s); throughput of that sample")
+                sample=(f"fp64 numpy oracle, forward and backward timed separately, on {hl['heads']} "
+                        f"of {w.heads} heads of the {headline} pack ({t:.1f} s) for the value; "
+                        f"per_config: 1 head of gen1024 (forward only), gen2048 and small64, "
+                        f"{heads} of mixed6 ({total_s:.1f} s in all)"),
+                per_config=per, **{k: info[k] for k in ("cpu_model", "blas", "affinity_cores")})
+
+
+# ---------------------------------------------------------------------------
+# Timing machinery: HIP events on the launch stream, an Infinity-Cache flush
+# before each rep of memory-bound work, a sampler of the reported core clock.
+# ---------------------------------------------------------------------------
+FLUSH_BYTES = 512 << 20       # > the 256 MB Infinity Cache
+
+
+class Flush:
+    """Reads a 512 MiB device buffer (a sum into one word): evicts the
+    Infinity Cache and the L2s without leaving dirty lines whose write-back
+    would land in the next timed kernel."""
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        self.out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.torch.sum(self.buf, dim=0, out=self.out)
+
+
+def _sclk_path():
+    """hwmon core-clock file of the GPU in use (matched by PCI address when
+    several cards are listed), or None."""
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/freq1_input"))
+    paths = [p for p in paths if os.access(p, os.R_OK)]
+    if len(paths) <= 1:
+        return paths[0] if paths else None
+    try:
+        import torch
+        pr = torch.cuda.get_device_properties(torch.cuda.current_device())
+        want = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}"
+    except Exception:
+        return None
+    for p in paths:
+        dev = os.path.basename(os.path.realpath(p.split("/hwmon/")[0]))
+        if dev.lower().startswith(want):
+            return p
+    return None
+
+
+class ClockSampler:
+    """Samples the GPU's reported core clock (hwmon freq1_input, in Hz) every
+    few milliseconds from a thread while work runs; summary() is None where
+    the file is not readable."""
+
+    def __init__(self, period_s=0.005):
+        self.path = _sclk_path()
+        self.period = period_s
+        self.samples = []
+
+    def _run(self):
+        while not self.stop.is_set():
+            try:
+                with open(self.path) as fh:
+                    self.samples.append(int(fh.read().strip()) / 1e6)
+            except (OSError, ValueError):
+                pass
+            time.sleep(self.period)
+
+    def __enter__(self):
+        import threading
+        self.stop = threading.Event()
+        self.th = threading.Thread(target=self._run, daemon=True) if self.path else None
+        if self.th:
+            self.th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.th:
+            self.th.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        a = np.asarray(self.samples)
+        return {"mhz_median": round(float(np.median(a)), 1), "mhz_min": round(float(a.min()), 1),
+                "mhz_max": round(float(a.max()), 1), "samples": int(a.size)}
+
+
+def time_stage(torch, fn, flush=None, min_reps=50, max_reps=2000, target_s=0.5):
+    """Median milliseconds of fn over reps = clamp(target_s / its time, 50,
+    2000) reps, each bracketed by HIP events on the current stream (the one
+    the library launches on), after 3 untimed calls; flush (if given) runs
+    before every rep, outside the events."""
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    est = max(e0.elapsed_time(e1) / 3, 1e-3)
+    reps = int(min(max_reps, max(min_reps, np.ceil(target_s * 1e3 / est))))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.asarray([a.elapsed_time(b) for a, b in evs])
+    return float(np.median(t)), reps
+
+
+def device_inputs(torch, dev, N, H, d, seed, backward):
+    """Seeded N(0,1) bf16 Q, K, V (and dO) and gains 1 + 0.1 N(0,1), drawn on
+    the device: the workloads' distributions, used where only timing counts."""
+    g = torch.Generator(device=dev).manual_seed(seed)
+    rnd = lambda: torch.randn((N, H, d), generator=g, device=dev).to(torch.bfloat16)
+    q, k, v = rnd(), rnd(), rnd()
+    gains = 1.0 + 0.1 * torch.randn((4, d), generator=g, device=dev)
+    do = rnd() if backward else None
+    return q, k, v, do, gains
+
+
+def measure_config(pam, torch, dev, name, flush, seed):
+    """Per-stage times of one workload's pack on the device (medians of HIP
+    event pairs): the prologue and the whole forward call after a cache flush
+    (memory-bound / the per-layer latency), the attention kernels and the
+    backward stages back to back. Returns the per-config record."""
+    w = workloads.get(name)
+    text, grids, src = workloads.geometry(name)
+    hs, ws = [g[0] for g in grids], [g[1] for g in grids]
+    H, d = w.heads, w.head_dim
+    pack = pam.Pack(text, hs, ws, H, d, "bf16", device=dev)
+    N = pack.N
+    L = np.asarray(text, np.int64) + np.asarray(hs, np.int64) * np.asarray(ws, np.int64)
+    sl2 = int((L * L).sum())
+    q, k, v, do, gains = device_inputs(torch, dev, N, H, d, seed, w.backward)
+    bf = torch.bfloat16
+    o = torch.empty((N, H, d), dtype=bf, device=dev)
+    q_hat, k_hat = torch.empty_like(o), torch.empty_like(o)
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev)
+    rstd = torch.empty((2, N, H), dtype=torch.float32, device=dev)
+    HD = H * d
+    fa = dict(q=q, k=k, v=v, q_stride=HD, k_stride=HD, v_stride=HD, gains=gains, o=o, lse=lse,
+              q_hat=q_hat, k_hat=k_hat, rstd=rstd)
+    F = pam.FWD_STAGES
+    fwd = lambda st: (lambda: pam.mmdit_attn_fwd(pack.plan, pack.blob_dev, stages=st, **fa))
+    rec = {"workload": w.title, "tokens": N, "samples": len(text), "sum_L2": sl2}
+    clk = ClockSampler()
+    with clk:
+        t_pro, n_pro = time_stage(torch, fwd(F["prologue"]), flush)
+        t_att, n_att = time_stage(torch, fwd(F["attention"]))
+        if w.backward:
+            t_call, n_call = time_stage(torch, fwd(0), flush)
+        else:  # inference call: Q-hat / K-hat in the workspace, no rstd
+            fws = pack.workspace("fwd")
+            out_inf = dict(o=o, lse=lse)
+            call = lambda: pam.mmdit_attn_fwd(pack.plan, pack.blob_dev, q=q, k=k, v=v, q_stride=HD,
+                                              k_stride=HD, v_stride=HD, gains=gains,
+                                              workspace=fws, **out_inf)
+            t_call, n_call = time_stage(torch, call, flush)
+        fwd_flop = 4.0 * H * d * sl2
+        pro_bytes = 8.0 * N * H * d
+        rec["prologue_fwd"] = {"ms": round(t_pro, 4), "gbs": round(pro_bytes / t_pro / 1e6, 1),
+                               "frac_hbm": round(pro_bytes / t_pro / 1e6 / PEAK_HBM_GBS, 4),
+                               "reps": n_pro, "cache_flushed": True}
+        rec["attn_fwd"] = {"ms": round(t_att, 4), "tflops": round(fwd_flop / t_att / 1e9, 2),
+                           "frac": round(fwd_flop / t_att / 1e9 / PEAK_BF16_TFLOPS, 4), "reps": n_att}
+        rec["fwd_call"] = {"ms": round(t_call, 4), "reps": n_call, "cache_flushed": True,
+                           "saves_for_backward": bool(w.backward)}
+        if w.backward:
+            # the forward just ran: its outputs are the backward's inputs
+            torch.cuda.synchronize()
+            dq, dk, dv = torch.empty_like(o), torch.empty_like(o), torch.empty_like(o)
+            dgains = torch.empty((4, d), dtype=torch.float32, device=dev)
+            wsb = pack.workspace("bwd")
+            ba = dict(q=q, k=k, v=v, q_hat=q_hat, k_hat=k_hat, o=o, dout=do, q_stride=HD,
+                      k_stride=HD, v_stride=HD, dout_stride=HD, gains=gains, lse=lse, rstd=rstd,
+                      dq=dq, dk=dk, dv=dv, dgains=dgains, workspace=wsb)
+            B = pam.BWD_STAGES
+            bwd = lambda st: (lambda: pam.mmdit_attn_bwd(pack.plan, pack.blob_dev, stages=st, **ba))
+            t_dq, n_dq = time_stage(torch, bwd(B["dq"]))
+            t_kv, n_kv = time_stage(torch, bwd(B["dkdv"]))
+            t_gn, _ = time_stage(torch, bwd(B["gains"]))
+            t_bcall, n_bcall = time_stage(torch, bwd(0))
+            bwd_flop = 10.0 * H * d * sl2
+            t_b = t_dq + t_kv
+            rec["attn_bwd_dq"] = {"ms": round(t_dq, 4), "reps": n_dq}
+            rec["attn_bwd_dkdv"] = {"ms": round(t_kv, 4), "reps": n_kv,
+                                    "tflops_own_work": round(8.0 * H * d * sl2 / t_kv / 1e9, 2),
+                                    "frac_own_work": round(8.0 * H * d * sl2 / t_kv / 1e9 / PEAK_BF16_TFLOPS, 4)}
+            rec["gain_reduce"] = {"ms": round(t_gn, 4)}
+            rec["attn_bwd"] = {"ms": round(t_b, 4), "tflops": round(bwd_flop / t_b / 1e9, 2),
+                               "frac": round(bwd_flop / t_b / 1e9 / PEAK_BF16_TFLOPS, 4)}
+            rec["bwd_call"] = {"ms": round(t_bcall, 4), "reps": n_bcall}
+    rec["sclk_reported"] = clk.summary()
+    return rec
+
+
+def probes(pam, torch, dev):
+    """Measured context for the spec peaks: a dense bf16 matrix-instruction
+    loop (throughput and core clock under that load) and a 1 GiB device copy
+    (HBM bandwidth)."""
+    import ctypes as C
+    L = pam.lib()
+    L.mmdit_probe_mfma.restype = C.c_int
+    L.mmdit_probe_mfma.argtypes = [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
+    blocks, iters = 1024, 40000
+    clocks = torch.zeros((blocks, 4), dtype=torch.int64, device=dev)
+    sums = torch.zeros(blocks, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    run = lambda: L.mmdit_probe_mfma(blocks, iters, clocks.data_ptr(), sums.data_ptr(),
+                                     stream.cuda_stream)
+    assert run() == 0, pam.mmdit_last_error()
+    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        t, _ = time_stage(torch, run, min_reps=5, max_reps=10, target_s=0.1)
+    c = clocks.cpu().numpy().astype(np.float64)
+    ghz = (c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1) * 0.1
+    flop = blocks * 4.0 * iters * 8 * 32768
+    mfma = {"tflops": round(flop / t / 1e9, 1), "frac_of_spec": round(flop / t / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "core_clock_ghz": round(float(np.median(ghz)), 3), "sclk_reported": clk.summary(),
+            "kernel": "mmdit::mfma_loop_kernel", "launch": f"{blocks} x 256 threads, {iters} rounds"}
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    t_copy, _ = time_stage(torch, lambda: b.copy_(a), min_reps=20, max_reps=50, target_s=0.05)
+    copy = {"gbs": round(2.0 * (1 << 30) / t_copy / 1e6, 1),
+            "frac_of_spec": round(2.0 * (1 << 30) / t_copy / 1e6 / PEAK_HBM_GBS, 4),
+            "what": "torch copy_ of 1 GiB (read + write counted)"}
+    del a, b
+    return {"mfma_loop": mfma, "hbm_copy": copy}
 
 
 def pass_runner(pam, torch, dev, text, hs, ws, H, d, backward, seed, src=None):
@@ -128,23 +434,16 @@ def pass_runner(pam, torch, dev, text, hs, ws, H, d, backward, seed, src=None):
     return run
 
 
-def time_passes(torch, runs, reps=20):
-    """Milliseconds per round of the given callables run back to back."""
-    for _ in range(3):
+def time_passes(torch, runs, flush, min_reps=20):
+    """Median milliseconds of one round of the given callables run back to
+    back (HIP events around each round, the cache flushed before it)."""
+    def one():
         for r in runs:
             r()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        for r in runs:
-            r()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    return time_stage(torch, one, flush, min_reps=min_reps, max_reps=200, target_s=0.2)[0]
 
 
-def packed_cfg_1024(pam, torch, dev, H, d):
+def packed_cfg_1024(pam, torch, dev, H, d, flush):
     """Packed classifier-free guidance at 1024^2: the conditional sample
     (512 text tokens + 64x64 latents) and its unconditional twin (same grid,
     a null prompt) as one forward pass, against the two branches as two
@@ -155,14 +454,14 @@ def packed_cfg_1024(pam, torch, dev, H, d):
         packed = pass_runner(pam, torch, dev, t, h, w, H, d, False, 1)
         cond = pass_runner(pam, torch, dev, t[:1], h[:1], w[:1], H, d, False, 2)
         unc = pass_runner(pam, torch, dev, t[1:], h[1:], w[1:], H, d, False, 3)
-        t_packed = time_passes(torch, [packed], 50)
-        t_two = time_passes(torch, [cond, unc], 50)
+        t_packed = time_passes(torch, [packed], flush)
+        t_two = time_passes(torch, [cond, unc], flush)
         out[f"null_text_{null}"] = {"packed_ms": round(t_packed, 4), "two_passes_ms": round(t_two, 4),
                                     "speedup": round(t_two / t_packed, 3)}
     return out
 
 
-def edit_1024(pam, torch, dev):
+def edit_1024(pam, torch, dev, flush):
     """One 1024^2 editing step's attention core: 512 text tokens, the 64x64
     target latents and the 64x64 source latents on a second RoPE frame
     (8,704 tokens, H=24, d=128): whole forward call, and forward + backward."""
@@ -173,13 +472,13 @@ def edit_1024(pam, torch, dev):
     both = pass_runner(pam, torch, dev, t, hs, ws, w.heads, w.head_dim, True, 5, src)
     L = t[0] + hs[0] * ws[0] + src[0][0] * src[1][0]
     flop1 = w.heads * w.head_dim * float(L) ** 2
-    t_f = time_passes(torch, [fwd], 50)
-    t_fb = time_passes(torch, [both], 20)
+    t_f = time_passes(torch, [fwd], flush)
+    t_fb = time_passes(torch, [both], flush)
     return {"tokens": L, "fwd_ms": round(t_f, 4), "fwd_tflops": round(4 * flop1 / t_f / 1e9, 1),
             "fwd_bwd_ms": round(t_fb, 4), "fwd_bwd_tflops": round(14 * flop1 / t_fb / 1e9, 1)}
 
 
-def adaln_block(pam, torch, dev, inp, D):
+def adaln_block(pam, torch, dev, inp, D, flush):
     """adaLN modulation with the fused gated residual on the timed pack at
     model width D (= H * d): forward (x, y -> z, h, statistics) and backward
     (x, y, dh, dz -> dx, dy and the modulation gradients), bf16, inputs drawn
@@ -206,14 +505,14 @@ def adaln_block(pam, torch, dev, inp, D):
                             dz_stride=D, dx=dx, dy=dy, dshift=dsh, dscale=dsc, dgate=dg, workspace=ws)
     out = {"model_dim": D, "tokens": N}
     for name, fn, nbytes in (("fwd", fwd, 8 * N * D + 8 * N), ("bwd", bwd, 12 * N * D + 8 * N)):
-        ms = time_passes(torch, [fn], 50)
+        ms = time_passes(torch, [fn], flush, min_reps=50)
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[name] = {"us": round(ms * 1e3, 1), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
                      "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
     return out
 
 
-def bucket_padding(pam, torch, dev, inp, H, d):
+def bucket_padding(pam, torch, dev, inp, H, d, flush):
     """The same samples as dense per-bucket batches: one batch per distinct
     latent grid, every text padded to the longest prompt of the workload's
     range (512, or the longest drawn), padded tokens computed. Forward +
@@ -227,9 +526,9 @@ def bucket_padding(pam, torch, dev, inp, H, d):
     for j, ((hh, ww), n) in enumerate(sorted(buckets.items())):
         runs.append(pass_runner(pam, torch, dev, [text_pad] * n, [hh] * n, [ww] * n, H, d, True, 10 + j))
         padded_l2 += n * float(text_pad + hh * ww) ** 2
-    t_buckets = time_passes(torch, runs, 10)
+    t_buckets = time_passes(torch, runs, flush, min_reps=10)
     packed = pass_runner(pam, torch, dev, inp.text_len, inp.grid_h, inp.grid_w, H, d, True, 9)
-    packed_ms = time_passes(torch, [packed], 10)
+    packed_ms = time_passes(torch, [packed], flush, min_reps=10)
     return {"buckets": len(buckets), "text_padded_to": text_pad,
             "padded_flop_ratio": round(padded_l2 / sum_l2(inp), 3),
             "bucketed_ms": round(t_buckets, 4), "packed_ms": round(packed_ms, 4),
@@ -242,7 +541,13 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed6", choices=["mixed6", "gen2048", "small64"])
-    ap.add_argument("--cpu-heads", type=int, default=12)
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="heads of the headline pack the oracle is timed on")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-configuration stage timings")
+    ap.add_argument("--no-probes", action="store_true", help="skip the peak probes")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip packed CFG, editing, adaLN and bucket-padding fields")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bwd-mode", default="recompute", choices=["recompute", "stored_ds"],
                     help="backward mode of the timed step (stored_ds: dQ from the dS the "
@@ -330,11 +635,13 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, ev[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, ev[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    step_clock = clk.summary()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
     kt = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
@@ -361,34 +668,23 @@ def main():
     pro_bytes = 8.0 * N * H * d
     pro_gbs = pro_bytes / (kt["prologue_fwd"] * 1e-3) / 1e9
 
-    # ms/layer at 1024^2: the whole forward call (prologue + attention) on the
-    # 1024^2 generation pack (512 text + 64x64 latents, H=24, d=128).
-    g = workloads.draw("gen1024")
-    gpack = pam.Pack(g.text_len, g.grid_h, g.grid_w, g.heads, g.head_dim, "bf16", device=dev)
-    gq, gk, gv = up(g.q), up(g.k), up(g.v)
-    ggains = torch.from_numpy(g.gains).to(dev)
-    for _ in range(5):
-        pam.forward(gpack, gq, gk, gv, ggains, save_for_backward=False)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 50
-    gout = dict(o=torch.empty((g.num_tokens, g.heads, g.head_dim), dtype=bf, device=dev),
-                lse=torch.empty((g.heads, g.num_tokens), dtype=torch.float32, device=dev))
-    gws = gpack.workspace("fwd")
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        pam.mmdit_attn_fwd(gpack.plan, gpack.blob_dev, q=gq, k=gk, v=gv, q_stride=g.heads * g.head_dim,
-                           k_stride=g.heads * g.head_dim, v_stride=g.heads * g.head_dim,
-                           gains=ggains, workspace=gws, **gout)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_layer_1024 = e0.elapsed_time(e1) / reps
-    gen_fwd_tflops = 4.0 * g.heads * g.head_dim * sum_l2(g) / (ms_layer_1024 * 1e-3) / 1e12
+    # Every configuration's pack, stage by stage (c1 forward only): the
+    # prologue and the whole forward call cache-flushed, the attention kernels
+    # and backward stages back to back; then the probes of the achievable peaks.
+    flush = Flush(torch, dev)
+    per_config = {}
+    if not args.no_per_config:
+        for j, name in enumerate(["gen1024", "mixed6", "gen2048", "small64"]):
+            per_config[name] = measure_config(pam, torch, dev, name, flush, 100 + j)
+    peaks = probes(pam, torch, dev) if not args.no_probes else None
+    g1 = per_config.get("gen1024")
 
-    cfg = packed_cfg_1024(pam, torch, dev, H, d)
-    edit = edit_1024(pam, torch, dev)
-    adaln = adaln_block(pam, torch, dev, inp, H * d)
-    bucket = bucket_padding(pam, torch, dev, inp, H, d)
+    extras = {}
+    if not args.no_extras:
+        extras["packed_cfg_1024"] = packed_cfg_1024(pam, torch, dev, H, d, flush)
+        extras["edit_1024"] = edit_1024(pam, torch, dev, flush)
+        extras["adaln_gated_residual"] = adaln_block(pam, torch, dev, inp, H * d, flush)
+        extras["bucket_padding"] = bucket_padding(pam, torch, dev, inp, H, d, flush)
 
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -421,16 +717,16 @@ def main():
         "attn_bwd_frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
         "prologue_fwd_gbs": round(pro_gbs, 1),
         "prologue_fwd_frac_hbm": round(pro_gbs / PEAK_HBM_GBS, 4),
-        "ms_per_layer_1024": round(ms_layer_1024, 4),
-        "gen1024_fwd_tflops": round(gen_fwd_tflops, 2),
+        "ms_per_layer_1024": g1["fwd_call"]["ms"] if g1 else None,
+        "gen1024_fwd_tflops": round(4.0 * 24 * 128 * g1["sum_L2"] / g1["fwd_call"]["ms"] / 1e9, 2) if g1 else None,
         "roofline": roof,
-        "packed_cfg_1024": cfg,
-        "edit_1024": edit,
-        "adaln_gated_residual": adaln,
-        "bucket_padding": bucket,
+        "per_config": per_config,
+        "measured_peaks": peaks,
+        "sclk_reported_step": step_clock,
     }
+    result.update(extras)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_heads)
+        result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_heads)
     print(json.dumps(result), flush=True)
 
 

@@ -47,12 +47,18 @@
  *
  * Ownership and threading: the caller owns every buffer (host descriptor
  * arrays, the host plan blob, its device copy, tensors, workspace). The
- * library never allocates or frees device memory and never synchronises:
- * mmdit_attn_fwd / mmdit_attn_bwd only enqueue kernels on the caller's HIP
- * stream and return; buffers must stay alive until the stream passes them.
+ * library never allocates or frees device memory, and only
+ * mmdit_device_faults synchronises: mmdit_attn_fwd / mmdit_attn_bwd only
+ * enqueue kernels on the caller's HIP stream and return; buffers must stay
+ * alive until the stream passes them.
  * All entry points are reentrant. Errors: every argument is validated on the
  * host before anything is launched; on a non-OK return nothing was enqueued
  * and no output was touched, and mmdit_last_error() (thread-local) says why.
+ * The stream of a launching call (NULL = the default stream) must belong to
+ * the current device. On the device, every kernel first checks that the blob
+ * it was given is the plan's (its header fingerprint); a kernel given another
+ * pack's blob writes nothing and records MMDIT_DEVICE_FAULT_STALE_BLOB, which
+ * mmdit_device_faults reports after the work has run.
  */
 #ifndef MMDIT_H
 #define MMDIT_H
@@ -63,7 +69,7 @@
 extern "C" {
 #endif
 
-#define MMDIT_ABI_VERSION 4
+#define MMDIT_ABI_VERSION 5
 
 /* Largest accepted token stride, in elements (2^24). */
 #define MMDIT_MAX_ROW_STRIDE (1ll << 24)
@@ -145,10 +151,20 @@ typedef struct {
   uint64_t fingerprint;          /* hash of every field above; checked on each call */
 } mmdit_plan;
 
-/* Build the plan of one pack. host_blob == NULL: size query only (plan is
- * filled, plan->blob_bytes says how much host memory the blob needs). Runs on
- * the host, touches no device. Errors: INVALID_ARG, UNSUPPORTED (head_dim),
- * BUDGET, BUFFER_TOO_SMALL (host_blob_bytes < plan->blob_bytes). */
+/* Build the plan of one pack: the per-sample cumulative offsets (cu_seqlens)
+ * of the samples laid back to back without padding, every token's modality
+ * and (row, col), the work lists and the RoPE table (picx.dev "Mage-Flow: An
+ * Efficient Native-Resolution Foundation Model for Image Generation and
+ * Editing", section "Native-Resolution MMDiT (NR-MMDiT)", bullet
+ * "Native-resolution packing": variable-length sequences packed into one
+ * batch with per-sample cumulative offsets; findtube.ai transcript
+ * "Mage-Flow: Efficient Native-Resolution Image Generation and Editing" at
+ * [00:03:16] and [00:04:03]: one contiguous batch under a fixed token budget,
+ * 2D RoPE per sample from its own grid). host_blob == NULL: size query only
+ * (plan is filled, plan->blob_bytes says how much host memory the blob
+ * needs). Runs on the host, touches no device. Errors: INVALID_ARG,
+ * UNSUPPORTED (head_dim), BUDGET, BUFFER_TOO_SMALL (host_blob_bytes <
+ * plan->blob_bytes). */
 mmdit_status mmdit_pack_plan(const mmdit_pack_desc *desc, mmdit_plan *plan,
                              void *host_blob, uint64_t host_blob_bytes);
 
@@ -198,7 +214,8 @@ mmdit_status mmdit_cfg_pack_desc(const mmdit_pack_desc *cond, int32_t null_text_
                                          backward -> dk, dv, K gain partials (workspace) */
 #define MMDIT_STAGE_BWD_GAINS     4u  /* bwd: fixed-order sum of the gain partials -> dgains */
 #define MMDIT_STAGE_BWD_D         8u  /* bwd, stored-dS mode only: D = rowsum(dO * O) */
-#define MMDIT_STAGE_BWD_STORE_DS 16u  /* bwd mode flag: the stored-dS backward (see mmdit_attn_bwd) */
+#define MMDIT_STAGE_BWD_STORE_DS 16u  /* bwd mode flag: the stored-dS backward (see mmdit_attn_bwd);
+                                         alone (no stage bit) = all stages of that mode */
 
 typedef struct {
   const void *q, *k, *v;              /* [N][H][d] device, dtype; pre-norm */
@@ -212,8 +229,14 @@ typedef struct {
   uint32_t stages;                    /* 0 = all */
 } mmdit_fwd_args;
 
-/* Forward: o = per-sample softmax(q_hat k_hat^T / sqrt(d)) v with q_hat, k_hat
- * the normalised and rotated q, k. workspace may be NULL when q_hat and k_hat
+/* Forward: q_hat, k_hat = RoPE(RMSNorm_m(q, k) * gain_m) per modality m, then
+ * o = per-sample softmax(q_hat k_hat^T / sqrt(d)) v: joint text+image
+ * attention confined to each sample of the pack (picx.dev "Mage-Flow ...",
+ * section "Native-Resolution MMDiT (NR-MMDiT)": modality-specific
+ * normalisation before joint attention, FlashAttention over per-sample
+ * cumulative offsets; section "Training Infrastructure": RoPE and
+ * normalisation fused into the kernels; transcript at [00:03:16]: 2D RoPE
+ * of each image's own grid). workspace may be NULL when q_hat and k_hat
  * are given; else workspace_bytes >= plan->fwd_workspace_bytes. hip_stream is
  * a hipStream_t (NULL = the default stream). Deterministic: the same inputs
  * give bitwise the same outputs. */
@@ -234,7 +257,11 @@ typedef struct {
   uint32_t stages;                    /* 0 = all */
 } mmdit_bwd_args;
 
-/* Backward of mmdit_attn_fwd for the loss sum(dout * o). workspace_bytes >=
+/* Backward of mmdit_attn_fwd for the loss sum(dout * o): the gradients of the
+ * pre-norm q, k, v and of the four gain rows, what training through the
+ * attention of the pages needs (picx.dev "Mage-Flow ...", sections
+ * "Native-Resolution MMDiT (NR-MMDiT)" and "Training Infrastructure";
+ * transcript at [00:02:50] and [00:04:20]). workspace_bytes >=
  * plan->bwd_workspace_bytes. Workspace layout (fp32, each part 256-byte
  * aligned): D [H][N] at offset 0, then the Q and K gain-gradient partials;
  * fp32 plans also keep fp32 dQ-hat and dK-hat [N][H][d] after them. A stage
@@ -243,25 +270,38 @@ typedef struct {
  * recompute mode); DKDV needs k, dk, dv; both need q_hat, k_hat, v, dout,
  * lse, gains.
  * dQ is formed one of two ways, with equal results up to rounding order:
- *  - recompute: the DQ stage forms D, then S and dP again for each query
- *    tile, and dQ; stages in the order DQ, DKDV, GAINS;
- *  - stored dS (bf16 plans with bwd_ds_workspace_bytes > bwd_workspace_bytes,
- *    workspace_bytes >= plan->bwd_ds_workspace_bytes): stage D forms D, the
- *    DKDV stage also writes dS (bf16, 2 bytes per score of every sample and
- *    head) to the workspace past bwd_workspace_bytes (rounded up to 4 KiB),
- *    and the DQ stage multiplies it by K-hat; stages in the order D, DKDV,
- *    DQ, GAINS. Faster; the area takes ds_base[S] KiB, about
- *    2 * H * sum(L_i^2) bytes.
- * stages = 0 runs everything, in the stored-dS mode when the workspace is
- * large enough. Stage subsets select the stored-dS mode with
- * MMDIT_STAGE_BWD_STORE_DS in each call (UNSUPPORTED where the plan has no
- * such mode, BUFFER_TOO_SMALL without the room); stage D is only valid in
- * that mode.
+ *  - recompute (the default): the DQ stage forms D, then S and dP again for
+ *    each query tile, and dQ; stages in the order DQ, DKDV, GAINS;
+ *  - stored dS, selected only by MMDIT_STAGE_BWD_STORE_DS in stages (bf16
+ *    plans with bwd_ds_workspace_bytes > bwd_workspace_bytes; workspace_bytes
+ *    >= plan->bwd_ds_workspace_bytes): stage D forms D, the DKDV stage also
+ *    writes dS (bf16, 2 bytes per score of every sample and head) to the
+ *    workspace past bwd_workspace_bytes (rounded up to 4 KiB), and the DQ
+ *    stage multiplies it by K-hat; stages in the order D, DKDV, DQ, GAINS.
+ *    Measured within about 2% of the recompute mode on the mixed-resolution
+ *    pack; the area takes ds_base[S] KiB, about 2 * H * sum(L_i^2) bytes.
+ * stages = 0 runs every stage of the recompute mode, stages =
+ * MMDIT_STAGE_BWD_STORE_DS every stage of the stored-dS mode. The flag is
+ * UNSUPPORTED where the plan has no such mode and BUFFER_TOO_SMALL without
+ * the room; stage D is INVALID_ARG without it; and a stored-dS call that
+ * asks for both DQ and DKDV must include D (INVALID_ARG otherwise: the dK/dV
+ * kernel reads the D that stage D writes).
  * Deterministic: the same inputs and the same workspace size give bitwise
  * the same outputs (no atomics; fixed-order reductions). */
 mmdit_status mmdit_attn_bwd(const mmdit_plan *plan, const void *plan_blob_dev,
                             const mmdit_bwd_args *args, void *workspace,
                             uint64_t workspace_bytes, void *hip_stream);
+
+/* Device-side fault flags (see mmdit_device_faults). */
+#define MMDIT_DEVICE_FAULT_STALE_BLOB 1u  /* a kernel was given a device blob that is not the plan's */
+
+/* Read and clear the current device's fault word: *flags gets the OR of the
+ * MMDIT_DEVICE_FAULT_* flags that the library's kernels on this GPU recorded
+ * since the previous call (0 = none). The read is queued on hip_stream (NULL =
+ * default; it must belong to the current device) behind the work already
+ * queued there, and the call synchronises that stream: the only entry point
+ * that does. Errors: INVALID_ARG (flags NULL, stream of another device), HIP. */
+mmdit_status mmdit_device_faults(uint32_t *flags, void *hip_stream);
 
 /* Size of the per-GPU device array that mmdit_attn_bwd_noalloc uses as its
  * workspace (64 MiB): packs whose plan->bwd_workspace_bytes exceed it are

@@ -1,0 +1,35 @@
+/*
+ * mmdit_probe.h - measurement probe of libmmdit (context for the rooflines
+ * the benchmark reports; not part of the attention method or its ABI
+ * contract).
+ */
+#ifndef MMDIT_PROBE_H
+#define MMDIT_PROBE_H
+
+#include <stdint.h>
+
+#include "mmdit.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Launch `blocks` workgroups of 256 threads (4 waves) on hip_stream (NULL =
+ * default); every wave runs `iters` rounds of 8 independent bf16
+ * 32x32x16 matrix instructions (32,768 FLOP each) on register operands, so
+ * one launch does blocks * 4 * iters * 8 * 32768 FLOP. Thread 0 of workgroup
+ * b writes {core clock counter at its start, at its end, 100 MHz real-time
+ * counter at its start, at its end} to clocks[4b .. 4b+3] (device memory,
+ * uint64, 16-byte aligned, caller-owned); (end - start) of the first over the
+ * second, times 100 MHz, is the core clock the workgroup ran at. It also
+ * writes its wave 0's sum of the results to sums[b] (device float, so that
+ * the work cannot be optimised away). Enqueues only; errors: INVALID_ARG
+ * (blocks or iters < 1, clocks NULL or misaligned, sums NULL), HIP (launch
+ * failure). */
+mmdit_status mmdit_probe_mfma(int32_t blocks, int32_t iters, uint64_t *clocks, float *sums,
+                              void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MMDIT_PROBE_H */

@@ -21,16 +21,17 @@ __all__ = [
     "MmditError", "lib", "mmdit_pack_plan", "mmdit_pack_plan_edit", "mmdit_attn_fwd",
     "mmdit_attn_bwd", "mmdit_attn_bwd_noalloc", "mmdit_cfg_pack_desc", "mmdit_adaln_fwd", "mmdit_adaln_bwd",
     "adaln_forward", "adaln_backward",
-    "mmdit_status_str", "mmdit_last_error", "mmdit_abi_version", "Pack",
+    "mmdit_status_str", "mmdit_last_error", "mmdit_abi_version", "mmdit_device_faults", "Pack",
     "forward", "backward", "FWD_STAGES", "BWD_STAGES", "LIB_PATH",
 ]
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmmdit.so")
 
 MMDIT_F32, MMDIT_BF16 = 0, 1
 STAGE_PROLOGUE, STAGE_ATTENTION = 1, 2
 STAGE_BWD_DQ, STAGE_BWD_DKDV, STAGE_BWD_GAINS, STAGE_BWD_D, STAGE_BWD_STORE_DS = 1, 2, 4, 8, 16
+DEVICE_FAULT_STALE_BLOB = 1
 FWD_STAGES = {"prologue": STAGE_PROLOGUE, "attention": STAGE_ATTENTION}
 BWD_STAGES = {"dq": STAGE_BWD_DQ, "dkdv": STAGE_BWD_DKDV, "gains": STAGE_BWD_GAINS,
               "d": STAGE_BWD_D, "store_ds": STAGE_BWD_STORE_DS}
@@ -43,7 +44,8 @@ class PackDesc(C.Structure):
                 ("rope_theta", C.c_float), ("rms_eps", C.c_float), ("token_budget", C.c_int64)]
 
 
-# Largest workspace Pack.workspace("bwd") takes for the stored-dS backward.
+# Largest workspace Pack.workspace("bwd_ds") (the stored-dS backward's) allocates
+# unless told otherwise.
 DS_WORKSPACE_LIMIT = 16 << 30
 
 
@@ -147,6 +149,8 @@ def lib():
         L.mmdit_last_error.argtypes = []
         L.mmdit_abi_version.restype = C.c_int32
         L.mmdit_abi_version.argtypes = []
+        L.mmdit_device_faults.restype = C.c_int
+        L.mmdit_device_faults.argtypes = [C.POINTER(C.c_uint32), C.c_void_p]
         if L.mmdit_abi_version() != ABI_VERSION:
             raise ImportError("libmmdit ABI version mismatch")
         _lib = L
@@ -163,6 +167,14 @@ def mmdit_last_error() -> str:
 
 def mmdit_abi_version() -> int:
     return int(lib().mmdit_abi_version())
+
+
+def mmdit_device_faults(stream=None) -> int:
+    """Read and clear this GPU's fault word (synchronises the stream): the OR
+    of the DEVICE_FAULT_* flags the kernels recorded since the last read."""
+    out = C.c_uint32(0)
+    _check(lib().mmdit_device_faults(C.byref(out), _stream(stream)))
+    return int(out.value)
 
 
 def _check(status: int):
@@ -250,6 +262,21 @@ def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _on_stream(stream):
+    """Context for the conveniences below: with `stream` (a torch stream or a
+    raw hipStream_t handle) made current, every buffer they allocate (outputs
+    and the workspace they drop on return) belongs to the stream the kernels
+    run on, so torch's caching allocator cannot hand it to other work while
+    the kernels still use it."""
+    import contextlib
+    import torch
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
 
 
 def mmdit_attn_fwd(plan: Plan, blob_dev, *, q=None, k=None, v=None, q_stride=0, k_stride=0,
@@ -377,7 +404,14 @@ class Pack:
 
 
 def forward(pack: Pack, q, k, v, gains, *, save_for_backward: bool = True, stream=None):
-    """O (and lse, q_hat, k_hat, rstd when saving for the backward)."""
+    """O (and lse, q_hat, k_hat, rstd when saving for the backward). With
+    `stream`, outputs and workspace are allocated on it and the kernels run on
+    it."""
+    with _on_stream(stream):
+        return _forward(pack, q, k, v, gains, save_for_backward)
+
+
+def _forward(pack, q, k, v, gains, save_for_backward):
     import torch
     N, H, d = pack.N, pack.H, pack.d
     qs = _token_stride(q, N, H, d, "q")
@@ -398,18 +432,30 @@ def forward(pack: Pack, q, k, v, gains, *, save_for_backward: bool = True, strea
         rstd = torch.empty((2, N, H), dtype=torch.float32, device=dev)
         mmdit_attn_fwd(pack.plan, pack.blob_dev, q=q, k=k, v=v, q_stride=qs, k_stride=ks,
                        v_stride=vs, gains=gains, o=o, lse=lse, q_hat=q_hat, k_hat=k_hat,
-                       rstd=rstd, stream=stream)
+                       rstd=rstd)
         out.update(q_hat=q_hat, k_hat=k_hat, rstd=rstd)
     else:
         ws = pack.workspace("fwd")
         mmdit_attn_fwd(pack.plan, pack.blob_dev, q=q, k=k, v=v, q_stride=qs, k_stride=ks,
-                       v_stride=vs, gains=gains, o=o, lse=lse, workspace=ws, stream=stream)
+                       v_stride=vs, gains=gains, o=o, lse=lse, workspace=ws)
     return out
 
 
-def backward(pack: Pack, q, k, v, gains, saved: dict, dout, *, workspace=None, stream=None):
-    """dq, dk, dv (w.r.t. the pre-norm inputs) and dgains for loss sum(dout * o)."""
+def backward(pack: Pack, q, k, v, gains, saved: dict, dout, *, workspace=None,
+             mode: str = "recompute", stream=None):
+    """dq, dk, dv (w.r.t. the pre-norm inputs) and dgains for loss sum(dout * o).
+    mode "recompute" (dQ with S and dP formed again) or "stored_ds" (dQ from
+    the dS the dK/dV kernel stores; needs Pack.workspace("bwd_ds")); the
+    workspace defaults to the mode's. With `stream`, outputs and workspace are
+    allocated on it and the kernels run on it."""
+    with _on_stream(stream):
+        return _backward(pack, q, k, v, gains, saved, dout, workspace, mode)
+
+
+def _backward(pack, q, k, v, gains, saved, dout, workspace, mode):
     import torch
+    if mode not in ("recompute", "stored_ds"):
+        raise ValueError(f"unknown backward mode {mode!r}")
     N, H, d = pack.N, pack.H, pack.d
     qs = _token_stride(q, N, H, d, "q")
     ks = _token_stride(k, N, H, d, "k")
@@ -422,12 +468,13 @@ def backward(pack: Pack, q, k, v, gains, saved: dict, dout, *, workspace=None, s
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
     dgains = torch.empty((4, d), dtype=torch.float32, device=dev)
-    ws = pack.workspace("bwd") if workspace is None else workspace
+    ds = mode == "stored_ds"
+    ws = pack.workspace("bwd_ds" if ds else "bwd") if workspace is None else workspace
     mmdit_attn_bwd(pack.plan, pack.blob_dev, q=q, k=k, v=v, q_hat=saved["q_hat"],
                    k_hat=saved["k_hat"], o=saved["o"], dout=dout, q_stride=qs, k_stride=ks,
                    v_stride=vs, dout_stride=gs, gains=gains, lse=saved["lse"],
                    rstd=saved.get("rstd"), dq=dq, dk=dk, dv=dv, dgains=dgains, workspace=ws,
-                   stream=stream)
+                   stages=STAGE_BWD_STORE_DS if ds else 0)
     return dict(dq=dq, dk=dk, dv=dv, dgains=dgains, workspace=ws)
 
 
@@ -440,7 +487,13 @@ def _rows_stride(t, N, name):
 def adaln_forward(pack: Pack, x, shift, scale, *, y=None, gate=None, eps: float = 1e-6,
                   save_stats: bool = True, stream=None):
     """h = adaLN(z) with z = x (+ gate * y); returns dict with h, z (with y)
-    and stats ([N, 2] mean and rstd, when saved)."""
+    and stats ([N, 2] mean and rstd, when saved). With `stream`, outputs are
+    allocated on it and the kernels run on it."""
+    with _on_stream(stream):
+        return _adaln_forward(pack, x, shift, scale, y, gate, eps, save_stats)
+
+
+def _adaln_forward(pack, x, shift, scale, y, gate, eps, save_stats):
     import torch
     N, D = pack.N, int(x.shape[-1])
     xs = _rows_stride(x, N, "x")
@@ -449,8 +502,7 @@ def adaln_forward(pack: Pack, x, shift, scale, *, y=None, gate=None, eps: float 
     z = None if y is None else torch.empty_like(h)
     stats = torch.empty((N, 2), dtype=torch.float32, device=x.device) if save_stats else None
     mmdit_adaln_fwd(pack.plan, pack.blob_dev, x=x, y=y, x_stride=xs, y_stride=ys, shift=shift,
-                    scale=scale, gate=gate, model_dim=D, eps=eps, z=z, h=h, stats=stats,
-                    stream=stream)
+                    scale=scale, gate=gate, model_dim=D, eps=eps, z=z, h=h, stats=stats)
     out = dict(h=h)
     if z is not None:
         out["z"] = z
@@ -461,7 +513,14 @@ def adaln_forward(pack: Pack, x, shift, scale, *, y=None, gate=None, eps: float 
 
 def adaln_backward(pack: Pack, x, scale, dh, *, y=None, gate=None, dz=None, stats=None,
                    eps: float = 1e-6, workspace=None, stream=None):
-    """dx (= dz_total), dy, dshift, dscale, dgate of ``adaln_forward``."""
+    """dx (= dz_total), dy, dshift, dscale, dgate of ``adaln_forward``. With
+    `stream`, outputs and workspace are allocated on it and the kernels run on
+    it."""
+    with _on_stream(stream):
+        return _adaln_backward(pack, x, scale, dh, y, gate, dz, stats, eps, workspace)
+
+
+def _adaln_backward(pack, x, scale, dh, y, gate, dz, stats, eps, workspace):
     import torch
     N, D = pack.N, int(x.shape[-1])
     S = pack.plan.num_samples
@@ -476,7 +535,7 @@ def adaln_backward(pack: Pack, x, scale, dh, *, y=None, gate=None, dz=None, stat
                     model_dim=D, eps=eps, stats=stats, dh=dh, dz=dz,
                     dh_stride=_rows_stride(dh, N, "dh"),
                     dz_stride=0 if dz is None else _rows_stride(dz, N, "dz"), dx=dx, dy=dy,
-                    dshift=dshift, dscale=dscale, dgate=dgate, workspace=ws, stream=stream)
+                    dshift=dshift, dscale=dscale, dgate=dgate, workspace=ws)
     out = dict(dx=dx, dshift=dshift, dscale=dscale)
     if y is not None:
         out.update(dy=dy, dgate=dgate)

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmmdit.so")
 
 SOURCES = ["plan.cpp", "api.cpp", "prologue.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_f32.hip",
-           "adaln.hip", "noalloc.hip"]
+           "adaln.hip", "noalloc.hip", "probe.hip", "status.hip"]
 ARCH = "gfx950"
 
 

@@ -162,6 +162,7 @@ __device__ __forceinline__ void row_stats(const float (&z)[RB][G][4], const bool
 // pieces only add workgroups in flight.
 template <typename T, int G, bool RES>
 __global__ __launch_bounds__(kThreads) void adaln_fwd_kernel(PlanDev p, AdalnFwdArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   constexpr int RB = 2;
   typedef typename Quad<T>::raw raw;
   __shared__ float red[2][64];
@@ -246,6 +247,7 @@ __global__ __launch_bounds__(kThreads) void adaln_fwd_kernel(PlanDev p, AdalnFwd
 // Backward, also one row ahead (x, y, dh and dz of row k+1 in flight).
 template <typename T, int G, bool RES>
 __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwdArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   constexpr int RB = 1;
   typedef typename Quad<T>::raw raw;
   __shared__ float red[2][64];
@@ -389,8 +391,10 @@ __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwd
 // 2 dgate). Wave w adds chunks c0 + w, c0 + w + 4, ... of the range for its
 // block's 64 columns; the four wave sums are then added in wave order. The
 // split depends only on the plan, so the result is the same on every run.
-__global__ __launch_bounds__(256) void adaln_reduce_kernel(const int32_t *ranges, const float *part, int D,
-                                                           float *o0, float *o1, float *o2) {
+__global__ __launch_bounds__(256) void adaln_reduce_kernel(BlobGuard guard, const int32_t *ranges,
+                                                           const float *part, int D, float *o0, float *o1,
+                                                           float *o2) {
+  if (blob_stale(guard)) return;  // another pack's blob: touch nothing
   __shared__ float red[4][64];
   const int nxb = (D + 63) / 64;
   const int r = blockIdx.x / nxb, k = blockIdx.y;
@@ -487,8 +491,8 @@ hipError_t launch_adaln_bwd(int dtype, const PlanDev &p, const AdalnBwdArgs &a, 
 hipError_t launch_adaln_reduce(const PlanDev &p, const float *partials, int dim, float *out0, float *out1,
                                float *out2, hipStream_t stream) {
   const dim3 grid((unsigned)((dim + 63) / 64) * 2u * (unsigned)p.num_samples, out2 ? 3 : 2);
-  hipLaunchKernelGGL(adaln_reduce_kernel, grid, dim3(256), 0, stream, p.mod_ranges, partials, dim, out0, out1,
-                     out2);
+  hipLaunchKernelGGL(adaln_reduce_kernel, grid, dim3(256), 0, stream, p.guard, p.mod_ranges, partials, dim,
+                     out0, out1, out2);
   return hipGetLastError();
 }
 

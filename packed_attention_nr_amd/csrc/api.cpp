@@ -2,6 +2,7 @@
 // launches on the caller's stream. Nothing is launched unless every check
 // passes; no device memory is allocated, freed or synchronised here.
 #include <cmath>
+#include <cstddef>
 #include <cstdio>
 #include <string>
 #include <vector>
@@ -78,9 +79,11 @@ static mmdit_status check_ptr(const char *name, const void *p) {
   return MMDIT_OK;
 }
 
-static PlanDev plan_dev(const mmdit_plan &p, const void *blob) {
+static PlanDev plan_dev(const mmdit_plan &p, const void *blob, uint32_t *fault_word) {
   const char *b = static_cast<const char *>(blob);
   PlanDev d;
+  d.guard = BlobGuard{reinterpret_cast<const uint64_t *>(b + offsetof(BlobHeader, fingerprint)), p.fingerprint,
+                      fault_word};
   d.cu_seqlens = reinterpret_cast<const int32_t *>(b + p.off_cu_seqlens);
   d.tok_meta = reinterpret_cast<const int32_t *>(b + p.off_tok_meta);
   d.fwd_items = reinterpret_cast<const int4 *>(b + p.off_fwd_items);
@@ -165,8 +168,10 @@ static mmdit_status attn_fwd(const mmdit_plan *plan, const void *blob, const mmd
     }
   }
   if ((st = check_aliasing(spans))) return st;
+  uint32_t *fault = nullptr;
+  if ((st = device_fault_word(stream, &fault))) return st;
 
-  const PlanDev pd = plan_dev(*plan, blob);
+  const PlanDev pd = plan_dev(*plan, blob, fault);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (pro) {
     PrologueFwdArgs pa{a->q, a->k, a->q_stride, a->k_stride, a->gains, qh, kh, a->rstd};
@@ -200,22 +205,21 @@ mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmdit_bwd_
                 (unsigned long long)plan->bwd_workspace_bytes, (unsigned long long)ws_bytes);
   const BwdLayout wl = bwd_layout(*plan);
   const bool has_ds = wl.ds_total > wl.total;  // the plan offers the stored-dS mode
-  uint32_t stages = a->stages;
-  bool store_ds;
-  if (!stages) {  // everything; stored dS when the workspace has room for it
-    store_ds = has_ds && ws_bytes >= wl.ds_total;
-    stages = all | (store_ds ? MMDIT_STAGE_BWD_D : 0u);
-  } else {
-    store_ds = stages & MMDIT_STAGE_BWD_STORE_DS;
-    if (store_ds && !has_ds)
-      return fail(MMDIT_ERR_UNSUPPORTED, "this plan has no stored-dS backward (fp32, or a sample over %d tokens)",
-                  kDsMaxSeqlen);
-    if (store_ds && ws_bytes < wl.ds_total)
-      return fail(MMDIT_ERR_BUFFER_TOO_SMALL, "stored-dS backward workspace needs %llu bytes, got %llu",
-                  (unsigned long long)wl.ds_total, (unsigned long long)ws_bytes);
-    if ((stages & MMDIT_STAGE_BWD_D) && !store_ds)
-      return fail(MMDIT_ERR_INVALID_ARG, "stage D belongs to the stored-dS backward (the DQ stage forms D otherwise)");
-  }
+  // The mode comes from the flag alone; no stage bit = every stage of it.
+  const bool store_ds = a->stages & MMDIT_STAGE_BWD_STORE_DS;
+  uint32_t stages = a->stages & ~MMDIT_STAGE_BWD_STORE_DS;
+  if (store_ds && !has_ds)
+    return fail(MMDIT_ERR_UNSUPPORTED, "this plan has no stored-dS backward (fp32, or a sample over %d tokens)",
+                kDsMaxSeqlen);
+  if (store_ds && ws_bytes < wl.ds_total)
+    return fail(MMDIT_ERR_BUFFER_TOO_SMALL, "stored-dS backward workspace needs %llu bytes, got %llu",
+                (unsigned long long)wl.ds_total, (unsigned long long)ws_bytes);
+  if (!stages) stages = all | (store_ds ? MMDIT_STAGE_BWD_D : 0u);
+  if ((stages & MMDIT_STAGE_BWD_D) && !store_ds)
+    return fail(MMDIT_ERR_INVALID_ARG, "stage D belongs to the stored-dS backward (the DQ stage forms D otherwise)");
+  if (store_ds && (stages & MMDIT_STAGE_BWD_DQ) && (stages & MMDIT_STAGE_BWD_DKDV) && !(stages & MMDIT_STAGE_BWD_D))
+    return fail(MMDIT_ERR_INVALID_ARG,
+                "a stored-dS call with both DQ and DKDV must include stage D (the dK/dV kernel reads its D)");
   const bool sd = stages & MMDIT_STAGE_BWD_D, sdq = stages & MMDIT_STAGE_BWD_DQ,
              skv = stages & MMDIT_STAGE_BWD_DKDV, sgn = stages & MMDIT_STAGE_BWD_GAINS;
   char *w = static_cast<char *>(ws);
@@ -272,8 +276,10 @@ mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmdit_bwd_
     spans.push_back(span("dgains", a->dgains, 4, d, d, 4, true));
   }
   if ((st = check_aliasing(spans))) return st;
+  uint32_t *fault = nullptr;
+  if ((st = device_fault_word(stream, &fault))) return st;
 
-  const PlanDev pd = plan_dev(*plan, blob);
+  const PlanDev pd = plan_dev(*plan, blob, fault);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float scale = (float)(1.0 / std::sqrt((double)d));
   AttnBwdArgs ba{a->q_hat, a->k_hat, a->v, a->dout, a->o, a->v_stride, a->dout_stride, a->lse,
@@ -307,7 +313,7 @@ mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmdit_bwd_
     if (e != hipSuccess) return hip_fail("attention backward (dK, dV)", e);
   }
   if (sgn && a->dgains) {
-    hipError_t e = launch_gain_reduce(part_q, wl.nq, part_k, wl.nk, (int)d, a->dgains, s);
+    hipError_t e = launch_gain_reduce(pd.guard, part_q, wl.nq, part_k, wl.nk, (int)d, a->dgains, s);
     if (e != hipSuccess) return hip_fail("gain-gradient reduction", e);
   }
   return MMDIT_OK;
@@ -362,7 +368,9 @@ static mmdit_status adaln_fwd(const mmdit_plan *plan, const void *blob, const mm
     spans.push_back(span("stats", a->stats, N, 2, 2, 4, true));
   }
   if ((st = check_aliasing(spans))) return st;
-  const PlanDev pd = plan_dev(*plan, blob);
+  uint32_t *fault = nullptr;
+  if ((st = device_fault_word(stream, &fault))) return st;
+  const PlanDev pd = plan_dev(*plan, blob, fault);
   AdalnFwdArgs fa{a->x, a->y, a->x_stride, a->y_stride, a->shift, a->scale, a->gate, a->z, a->h,
                   reinterpret_cast<float2 *>(a->stats), a->model_dim, a->eps};
   hipError_t e = launch_adaln_fwd(plan->dtype, pd, fa, static_cast<hipStream_t>(stream));
@@ -419,7 +427,9 @@ static mmdit_status adaln_bwd(const mmdit_plan *plan, const void *blob, const mm
     spans.push_back(span("stats", a->stats, N, 2, 2, 4, false));
   }
   if ((st = check_aliasing(spans))) return st;
-  const PlanDev pd = plan_dev(*plan, blob);
+  uint32_t *fault = nullptr;
+  if ((st = device_fault_word(stream, &fault))) return st;
+  const PlanDev pd = plan_dev(*plan, blob, fault);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float *part = static_cast<float *>(ws);
   AdalnBwdArgs ba{a->x, a->y, a->dh, a->dz, a->x_stride, a->y_stride, a->dh_stride, a->dz_stride,

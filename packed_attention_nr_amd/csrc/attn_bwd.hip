@@ -214,6 +214,7 @@ __device__ __forceinline__ void sum_wave_partials(const float *red, int nw, floa
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p, AttnBwdArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   using namespace bwd;
   constexpr int NT = 64 * NWQ;        // threads
   constexpr int KS = D / 16;
@@ -430,6 +431,7 @@ __device__ __forceinline__ bf16x8 ds_frag(const char *sw, int t, int lane) {
 
 template <int D>
 __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_ds_kernel(PlanDev p, AttnBwdArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   using namespace bwd;
   constexpr int DB = D / 32;
   constexpr int TK = DQS_TK;
@@ -589,6 +591,7 @@ constexpr int KV_NS = 4;   // Q-hat / dO ring stages
 
 template <int D, bool DS>
 __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanDev p, AttnBwdArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   using namespace bwd;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;

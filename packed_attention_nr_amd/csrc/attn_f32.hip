@@ -25,6 +25,7 @@ static_assert(f32k::ROWS == kFwdTileF32 && f32k::ROWS == kBwdTile, "fp32 kernels
 
 template <int D>
 __global__ __launch_bounds__(512) void attn_fwd_f32_kernel(PlanDev p, AttnFwdArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   using namespace f32k;
   constexpr int DC = D / TPR;
   __shared__ float ks[ST][D], vs[ST][D];
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(512) void attn_fwd_f32_kernel(PlanDev p, AttnFwdArg
 // dK-hat and dV: 4 lanes per key, looping over the segment's queries.
 template <int D>
 __global__ __launch_bounds__(512) void attn_bwd_kv_f32_kernel(PlanDev p, AttnBwdArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   using namespace f32k;
   constexpr int DC = D / TPR;
   __shared__ float qs[ST][D], gs[ST][D], ls[ST], ds_[ST];
@@ -165,6 +167,7 @@ __global__ __launch_bounds__(512) void attn_bwd_kv_f32_kernel(PlanDev p, AttnBwd
 // dQ-hat: 4 lanes per query, looping over the segment's keys.
 template <int D>
 __global__ __launch_bounds__(512) void attn_bwd_q_f32_kernel(PlanDev p, AttnBwdArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   using namespace f32k;
   constexpr int DC = D / TPR;
   __shared__ float ks[ST][D], vs[ST][D];

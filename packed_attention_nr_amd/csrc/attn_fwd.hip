@@ -52,6 +52,7 @@ static_assert(fwd::BM == kFwdTileBf16, "forward tile must match the plan");
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFwdArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   using namespace fwd;
   constexpr int KS = D / 16;       // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T

@@ -15,7 +15,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace mmdit {
+
+// True when the device blob is not the one the host plan describes (its
+// header fingerprint differs): thread 0 flags it in the fault word and the
+// caller exits before touching anything else. The fingerprint is read first,
+// on its own, so no work-list entry of a foreign blob is ever read.
+__device__ __forceinline__ bool blob_stale(const BlobGuard &g) {
+  const uint64_t f = *g.blob_fingerprint;
+  if (__builtin_expect(f == g.fingerprint, 1)) return false;
+  if (threadIdx.x == 0) atomicOr(g.status, (uint32_t)MMDIT_DEVICE_FAULT_STALE_BLOB);
+  return true;
+}
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

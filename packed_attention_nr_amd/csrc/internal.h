@@ -81,6 +81,21 @@ mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmdit_bwd_
 // ---------------------------------------------------------------------------
 // Kernel launch arguments (device pointers; plain data passed by value).
 // ---------------------------------------------------------------------------
+// Check of the device blob against the host plan that every kernel makes
+// before it reads anything else of the blob or writes anything: the blob
+// header's fingerprint must equal the plan's. A kernel that finds otherwise
+// ORs MMDIT_DEVICE_FAULT_STALE_BLOB into *status (this device's fault word,
+// see mmdit_device_faults) and exits.
+struct BlobGuard {
+  const uint64_t *blob_fingerprint;  // the fingerprint word of the device blob's header
+  uint64_t fingerprint;              // the host plan's
+  uint32_t *status;                  // the device's fault word
+};
+
+// The current device's fault word, after checking that `stream` (NULL =
+// the default stream) belongs to the current device.
+mmdit_status device_fault_word(void *stream, uint32_t **word);
+
 struct PlanDev {
   const int32_t *cu_seqlens;   // [S+1]
   const int32_t *tok_meta;     // [N]
@@ -97,6 +112,7 @@ struct PlanDev {
   int32_t num_mod_chunks;
   float rms_eps;
   const int64_t *ds_base;      // [S+1] first dS block of each sample (all heads)
+  BlobGuard guard;
 };
 
 struct PrologueFwdArgs {
@@ -200,7 +216,7 @@ hipError_t launch_adaln_bwd(int dtype, const PlanDev &p, const AdalnBwdArgs &a, 
 // for k = 0 (dshift), 1 (dscale), 2 (dgate, skipped when out2 is nullptr).
 hipError_t launch_adaln_reduce(const PlanDev &p, const float *partials, int dim, float *out0,
                                float *out1, float *out2, hipStream_t stream);
-hipError_t launch_gain_reduce(const float *part_q, int nq, const float *part_k, int nk, int d,
-                              float *dgains, hipStream_t stream);
+hipError_t launch_gain_reduce(const BlobGuard &guard, const float *part_q, int nq, const float *part_k,
+                              int nk, int d, float *dgains, hipStream_t stream);
 
 }  // namespace mmdit

@@ -76,6 +76,7 @@ __device__ __forceinline__ void rope_lane(float *x, const float2 *rope, int e0, 
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prologue_fwd_kernel(PlanDev p, PrologueFwdArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   constexpr int VEC = Vec<T>::N;
   constexpr int LPR = D / VEC;
   constexpr int RPB = 256 / LPR;
@@ -127,6 +128,7 @@ __global__ __launch_bounds__(256) void prologue_fwd_kernel(PlanDev p, PrologueFw
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(PlanDev p, BwdPreArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   constexpr int VEC = Vec<T>::N;
   constexpr int LPR = D / VEC;
   constexpr int RPB = 256 / LPR;
@@ -159,6 +161,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PlanDev p, BwdPreArgs a) {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prologue_bwd_kernel(PlanDev p, PrologueBwdArgs a) {
+  if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
   constexpr int VEC = Vec<T>::N;
   constexpr int LPR = D / VEC;
   constexpr int RPB = 256 / LPR;
@@ -236,8 +239,9 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(PlanDev p, PrologueBw
 // for m = 2, 3 over b < nk of part_k[b][m-2][e]. Workgroup (m, 64-column
 // chunk): wave w sums blocks w, w+16, ... in order, then the 16 wave sums are
 // added in order -- the same result on every run.
-__global__ __launch_bounds__(1024) void gain_reduce_kernel(const float *part_q, int nq, const float *part_k,
-                                                           int nk, int d, float *dgains) {
+__global__ __launch_bounds__(1024) void gain_reduce_kernel(BlobGuard guard, const float *part_q, int nq,
+                                                           const float *part_k, int nk, int d, float *dgains) {
+  if (blob_stale(guard)) return;  // the partials came from another pack's blob: write nothing
   __shared__ float red[16][64];
   const int m = blockIdx.x / (d / 64);
   const int e = (blockIdx.x % (d / 64)) * 64 + (threadIdx.x & 63);
@@ -314,10 +318,10 @@ hipError_t launch_prologue_bwd(int dtype, const PlanDev &p, const PrologueBwdArg
                                hipStream_t stream) {
   MMDIT_DISPATCH(prologue_bwd_t, p, a, stream);
 }
-hipError_t launch_gain_reduce(const float *part_q, int nq, const float *part_k, int nk, int d,
-                              float *dgains, hipStream_t stream) {
+hipError_t launch_gain_reduce(const BlobGuard &guard, const float *part_q, int nq, const float *part_k,
+                              int nk, int d, float *dgains, hipStream_t stream) {
   if (d % 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gain_reduce_kernel, dim3(4 * (d / 64)), dim3(1024), 0, stream, part_q, nq, part_k,
+  hipLaunchKernelGGL(gain_reduce_kernel, dim3(4 * (d / 64)), dim3(1024), 0, stream, guard, part_q, nq, part_k,
                      nk, d, dgains);
   return hipGetLastError();
 }

@@ -59,11 +59,10 @@ def host(t):
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def run_gpu(inp, backward=True, device="cuda", bwd_workspace="bwd"):
+def run_gpu(inp, backward=True, device="cuda", bwd_mode="recompute"):
     """Forward (and backward) through the binding. Returns numpy fp64 arrays.
-    bwd_workspace: a Pack.workspace kind: "bwd" (the default choice),
-    "bwd_ds" (dQ from the stored dS) or "bwd_recompute" (dQ with S and dP
-    recomputed)."""
+    bwd_mode: "recompute" (dQ with S and dP formed again, the default) or
+    "stored_ds" (dQ from the dS the dK/dV kernel stores)."""
     import packed_attention_nr_amd as pam
     import torch
     pack = pam.Pack(inp.text_len, inp.grid_h, inp.grid_w, inp.heads, inp.head_dim,
@@ -73,8 +72,7 @@ def run_gpu(inp, backward=True, device="cuda", bwd_workspace="bwd"):
     saved = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"])
     out = {k: host(v) for k, v in saved.items()}
     if backward and inp.dout is not None:
-        g = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], saved, t["dout"],
-                         workspace=pack.workspace(bwd_workspace))
+        g = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], saved, t["dout"], mode=bwd_mode)
         out.update({k: host(v) for k, v in g.items() if k != "workspace"})
     torch.cuda.synchronize()
     out["lse"] = out["lse"].T            # [N, H] like the oracle

@@ -74,19 +74,19 @@ def test_edge_packs(case, d, dtype):
     _compare(inp, run_gpu(inp), run_oracle(inp))
 
 
-@pytest.mark.parametrize("mode", ["bwd_recompute", "bwd_ds"])
+@pytest.mark.parametrize("mode", ["recompute", "stored_ds"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("case", ["one_token_samples", "exact_tiles", "ragged_multi_tile", "wide_4to1"])
 def test_backward_modes(case, d, mode):
     """Both bf16 backward modes at both head sizes: dQ with S and dP formed
-    again per query tile (a workspace too small for dS), and dQ from the dS
-    that the dK/dV kernel stores. (The other cases take the default
-    workspace: recompute.)"""
+    again per query tile (the default), and dQ from the dS that the dK/dV
+    kernel stores (selected by the stored-dS flag). The other cases run the
+    default."""
     spec = EDGE_PACKS[case]
     inp = workloads.random_pack(40 + sorted(EDGE_PACKS).index(case), heads=3, head_dim=d, dtype="bf16",
                                 text=spec["text"], grids=spec["grids"])
     _say(f"backward {mode} {case} d={d} N={inp.num_tokens}")
-    _compare(inp, run_gpu(inp, bwd_workspace=mode), run_oracle(inp))
+    _compare(inp, run_gpu(inp, bwd_mode=mode), run_oracle(inp))
 
 
 def test_stored_ds_stage_calls_match_one_call():
@@ -101,8 +101,7 @@ def test_stored_ds_stage_calls_match_one_call():
     assert pack.plan.bwd_ds_workspace_bytes > pack.plan.bwd_workspace_bytes
     t = to_device(inp)
     saved = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"])
-    one = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], saved, t["dout"],
-                       workspace=pack.workspace("bwd_ds"))
+    one = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], saved, t["dout"], mode="stored_ds")
     N, H, d = pack.N, pack.H, pack.d
     out = {n: torch.empty_like(one[n]) for n in ("dq", "dk", "dv", "dgains")}
     ws = pack.workspace("bwd_ds")
@@ -273,20 +272,38 @@ FULL = [("gen1024", [0, 11, 23]), ("mixed6", [0, 13]), ("gen2048", [5]), ("small
         ("edit1024", [0, 17])]
 
 
-@pytest.mark.parametrize("name,heads", [("mixed6", [5, 19]), ("edit1024", [7])], ids=["mixed6", "edit1024"])
+STORED_DS_FULL = [("mixed6", [5, 19]), ("edit1024", [7]), ("small64", [3, 20]), ("gen2048", [11])]
+
+
+@pytest.mark.parametrize("name,heads", STORED_DS_FULL, ids=[c[0] for c in STORED_DS_FULL])
 def test_full_workload_stored_ds(name, heads):
-    """The stored-dS backward at full size (the mixed-resolution training
-    pack: 3.6 GiB of dS), against the oracle on sampled heads, and the
-    recompute backward's dV bit for bit (dV does not depend on D, which the two
-    modes sum in different orders; the kernel differs only in also storing
-    dS)."""
+    """The stored-dS backward at full size against the oracle on sampled heads:
+    the mixed-resolution pack (3.6 GiB of dS), the editing step, the 64-segment
+    pack (4.1 GiB: per-(sample, head) areas at byte offsets past 4 GiB, 64
+    samples of area bases) and the 2048^2 sample (12.8 GiB: one 16,896-token
+    segment, the largest dS area per head). The gain gradients through a
+    head-subset run in the same mode, whose per-head outputs must equal the
+    full run's bit for bit; and the recompute backward's dV bit for bit (dV
+    does not depend on D, which the two modes sum in different orders; the
+    kernel differs only in also storing dS)."""
     inp = workloads.draw(name)
     _say(f"{name} stored dS: N={inp.num_tokens} H={inp.heads} heads checked={heads}")
-    gpu = run_gpu(inp, bwd_workspace="bwd_ds")
+    gpu = run_gpu(inp, bwd_mode="stored_ds")
     ref = run_oracle(inp, heads=heads)
     _compare(inp, gpu, ref, heads=heads)
-    rec = run_gpu(inp, bwd_workspace="bwd_recompute")
-    assert np.array_equal(gpu["dv"], rec["dv"])
+    sub = run_gpu(subset_heads(inp, heads), bwd_mode="stored_ds")
+    fails = []
+    _, msg = check("dgains (checked heads only)", sub["dgains"], ref["dgains"], inp.dtype,
+                   l2_only=True, failures=fails)
+    _say("   " + msg)
+    for k in ("o", "dq", "dk", "dv"):
+        if not np.array_equal(sub[k], gpu[k][:, heads]):
+            fails.append(f"{k} differs between the full and the head-subset run")
+    del sub
+    rec = run_gpu(inp, bwd_mode="recompute")
+    if not np.array_equal(gpu["dv"], rec["dv"]):
+        fails.append("dv differs from the recompute backward's")
+    assert not fails, fails
 
 
 @pytest.mark.parametrize("name,heads", FULL, ids=[f[0] for f in FULL])

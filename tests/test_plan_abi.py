@@ -24,12 +24,15 @@ def L():
 
 
 def test_exports_every_header_symbol(L):
-    hdr = open(os.path.join(ROOT, "include", "mmdit.h")).read()
-    names = set(re.findall(r"\b(mmdit_[a-z_]+)\s*\(", hdr))
-    assert {"mmdit_pack_plan", "mmdit_attn_fwd", "mmdit_attn_bwd"} <= names
+    import glob
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        names |= set(re.findall(r"\b(mmdit_[a-z_]+)\s*\(", open(h).read()))
+    assert {"mmdit_pack_plan", "mmdit_attn_fwd", "mmdit_attn_bwd", "mmdit_attn_bwd_noalloc",
+            "mmdit_device_faults", "mmdit_probe_mfma"} <= names
     for n in sorted(names):
         assert hasattr(L, n), n
-    assert pam.mmdit_abi_version() == pam.ABI_VERSION == 4
+    assert pam.mmdit_abi_version() == pam.ABI_VERSION == 5
     assert pam.mmdit_status_str(0) == "ok"
 
 
@@ -370,6 +373,8 @@ def _bwd(plan, ws_bytes=None, **kw):
     (dict(stages=8 | 16), 3),             # stored-dS mode without room for dS
     (dict(stages=8 | 16, o=None, ws_bytes=1 << 20), 1),     # stage D reads o
     (dict(stages=8 | 16, dout=None, ws_bytes=1 << 20), 1),  # ... and dout
+    (dict(stages=1 | 2 | 16, ws_bytes=1 << 20), 1),   # stored dS: DQ and DKDV need D in the call
+    (dict(stages=1 | 2 | 4 | 16, ws_bytes=1 << 20), 1),
     (dict(ws_bytes=64), 3),
     (dict(stages=1, q=None), 1),          # the dQ stage writes dq from q
     (dict(stages=1, o=None), 1),          # ... and forms D from o

@@ -29,7 +29,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "draw", "bf16_round", "bf16_bits",
-    "random_pack", "Inputs", "draw_adaln",
+    "random_pack", "Inputs", "draw_adaln", "geometry",
 ]
 
 
@@ -184,6 +184,20 @@ def draw(w: Workload | str, seed: int = 0, backward: Optional[bool] = None) -> I
     bw = w.backward if backward is None else backward
     return _finish(rng, text, hs, ws, w.heads, w.head_dim, w.dtype, bw,
                    w.rope_theta, w.rms_eps, w.src)
+
+
+def geometry(w: Workload | str, seed: int = 0):
+    """Pack geometry of a named workload without drawing its tensors: (text
+    lengths, grids, source grids or None), the text lengths being the first
+    draw of ``draw``'s stream (so they equal the ones ``draw`` makes)."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    if w.text is None:
+        lo, hi = w.text_range
+        text = np.random.default_rng(seed).integers(lo, hi + 1, len(w.grids))
+    else:
+        text = np.asarray(w.text)
+    return [int(t) for t in text], list(w.grids), None if w.src is None else list(w.src)
 
 
 def draw_adaln(seed: int, num_tokens: int, num_samples: int, dim: int, dtype: str = "bf16",
