@@ -29,6 +29,13 @@ extern "C" {
 mmdit_status mmdit_probe_mfma(int32_t blocks, int32_t iters, uint64_t *clocks, float *sums,
                               void *hip_stream);
 
+/* Copy `bytes` (a multiple of 16) from src to dst (device, 16-byte aligned,
+ * not overlapping) with `blocks` workgroups of 256 threads, each thread
+ * moving four 16-byte words per grid-stride step with non-temporal loads and
+ * stores: the HBM bandwidth of a plain streaming kernel. Enqueues only;
+ * errors: INVALID_ARG, HIP. */
+mmdit_status mmdit_probe_copy(const void *src, void *dst, uint64_t bytes, int32_t blocks, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

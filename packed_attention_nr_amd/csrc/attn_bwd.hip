@@ -75,73 +75,102 @@ static_assert(bwd::QT == kFwdTileBf16 && bwd::KT == kBwdTile, "backward tiles mu
 // the dense output. Writes dx (bf16) for a valid row and
 // leaves in red[m * D + d] (m = 0 text, 1 image) this wave's sums of
 // rho*dy*x over its 32 tokens (invalid rows add nothing).
-template <int D, typename XA>
-__device__ __forceinline__ void prologue_bwd_rows(const f32x16 (&acc)[D / 32], float scale, int32_t meta,
+// The pre-norm row's loads are issued before any arithmetic; the gradient
+// row is transformed in place (dX-hat -> dy -> gain terms), the pre-norm row
+// stays in bf16 and the RoPE entries are fetched per 16-pair block, so the
+// step keeps few registers live and the compiler need not spill.
+// B0, NB: the register blocks this wave finishes (d in [32 B0, 32 (B0 + NB))).
+// With XCH, another wave finishes the other blocks of the same rows: the two
+// exchange their partial row sums through xch (slots self and partner of
+// 128 floats; every wave of the workgroup passes the barrier inside), adding
+// them in a fixed order (the partial of the wave with first = true first), so
+// both get bitwise the same sums.
+template <int D, int B0, int NB, bool XCH, typename XA>
+__device__ __forceinline__ void prologue_bwd_rows(f32x16 (&acc)[D / 32], float scale, int32_t meta,
                                                   float rho, bool valid, const XA &xa, const float *g2,
                                                   const float2 *rope, int fp, float eps, bf16 *dx, int64_t out,
-                                                  float *red, int lane) {
+                                                  float *red, int lane, float *xch = nullptr, int self = 0,
+                                                  int partner = 0, bool first = true) {
   constexpr int DB = D / 32;
+  static_assert(B0 >= 0 && NB >= 1 && B0 + NB <= DB, "block range");
   const int lq = lane & 31, g = lane >> 5;
   bool img;
   int row, col, frame;
   tok_pos(meta, img, row, col, frame);
-  const float *gm = g2 + (img ? D : 0);
-  float dy[DB][16], xv[DB][16];
+  // The pre-norm row is loaded first (it stays in bf16); then, block by
+  // block, the RoPE entries of the block's pairs and the inverse rotation
+  // in place. Lane pairs (d, d+1) of register block b are pairs
+  // 16b + 4(k/2) + 2g + k%2, k = 0..7: two consecutive pairs per k/2, in one
+  // RoPE section (section boundaries are multiples of 4 pairs), so each k/2
+  // is one 16-byte load.
+  bf16x4 x4[DB][4];
 #pragma unroll
-  for (int b = 0; b < DB; ++b)
+  for (int b = B0; b < B0 + NB; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dy[b][i] = acc[b][i] * scale;
-  if (img) {  // inverse rotation of the pairs (d, d+1), d even
-    float2 cs[DB][8];
-    const int re = fp + (D / 2 - fp) / 2;
+    for (int r4 = 0; r4 < 4; ++r4) x4[b][r4] = xa(32 * b + 8 * r4 + 4 * g);
+  const int re = fp + (D / 2 - fp) / 2;
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+  for (int b = B0; b < B0 + NB; ++b) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int pair = 16 * b + 4 * (k >> 1) + 2 * g + (k & 1);
-        cs[b][k] = rope[rope_pos(pair, fp, re, row, col, frame) * (D / 2) + pair];
+    for (int i = 0; i < 16; ++i) acc[b][i] *= scale;
+    if (img) {
+      f32x4 cs[4];  // {cos, sin} of two consecutive pairs
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const int pair = 16 * b + 4 * k2 + 2 * g;
+        cs[k2] = *reinterpret_cast<const f32x4 *>(rope + rope_pos(pair, fp, re, row, col, frame) * (D / 2) + pair);
       }
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int i0 = 2 * k;
-        const float u = dy[b][i0], w = dy[b][i0 + 1];
-        dy[b][i0] = u * cs[b][k].x + w * cs[b][k].y;
-        dy[b][i0 + 1] = w * cs[b][k].x - u * cs[b][k].y;
-      }
-  }
-  float ss = 0.f, dot = 0.f;
-#pragma unroll
-  for (int b = 0; b < DB; ++b)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d0 = 32 * b + 8 * r4 + 4 * g;
-      const bf16x4 x4 = xa(d0);
-      const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gm + d0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * r4 + j;
-        xv[b][i] = (float)x4[j];
-        ss = fmaf(xv[b][i], xv[b][i], ss);
-        dot = fmaf(g4[j] * dy[b][i], xv[b][i], dot);
+        const float c = cs[k >> 1][2 * (k & 1)], sn = cs[k >> 1][2 * (k & 1) + 1];
+        const float u = acc[b][2 * k], w = acc[b][2 * k + 1];
+        acc[b][2 * k] = u * c + w * sn;
+        acc[b][2 * k + 1] = w * c - u * sn;
       }
     }
+  }
+  // Two passes over the row: row sums first, then outputs.
+  const float *gm = g2 + (img ? D : 0);
+  float ss = 0.f, dot = 0.f;
+#pragma unroll
+  for (int b = B0; b < B0 + NB; ++b) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gm + 32 * b + 8 * r4 + 4 * g);
+      const bf16x4 xb = x4[b][r4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = (float)xb[j];
+        ss = fmaf(x, x, ss);
+        dot = fmaf(g4[j] * acc[b][4 * r4 + j], x, dot);
+      }
+    }
+  }
+  if constexpr (XCH) {
+    xch[self * 128 + 2 * lane] = ss;
+    xch[self * 128 + 2 * lane + 1] = dot;
+    __syncthreads();
+    const float ss_p = xch[partner * 128 + 2 * lane], dot_p = xch[partner * 128 + 2 * lane + 1];
+    ss = first ? ss + ss_p : ss_p + ss;
+    dot = first ? dot + dot_p : dot_p + dot;
+  }
   if (rho < 0.f) rho = rsqrtf(half_sum(ss) * (1.0f / D) + eps);
   dot = half_sum(dot);
   const float c3 = rho * rho * rho * dot * (1.0f / D);
 #pragma unroll
-  for (int b = 0; b < DB; ++b)
+  for (int b = B0; b < B0 + NB; ++b) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d0 = 32 * b + 8 * r4 + 4 * g;
       const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gm + d0);
+      const bf16x4 xb = x4[b][r4];
       float o[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * r4 + j;
-        o[j] = rho * g4[j] * dy[b][i] - c3 * xv[b][i];
-        dy[b][i] = valid ? rho * dy[b][i] * xv[b][i] : 0.f;  // gain-gradient term
+        const float x = (float)xb[j];
+        o[j] = rho * g4[j] * acc[b][i] - c3 * x;
+        acc[b][i] = valid ? rho * acc[b][i] * x : 0.f;  // gain-gradient term
       }
       if (valid) {
         const bf16x2 t0 = pack2(o[0], o[1]), t1 = pack2(o[2], o[3]);
@@ -150,41 +179,27 @@ __device__ __forceinline__ void prologue_bwd_rows(const f32x16 (&acc)[D / 32], f
         *reinterpret_cast<bf16x4 *>(dx + out + d0) = o4;
       }
     }
+  }
   // Sum the gain terms over the wave's 32 tokens (lanes lq = 0..31 of each
-  // half) by recursive halving: step k pairs lanes lq and lq ^ 2^k, and each
-  // keeps the half of its current values selected by bit k of lq. After five
-  // steps value s of lane lq is the sum for index j = 2*rev5(lq) + s, where
-  // j = 16b + i names d = 32b + acc_row(i, g). A wave whose valid tokens are
-  // all of one modality reduces once; a mixed wave once per modality.
+  // half): for each register, DPP sums inside each 16-lane row, then one
+  // shuffle across lane bit 4, so every lane ends with the sums of all its
+  // registers; lane lq = i % 16 writes register i's. A wave whose valid
+  // tokens are all of one modality reduces once; a mixed wave once per
+  // modality.
   const uint64_t has_img = __ballot(valid && img), has_txt = __ballot(valid && !img);
-  const int rev = ((lq & 1) << 4) | ((lq & 2) << 2) | (lq & 4) | ((lq & 8) >> 2) | ((lq & 16) >> 4);
   auto reduce_into = [&](int m, bool select, bool want_img) __attribute__((always_inline)) {
-    float v[64];
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int b = B0; b < B0 + NB; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[16 * b + i] = (!select || img == want_img) ? dy[b][i] : 0.f;
-#pragma unroll
-    for (int i = 16 * DB; i < 64; ++i) v[i] = 0.f;
-#pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      const int half = 32 >> k;
-      const bool up = (lq >> k) & 1;
-#pragma unroll
-      for (int j = 0; j < half; ++j) {
-        const float keep = up ? v[j + half] : v[j];
-        const float send = up ? v[j] : v[j + half];
-        v[j] = keep + __shfl_xor(send, 1 << k);
+      for (int i = 0; i < 16; ++i) {
+        float v = (!select || img == want_img) ? acc[b][i] : 0.f;
+        v = group_sum<16>(v);
+        v += __shfl_xor(v, 16);
+        if (lq == i) red[m * D + 32 * b + acc_row(i, g)] = v;
       }
-    }
-#pragma unroll
-    for (int sidx = 0; sidx < 2; ++sidx) {
-      const int j = 2 * rev + sidx;
-      if (j < 16 * DB) red[m * D + 32 * (j >> 4) + acc_row(j & 15, g)] = v[sidx];
-    }
   };
   auto zero_row = [&](int m) __attribute__((always_inline)) {
-    for (int e = lane; e < D; e += 64) red[m * D + e] = 0.f;
+    for (int e = 32 * B0 + lane; e < 32 * (B0 + NB); e += 64) red[m * D + e] = 0.f;
   };
   if (has_img && has_txt) {
     reduce_into(0, true, false);
@@ -253,35 +268,6 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
   // This lane's query: Q-hat and dO rows as B operands (d = 16s + 8g + 0..7).
   const int qi = q0 + wave * 32 + lq;
   const int qc = min(qi, seg1 - 1);
-  // Epilogue inputs, fetched now: the wave's pre-norm q rows into LDS, the Q
-  // gains, this query's token word and rstd.
-  {
-    TileLoader<D, SWZ_ROWS, 32, 1> xload;
-    xload.init(0, lane, a.q_stride);
-    xload.issue(x_s + wave * 32 * D, static_cast<const bf16 *>(a.q) + h * D, q0 + wave * 32, seg1 - 1);
-  }
-  if (tid < 2 * D) g_s[tid] = a.gains[tid];
-  const int32_t meta = p.tok_meta[qc];
-  const float rho0 = a.rstd ? a.rstd[(int64_t)qc * H + h] : -1.f;
-  bf16x8 qf[KS], gf[KS];
-  float dlt = 0.f;
-  {
-    const bf16 *qs = qh + (int64_t)qc * HD + h * D + 8 * g;
-    const bf16 *gs = go + (int64_t)qc * a.dout_stride + h * D + 8 * g;
-    const bf16 *os = oo + (int64_t)qc * HD + h * D + 8 * g;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      qf[s] = ld_bf16x8(qs + 16 * s);
-      gf[s] = ld_bf16x8(gs + 16 * s);
-      const bf16x8 of = ld_bf16x8(os + 16 * s);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dlt = fmaf((float)gf[s][j], (float)of[j], dlt);
-    }
-    dlt = half_sum(dlt);
-  }
-  if (g == 0 && qi < seg1) a.delta[(int64_t)h * N + qi] = dlt;
-  const float lse2 = a.lse[(int64_t)h * N + qc] * kLog2e;
-
   // K/V tile staging: thread tid moves 16-byte chunk c8 of rows r0 + RSTEP*c;
   // rows clamped only in the segment's last tile.
   constexpr int RSTEP = NT / (D / 8);
@@ -315,6 +301,38 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
     }
   };
 
+  // Every start-up load is issued before the first wait: K/V tile 0, then the
+  // epilogue's inputs, then this lane's rows.
+  load_tile(seg0);
+  // Epilogue inputs, fetched now: the wave's pre-norm q rows into LDS, the Q
+  // gains, this query's token word and rstd.
+  {
+    TileLoader<D, SWZ_ROWS, 32, 1> xload;
+    xload.init(0, lane, a.q_stride);
+    xload.issue(x_s + wave * 32 * D, static_cast<const bf16 *>(a.q) + h * D, q0 + wave * 32, seg1 - 1);
+  }
+  if (tid < 2 * D) g_s[tid] = a.gains[tid];
+  const int32_t meta = p.tok_meta[qc];
+  const float rho0 = a.rstd ? a.rstd[(int64_t)qc * H + h] : -1.f;
+  const float lse2 = a.lse[(int64_t)h * N + qc] * kLog2e;
+  bf16x8 qf[KS], gf[KS];
+  float dlt = 0.f;
+  {
+    const bf16 *qs = qh + (int64_t)qc * HD + h * D + 8 * g;
+    const bf16 *gs = go + (int64_t)qc * a.dout_stride + h * D + 8 * g;
+    const bf16 *os = oo + (int64_t)qc * HD + h * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qf[s] = ld_bf16x8(qs + 16 * s);
+      gf[s] = ld_bf16x8(gs + 16 * s);
+      const bf16x8 of = ld_bf16x8(os + 16 * s);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dlt = fmaf((float)gf[s][j], (float)of[j], dlt);
+    }
+    dlt = half_sum(dlt);
+  }
+  if (g == 0 && qi < seg1) a.delta[(int64_t)h * N + qi] = dlt;
+
   f32x16 dq[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
@@ -322,7 +340,6 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
     for (int i = 0; i < 16; ++i) dq[b][i] = 0.f;
 
   const int ntiles = (seg1 - seg0 + BN - 1) / BN;
-  load_tile(seg0);
   store_tile(0);
   __syncthreads();
 
@@ -381,7 +398,7 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
   auto xa = [&](int d0) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x4 *>(xt + swz_off<D, SWZ_ROWS>(lq, d0));
   };
-  prologue_bwd_rows<D>(dq, a.scale, meta, rho0, qi < seg1, xa, g_s, p.rope, p.rope_frame_pairs, p.rms_eps,
+  prologue_bwd_rows<D, 0, D / 32, false>(dq, a.scale, meta, rho0, qi < seg1, xa, g_s, p.rope, p.rope_frame_pairs, p.rms_eps,
                        static_cast<bf16 *>(a.dq), ((int64_t)qc * H + h) * D, red + wave * 2 * D, lane);
   __syncthreads();
   sum_wave_partials<D>(red, NWQ, part, tid);
@@ -549,7 +566,7 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_ds_kernel(PlanDe
   auto xa = [&](int d0) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x4 *>(xg + d0);
   };
-  prologue_bwd_rows<D>(dq, a.scale, meta, rho0, qi < seg1, xa, g_s, p.rope, p.rope_frame_pairs, p.rms_eps,
+  prologue_bwd_rows<D, 0, D / 32, false>(dq, a.scale, meta, rho0, qi < seg1, xa, g_s, p.rope, p.rope_frame_pairs, p.rms_eps,
                        static_cast<bf16 *>(a.dq), ((int64_t)qc * H + h) * D, red + wave * 2 * D, lane);
   __syncthreads();
   sum_wave_partials<D>(red, NWQ, part, tid);
@@ -663,11 +680,10 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   const bool key_ok = kr < seg1;
   const int kc = min(kr, seg1 - 1);
   bf16x8 kv[KS];
-  // Epilogue inputs of the dS/dK waves, fetched now: K gains, this key's
-  // token word and rstd.
+  // Epilogue inputs, fetched now: K gains, this key's token word and rstd.
   if (tid < 2 * D) g_s[tid] = a.gains[2 * D + tid];
-  const int32_t meta = role ? p.tok_meta[kc] : 0;
-  const float rho0 = (role && a.rstd) ? a.rstd[((int64_t)N + kc) * H + h] : -1.f;
+  const int32_t meta = p.tok_meta[kc];
+  const float rho0 = a.rstd ? a.rstd[((int64_t)N + kc) * H + h] : -1.f;
   {
     const bf16 *src = role == 0 ? static_cast<const bf16 *>(a.k_hat) + (int64_t)kc * HD + h * D
                                 : static_cast<const bf16 *>(a.v) + (int64_t)kc * a.v_stride + h * D;
@@ -875,11 +891,20 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   }
 
   wait_vmem();  // no load into LDS may outlive the workgroup
+  __syncthreads();  // ... nor reach the ring once it is reused below
 
-  // Rows of this lane's key: register i of block b is d = 32b + acc_row(i, g).
-  // The P buffer is free after the loop's last barrier; it holds the dS/dK
-  // waves' gain partials.
+  // Epilogue. Rows of this lane's key: register i of block b is d = 32b +
+  // acc_row(i, g). The ring and the P buffer are free from here. Each dS/dK wave hands the dK-hat of register blocks DB/2 .. DB-1
+  // to its P/dV partner (the same keys) through ring stage 0, and the two
+  // finish the prologue backward of the key rows on half of the head
+  // dimension each, exchanging partial row sums through ring stage 1; so the
+  // P/dV waves, otherwise idle here, take half of the work and each wave
+  // needs half the registers. The P buffer holds the gain partials.
+  constexpr int HB = DB / 2;
+  static_assert(4 * HB * 16 * 64 * 4 <= STAGE * 2 && 8 * 128 * 4 <= STAGE * 2, "hand-over fits a stage");
   float *red = reinterpret_cast<float *>(p_s);
+  float *hand = reinterpret_cast<float *>(st0);  // [sub][HB * 16][64 lanes]
+  float *xch = reinterpret_cast<float *>(st1);   // [role * 4 + sub][128]
   if (role == 0) {
     if (key_ok) {
       bf16 *dvp = static_cast<bf16 *>(a.dv) + (int64_t)kr * HD + h * D;
@@ -895,13 +920,30 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
         }
     }
   } else {
-    const bf16 *xg = static_cast<const bf16 *>(a.k) + (int64_t)kc * a.k_stride + h * D;
-    auto xa = [&](int d0) __attribute__((always_inline)) {
-      return *reinterpret_cast<const bf16x4 *>(xg + d0);
-    };
-    prologue_bwd_rows<D>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope, p.rope_frame_pairs, p.rms_eps,
-                         static_cast<bf16 *>(a.dk), ((int64_t)kc * H + h) * D, red + sub * 2 * D, lane);
+#pragma unroll
+    for (int b = HB; b < DB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) hand[((sub * HB + (b - HB)) * 16 + i) * 64 + lane] = acc[b][i];
   }
+  __syncthreads();
+  if (role == 0) {
+#pragma unroll
+    for (int b = HB; b < DB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[b][i] = hand[((sub * HB + (b - HB)) * 16 + i) * 64 + lane];
+  }
+  const bf16 *xg = static_cast<const bf16 *>(a.k) + (int64_t)kc * a.k_stride + h * D;
+  auto xa = [&](int d0) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x4 *>(xg + d0);
+  };
+  bf16 *dkp = static_cast<bf16 *>(a.dk);
+  const int64_t out = ((int64_t)kc * H + h) * D;
+  if (role == 1)
+    prologue_bwd_rows<D, 0, HB, true>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope, p.rope_frame_pairs,
+                                      p.rms_eps, dkp, out, red + sub * 2 * D, lane, xch, 4 + sub, sub, true);
+  else
+    prologue_bwd_rows<D, HB, HB, true>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope, p.rope_frame_pairs,
+                                       p.rms_eps, dkp, out, red + sub * 2 * D, lane, xch, sub, 4 + sub, false);
   __syncthreads();
   sum_wave_partials<D>(red, KV_NW / 2, part, tid);
 }

@@ -1,6 +1,7 @@
-// Measurement probe (context for the rooflines, not part of the method): a
+// Measurement probes (context for the rooflines, not part of the method): a
 // dense loop of bf16 matrix instructions that gives the throughput the chip
-// sustains on them and its core clock under that load.
+// sustains on them and its core clock under that load, and a streaming copy
+// that gives the HBM bandwidth a plain read-once / write-once kernel reaches.
 //
 // Every wave runs `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16
 // (32,768 FLOP each) on register operands, so nothing but the matrix pipes
@@ -49,7 +50,39 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, uint64_t *clo
   }
 }
 
+// Streaming copy: each thread moves four 16-byte words per step, all four
+// loads issued before the stores, grid-stride over the buffer; n16 = number
+// of 16-byte words.
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4 *src, u32x4 *dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x; i < n16; i += stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + 256 * u < n16) v[u] = __builtin_nontemporal_load(src + i + 256 * u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + 256 * u < n16) __builtin_nontemporal_store(v[u], dst + i + 256 * u);
+  }
+}
+
 }  // namespace mmdit
+
+extern "C" mmdit_status mmdit_probe_copy(const void *src, void *dst, uint64_t bytes, int32_t blocks,
+                                         void *hip_stream) {
+  mmdit::clear_error();
+  if (!src || !dst || (reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(dst) & 15u) ||
+      bytes % 16 || blocks < 1)
+    return mmdit::fail(MMDIT_ERR_INVALID_ARG,
+                       "src and dst must be 16-byte aligned device pointers, bytes a multiple of 16, blocks >= 1");
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return mmdit::fail(MMDIT_ERR_INVALID_ARG, "src and dst overlap");
+  hipLaunchKernelGGL(mmdit::copy_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(hip_stream),
+                     static_cast<const mmdit::u32x4 *>(src), static_cast<mmdit::u32x4 *>(dst), (int64_t)(bytes / 16));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return mmdit::fail(MMDIT_ERR_HIP, "probe launch failed: %s", hipGetErrorString(e));
+  return MMDIT_OK;
+}
 
 extern "C" mmdit_status mmdit_probe_mfma(int32_t blocks, int32_t iters, uint64_t *clocks, float *sums,
                                          void *hip_stream) {
