@@ -301,37 +301,68 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
     }
   };
 
-  // Every start-up load is issued before the first wait: K/V tile 0, then the
-  // epilogue's inputs, then this lane's rows.
+  // Start-up: every load is issued before the first wait, and the wave's 32
+  // rows of Q-hat, dO and O are read whole (16 lanes per 256-byte row) rather
+  // than lane by lane: Q-hat and dO by direct load into LDS (Q-hat where the
+  // pre-norm rows go later, dO in the K/V buffers, both free until the first
+  // tile is staged), O into registers. Lanes then take their B operands from
+  // LDS, and D = rowsum(dO * O) is formed in the row-wide layout and handed to
+  // the query's lanes through LDS.
+  static_assert(4 * 32 * D <= 2 * BN * LDV && 4 * 32 * D <= 2 * BN * LDK, "dO staging fits the K/V buffers");
+  bf16 *q_stage = x_s + wave * 32 * D;
+  bf16 *g_stage = (wave < 4 ? &k_s[0][0] : &v_s[0][0]) + (wave & 3) * 32 * D;
   load_tile(seg0);
-  // Epilogue inputs, fetched now: the wave's pre-norm q rows into LDS, the Q
-  // gains, this query's token word and rstd.
   {
-    TileLoader<D, SWZ_ROWS, 32, 1> xload;
-    xload.init(0, lane, a.q_stride);
-    xload.issue(x_s + wave * 32 * D, static_cast<const bf16 *>(a.q) + h * D, q0 + wave * 32, seg1 - 1);
+    TileLoader<D, SWZ_ROWS, 32, 1> qload, gload;
+    qload.init(0, lane, HD);
+    gload.init(0, lane, a.dout_stride);
+    qload.issue(q_stage, qh + h * D, q0 + wave * 32, seg1 - 1);
+    gload.issue(g_stage, go + h * D, q0 + wave * 32, seg1 - 1);
   }
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;     // rows per wave-wide instruction
+  constexpr int OJ = 32 / RPI;      // instructions for the wave's 32 rows
+  const int orow = lane / CPR, ochunk = lane % CPR;
+  uint4 oreg[OJ];
+#pragma unroll
+  for (int j = 0; j < OJ; ++j) {
+    const int row = min(q0 + wave * 32 + RPI * j + orow, seg1 - 1);
+    oreg[j] = ld16(oo + (int64_t)row * HD + h * D + 8 * ochunk);
+  }
+  // Epilogue inputs: the Q gains, this query's token word and rstd.
   if (tid < 2 * D) g_s[tid] = a.gains[tid];
   const int32_t meta = p.tok_meta[qc];
   const float rho0 = a.rstd ? a.rstd[(int64_t)qc * H + h] : -1.f;
   const float lse2 = a.lse[(int64_t)h * N + qc] * kLog2e;
+  wait_vmem();  // this wave's rows are in LDS and registers
   bf16x8 qf[KS], gf[KS];
-  float dlt = 0.f;
-  {
-    const bf16 *qs = qh + (int64_t)qc * HD + h * D + 8 * g;
-    const bf16 *gs = go + (int64_t)qc * a.dout_stride + h * D + 8 * g;
-    const bf16 *os = oo + (int64_t)qc * HD + h * D + 8 * g;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      qf[s] = ld_bf16x8(qs + 16 * s);
-      gf[s] = ld_bf16x8(gs + 16 * s);
-      const bf16x8 of = ld_bf16x8(os + 16 * s);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dlt = fmaf((float)gf[s][j], (float)of[j], dlt);
-    }
-    dlt = half_sum(dlt);
+  for (int s = 0; s < KS; ++s) {
+    qf[s] = ld_bf16x8(q_stage + swz_off<D, SWZ_ROWS>(lq, 16 * s + 8 * g));
+    gf[s] = ld_bf16x8(g_stage + swz_off<D, SWZ_ROWS>(lq, 16 * s + 8 * g));
   }
+  float *dl = red + wave * 32;  // D of the wave's rows
+#pragma unroll
+  for (int j = 0; j < OJ; ++j) {
+    const int r = RPI * j + orow;
+    const bf16x8 gv = ld_bf16x8(g_stage + swz_off<D, SWZ_ROWS>(r, 8 * ochunk));
+    const bf16x8 ov = __builtin_bit_cast(bf16x8, oreg[j]);
+    float t = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t = fmaf((float)gv[e], (float)ov[e], t);
+    t = group_sum<CPR>(t);
+    if (ochunk == 0) dl[r] = t;
+  }
+  wait_lds();  // this wave's reads of its staged rows and its D writes are done
+  const float dlt = dl[lq];
   if (g == 0 && qi < seg1) a.delta[(int64_t)h * N + qi] = dlt;
+  // The pre-norm q rows for the epilogue, over the wave's Q-hat rows (read
+  // above); they land during the main loop.
+  {
+    TileLoader<D, SWZ_ROWS, 32, 1> xload;
+    xload.init(0, lane, a.q_stride);
+    xload.issue(q_stage, static_cast<const bf16 *>(a.q) + h * D, q0 + wave * 32, seg1 - 1);
+  }
 
   f32x16 dq[DB];
 #pragma unroll
@@ -340,6 +371,7 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
     for (int i = 0; i < 16; ++i) dq[b][i] = 0.f;
 
   const int ntiles = (seg1 - seg0 + BN - 1) / BN;
+  __syncthreads();  // every wave is done with its dO rows in the K/V buffers
   store_tile(0);
   __syncthreads();
 
@@ -394,6 +426,7 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
   }
 
   // dQ-hat row of this lane's query -> dq, and the block's Q gain partials.
+  wait_vmem();  // the pre-norm rows (a pack of one key tile issues no load after them)
   const bf16 *xt = x_s + wave * 32 * D;
   auto xa = [&](int d0) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x4 *>(xt + swz_off<D, SWZ_ROWS>(lq, d0));

@@ -188,6 +188,14 @@ __device__ __forceinline__ void wait_vmem_le() {
   asm volatile("" ::: "memory");
 }
 
+// Wait until this wave's LDS operations (reads returned, writes done) are
+// complete; no barrier.
+__device__ __forceinline__ void wait_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier that waits only for this wave's LDS operations, so global
 // (and global->LDS) loads in flight stay in flight across it. Global data a
 // wave loaded for others must be covered by its own wait_vmem() before a
