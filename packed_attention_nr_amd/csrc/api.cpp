@@ -224,6 +224,7 @@ mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmdit_bwd_
              skv = stages & MMDIT_STAGE_BWD_DKDV, sgn = stages & MMDIT_STAGE_BWD_GAINS;
   char *w = static_cast<char *>(ws);
   float *delta = reinterpret_cast<float *>(w + wl.delta);
+  float *nlse = reinterpret_cast<float *>(w + wl.nlse);
   float *part_q = reinterpret_cast<float *>(w + wl.part_q);
   float *part_k = reinterpret_cast<float *>(w + wl.part_k);
   float *dq_acc = f32 ? reinterpret_cast<float *>(w + wl.dq_acc) : nullptr;
@@ -283,13 +284,13 @@ mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmdit_bwd_
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float scale = (float)(1.0 / std::sqrt((double)d));
   AttnBwdArgs ba{a->q_hat, a->k_hat, a->v, a->dout, a->o, a->v_stride, a->dout_stride, a->lse,
-                 delta, dq_acc, dk_acc, a->dv, (float)(1.4426950408889634 / std::sqrt((double)d)),
+                 delta, nlse, dq_acc, dk_acc, a->dv, (float)(1.4426950408889634 / std::sqrt((double)d)),
                  scale, a->q, a->k, a->q_stride, a->k_stride, a->gains, a->rstd, a->dq, a->dk,
                  part_q, part_k, store_ds ? static_cast<void *>(w + wl.ds) : nullptr};
   if (store_ds) {  // D, then dK/dV writing dS, then dQ from dS
     hipError_t e = hipSuccess;
     if (sd) {
-      const BwdPreArgs pre{a->o, a->dout, a->dout_stride, delta, nullptr};
+      const BwdPreArgs pre{a->o, a->dout, a->dout_stride, delta, nullptr, a->lse, nlse};
       e = launch_bwd_pre(plan->dtype, pd, pre, s);
     }
     if (e == hipSuccess && skv) e = launch_attn_bwd(plan->dtype, pd, ba, kBwdDkdv, s);

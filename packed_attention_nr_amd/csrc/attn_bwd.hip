@@ -354,8 +354,7 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
     if (ochunk == 0) dl[r] = t;
   }
   wait_lds();  // this wave's reads of its staged rows and its D writes are done
-  const float dlt = dl[lq];
-  if (g == 0 && qi < seg1) a.delta[(int64_t)h * N + qi] = dlt;
+  const float dlt = dl[lq];  // written out with -lse*log2e after the loop
   // The pre-norm q rows for the epilogue, over the wave's Q-hat rows (read
   // above); they land during the main loop.
   {
@@ -425,6 +424,13 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
     __syncthreads();
   }
 
+  // D and -lse*log2e for the dK/dV kernel, stored after the loop: a store
+  // pending at the loop's start would make the compiler wait for every
+  // outstanding memory operation wherever the loop waits for a load.
+  if (g == 0 && qi < seg1) {
+    a.delta[(int64_t)h * N + qi] = dlt;
+    a.nlse[(int64_t)h * N + qi] = -lse2;
+  }
   // dQ-hat row of this lane's query -> dq, and the block's Q gain partials.
   wait_vmem();  // the pre-norm rows (a pack of one key tile issues no load after them)
   const bf16 *xt = x_s + wave * 32 * D;
@@ -703,7 +709,7 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   const int64_t gstride = a.dout_stride;
   const bf16 *qh = static_cast<const bf16 *>(a.q_hat) + h * D;
   const bf16 *go = static_cast<const bf16 *>(a.dout) + h * D;
-  const float *lse_h = a.lse + (int64_t)h * N;
+  const float *nlse_h = a.nlse + (int64_t)h * N;  // -lse * log2(e), from the dQ or D pass
   const float *dlt_h = a.delta + (int64_t)h * N;
   const float c2 = a.scale_log2;
 
@@ -736,13 +742,14 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   // tile the last tile is loaded again into the stage just freed, which
   // nothing reads afterwards.
   // Queries past the segment end need no mask: their Q-hat and dO rows land
-  // as zeros and their lse reads as 0 (its descriptor ends at the segment),
+  // as zeros and their -lse*log2e reads as 0 (its descriptor ends at the segment),
   // so S = 0 and P = exp2(0) = 1 there, finite, and both dV^T += dO^T P and
   // dK^T += Q-hat^T dS add zero for them.
   const uint32_t vec_bytes = 4u * (uint32_t)seg1;  // lse / D words up to the segment end
-  // With its tile, each role loads one per-query vector into the stage: lse
-  // (P/dV waves) or D (dS/dK waves), the same 64 words from each of the four.
-  const rsrc_t l_rs = make_rsrc(lse_h, vec_bytes);
+  // With its tile, each role loads one per-query vector into the stage:
+  // -lse*log2e (P/dV waves) or D (dS/dK waves), the same 64 words from each
+  // of the four.
+  const rsrc_t l_rs = make_rsrc(nlse_h, vec_bytes);
   const rsrc_t d_rs = make_rsrc(dlt_h, vec_bytes);
   auto issue_q = [&](auto stage, int t) __attribute__((always_inline)) {
     const int qb0 = seg0 + min(t, ntq - 1) * BMQ;
@@ -800,8 +807,6 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   auto softmax = [&](const float *Ls) __attribute__((always_inline)) {
     f32x4 nl[ROW_LOADS];
     read_rows(Ls, nl);
-#pragma unroll
-    for (int j = 0; j < ROW_LOADS; ++j) nl[j] = nl[j] * -kLog2e;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll

@@ -68,7 +68,7 @@ uint64_t bwd_partial_blocks(int64_t n_tokens);
 // stored-dS path (bf16) adds the dS area at `ds` (4 KiB aligned), ds_total
 // bytes in all (ds_total = total where the path does not apply).
 struct BwdLayout {
-  uint64_t delta, part_q, part_k, dq_acc, dk_acc, total, ds, ds_total;
+  uint64_t delta, nlse, part_q, part_k, dq_acc, dk_acc, total, ds, ds_total;
   int32_t nq, nk;
 };
 BwdLayout bwd_layout(const mmdit_plan &p);
@@ -136,6 +136,8 @@ struct BwdPreArgs {
   int64_t dout_stride;
   float *delta;                // [H][N]
   float *dq_acc;               // [N][H][d] fp32, zeroed here; nullptr: D only
+  const float *lse;            // [H][N] (with nlse)
+  float *nlse;                 // [H][N]: -lse * log2(e), or nullptr
 };
 
 struct AttnBwdArgs {
@@ -143,6 +145,7 @@ struct AttnBwdArgs {
   int64_t v_stride, dout_stride;
   const float *lse;            // [H][N]
   float *delta;                // [H][N]: written by the dQ pass, read by the dK/dV pass
+  float *nlse;                 // [H][N]: -lse * log2(e), written and read like delta (bf16 path)
   float *dq_acc;               // fp32 path: [N][H][d] dQ-hat (scaled by 1/sqrt(d))
   float *dk_acc;               // fp32 path: [N][H][d] dK-hat (scaled by 1/sqrt(d))
   void *dv;                    // [N][H][d] dtype

@@ -59,6 +59,8 @@ BwdLayout bwd_layout(const mmdit_plan &p) {
   uint64_t off = 0;
   w.delta = off;
   off = align_up(off + 4 * H * N, 256);
+  w.nlse = off;
+  off = align_up(off + 4 * H * N, 256);
   w.part_q = off;
   off = align_up(off + (uint64_t)w.nq * 2 * d * 4, 256);
   w.part_k = off;

@@ -123,9 +123,11 @@ __global__ __launch_bounds__(256) void prologue_fwd_kernel(PlanDev p, PrologueFw
 }
 
 // ---------------------------------------------------------------------------
-// Backward preprocess: D = rowsum(dO * O); clear the fp32 dQ-hat
-// accumulator when there is one.
+// Backward preprocess: D = rowsum(dO * O) and, for the bf16 dK/dV kernel,
+// -lse * log2(e) (the value the dQ kernel writes in the other mode, rounded
+// the same way); clear the fp32 dQ-hat accumulator when there is one.
 // ---------------------------------------------------------------------------
+constexpr float kLog2eBwd = 1.4426950408889634f;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(PlanDev p, BwdPreArgs a) {
   if (blob_stale(p.guard)) return;  // another pack's blob: touch nothing
@@ -146,7 +148,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PlanDev p, BwdPreArgs a) {
 #pragma unroll
   for (int i = 0; i < VEC; ++i) s += o[i] * g[i];
   s = group_sum<LPR>(s);
-  if (e0 == 0) a.delta[(int64_t)h * N + t] = s;
+  if (e0 == 0) {
+    a.delta[(int64_t)h * N + t] = s;
+    if (a.nlse) a.nlse[(int64_t)h * N + t] = -(a.lse[(int64_t)h * N + t] * kLog2eBwd);
+  }
   if (!a.dq_acc) return;
   float *z = a.dq_acc + r * D + e0;
 #pragma unroll
