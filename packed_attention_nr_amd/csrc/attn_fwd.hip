@@ -93,14 +93,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
   const int64_t vs = a.v_stride;
 
   // Q^T as the B operand: lane holds query q0 + 32*wave + lq, d = 16s + 8g + 0..7.
+  // The wave's 32 Q-hat rows arrive whole (direct loads of full rows) in ring
+  // stages 2 and 3, which the first two tiles leave free; rows past the
+  // segment end arrive as zeros (their scores are formed but never stored).
+  static_assert(2 * 32 * D == TILE, "two waves' Q-hat rows fill a stage");
   const int qi = q0 + wave * 32 + lq;
-  const int qc = min(qi, seg1 - 1);
-  bf16x8 qf[KS];
+  bf16 *const q_stage = (wave < 2 ? k2s : wave < 4 ? k3s : wave < 6 ? v2s : v3s) + (wave & 1) * 32 * D;
   {
-    const bf16 *src = qh + (int64_t)qc * HD + h * D + 8 * g;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = ld_bf16x8(src + 16 * s);
+    TileLoader<D, SWZ_ROWS, 32, 1> qload;
+    qload.init(0, lane, HD);
+    qload.issue(q_stage, qh + h * D, q0 + wave * 32, seg1 - 1);
   }
+  bf16x8 qf[KS];  // read from q_stage once tiles 0 and 1 are requested
 
   const int ntiles = (seg1 - seg0 + BN - 1) / BN;
   // Direct global -> LDS loads of tile t into ring stage t % NS (rows past the
@@ -235,7 +239,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
   issue(std::integral_constant<int, 0>{}, 0);
   issue(std::integral_constant<int, 1>{}, 1);
   wait_vmem();
-  lds_barrier();
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qf[s] = ld_bf16x8(q_stage + swz_off<D, SWZ_ROWS>(lq, 16 * s + 8 * g));
+  lds_barrier();  // tiles 0 and 1 visible; every wave's Q-hat reads done before tile 2 is issued
   if (grp == 1) lds_barrier();
   scores(std::integral_constant<int, 0>{});
   for (int t = 0; t < ntiles; t += NS) {
