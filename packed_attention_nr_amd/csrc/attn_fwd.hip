@@ -255,11 +255,21 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
   }
   if (grp == 0) lds_barrier();
 
-  // Epilogue: normalise, store O (rows inside the segment) and lse.
+  // Epilogue: normalise O, store it (rows inside the segment) and lse. The
+  // wave's 32 rows go out whole: each lane first writes its O^T columns into
+  // an LDS copy of the rows, then the wave stores them 16 lanes to a 256-byte
+  // row. The copy uses ring stages (L+2) % 4 and (L+3) % 4 (L = the last
+  // tile): no load is issued past the last tile and both groups have passed
+  // their last reads of those stages, while group 1's last matrix phase still
+  // reads stages L % 4 and (L+1) % 4. Each wave has its own 8 KiB (d = 128).
   const float l = half_sum(l_part);
   const float inv = 1.0f / l;
-  if (qi < seg1) {
-    bf16 *dst = static_cast<bf16 *>(a.o) + (int64_t)qi * HD + h * D;
+  {
+    const int bi = wave >> 1;                  // stage buffer: K or V of stage (L + 2 + bi / 2) % 4
+    const int sg = (ntiles + 1 + (bi >> 1)) & 3;
+    bf16 *const buf = (bi & 1) ? (sg == 0 ? v0s : sg == 1 ? v1s : sg == 2 ? v2s : v3s)
+                               : (sg == 0 ? k0s : sg == 1 ? k1s : sg == 2 ? k2s : k3s);
+    bf16 *const ost = buf + (wave & 1) * 32 * D;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -268,11 +278,23 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
         bf16x2 t0 = pack2(o[b][4 * r4 + 0] * inv, o[b][4 * r4 + 1] * inv);
         bf16x2 t1 = pack2(o[b][4 * r4 + 2] * inv, o[b][4 * r4 + 3] * inv);
         v4[0] = t0[0]; v4[1] = t0[1]; v4[2] = t1[0]; v4[3] = t1[1];
-        *reinterpret_cast<bf16x4 *>(dst + b * 32 + 8 * r4 + 4 * g) = v4;
+        *reinterpret_cast<bf16x4 *>(ost + swz_off<D, SWZ_ROWS>(lq, b * 32 + 8 * r4 + 4 * g)) = v4;
       }
-    if (a.lse && g == 0)
-      a.lse[(int64_t)h * p.total_tokens + qi] = (m_ref + __log2f(l)) * 0.69314718055994531f;
+    wait_lds();  // the wave's rows are complete in LDS
+    constexpr int CPR = D / 8;     // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;  // rows per instruction
+    const int orow = lane / CPR, ochunk = lane % CPR;
+    bf16 *const og = static_cast<bf16 *>(a.o) + h * D + 8 * ochunk;
+#pragma unroll
+    for (int j = 0; j < 32 / RPI; ++j) {
+      const int r = RPI * j + orow;
+      const int q = q0 + wave * 32 + r;
+      const bf16x8 v = ld_bf16x8(ost + swz_off<D, SWZ_ROWS>(r, 8 * ochunk));
+      if (q < seg1) st16(og + (int64_t)q * HD, as_u4(v));
+    }
   }
+  if (a.lse && g == 0 && qi < seg1)
+    a.lse[(int64_t)h * p.total_tokens + qi] = (m_ref + __log2f(l)) * 0.69314718055994531f;
 }
 
 hipError_t launch_attn_fwd_f32(const PlanDev &p, const AttnFwdArgs &a, hipStream_t stream);
