@@ -85,12 +85,15 @@ static_assert(bwd::QT == kFwdTileBf16 && bwd::KT == kBwdTile, "backward tiles mu
 // 128 floats; every wave of the workgroup passes the barrier inside), adding
 // them in a fixed order (the partial of the wave with first = true first), so
 // both get bitwise the same sums.
-template <int D, int B0, int NB, bool XCH, typename XA>
+// With LROWS the outputs go, for every row, to an LDS copy of the wave's 32
+// rows (lrows, [32][D], ROWS-swizzled) instead of dx; the caller stores the
+// valid rows whole.
+template <int D, int B0, int NB, bool XCH, bool LROWS = false, typename XA>
 __device__ __forceinline__ void prologue_bwd_rows(f32x16 (&acc)[D / 32], float scale, int32_t meta,
                                                   float rho, bool valid, const XA &xa, const float *g2,
                                                   const float2 *rope, int fp, float eps, bf16 *dx, int64_t out,
                                                   float *red, int lane, float *xch = nullptr, int self = 0,
-                                                  int partner = 0, bool first = true) {
+                                                  int partner = 0, bool first = true, bf16 *lrows = nullptr) {
   constexpr int DB = D / 32;
   static_assert(B0 >= 0 && NB >= 1 && B0 + NB <= DB, "block range");
   const int lq = lane & 31, g = lane >> 5;
@@ -172,12 +175,13 @@ __device__ __forceinline__ void prologue_bwd_rows(f32x16 (&acc)[D / 32], float s
         o[j] = rho * g4[j] * acc[b][i] - c3 * x;
         acc[b][i] = valid ? rho * acc[b][i] * x : 0.f;  // gain-gradient term
       }
-      if (valid) {
-        const bf16x2 t0 = pack2(o[0], o[1]), t1 = pack2(o[2], o[3]);
-        bf16x4 o4;
-        o4[0] = t0[0]; o4[1] = t0[1]; o4[2] = t1[0]; o4[3] = t1[1];
+      const bf16x2 t0 = pack2(o[0], o[1]), t1 = pack2(o[2], o[3]);
+      bf16x4 o4;
+      o4[0] = t0[0]; o4[1] = t0[1]; o4[2] = t1[0]; o4[3] = t1[1];
+      if constexpr (LROWS)
+        *reinterpret_cast<bf16x4 *>(lrows + swz_off<D, SWZ_ROWS>(lq, d0)) = o4;
+      else if (valid)
         *reinterpret_cast<bf16x4 *>(dx + out + d0) = o4;
-      }
     }
   }
   // Sum the gain terms over the wave's 32 tokens (lanes lq = 0..31 of each
@@ -210,6 +214,21 @@ __device__ __forceinline__ void prologue_bwd_rows(f32x16 (&acc)[D / 32], float s
   } else {
     reduce_into(0, false, false);  // text only (or no valid token: all zero)
     zero_row(1);
+  }
+}
+
+// Store rows r0 .. r0 + n - 1 of an LDS copy of 32 token rows ([32][D],
+// ROWS-swizzled; row r is token t0 + r) to dst (token t's row at t * stride),
+// 16 lanes to a 256-byte row, rows of tokens >= t_end skipped (one wave).
+template <int D>
+__device__ __forceinline__ void store_rows(const bf16 *lrows, int r0, int n, int t0, int t_end, bf16 *dst,
+                                           int64_t stride, int lane) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR;
+  const int orow = lane / CPR, ochunk = lane % CPR;
+  for (int j = 0; j < n / RPI; ++j) {
+    const int r = r0 + RPI * j + orow;
+    const bf16x8 v = ld_bf16x8(lrows + swz_off<D, SWZ_ROWS>(r, 8 * ochunk));
+    if (t0 + r < t_end) st16(dst + (int64_t)(t0 + r) * stride + 8 * ochunk, as_u4(v));
   }
 }
 
@@ -437,8 +456,13 @@ __global__ __launch_bounds__(64 * bwd::NWQ, 1) void attn_bwd_dq_kernel(PlanDev p
   auto xa = [&](int d0) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x4 *>(xt + swz_off<D, SWZ_ROWS>(lq, d0));
   };
-  prologue_bwd_rows<D, 0, D / 32, false>(dq, a.scale, meta, rho0, qi < seg1, xa, g_s, p.rope, p.rope_frame_pairs, p.rms_eps,
-                       static_cast<bf16 *>(a.dq), ((int64_t)qc * H + h) * D, red + wave * 2 * D, lane);
+  // The dQ rows go out whole through the wave's dO staging slice (free
+  // after the loop).
+  prologue_bwd_rows<D, 0, D / 32, false, true>(dq, a.scale, meta, rho0, qi < seg1, xa, g_s, p.rope,
+                                               p.rope_frame_pairs, p.rms_eps, nullptr, 0, red + wave * 2 * D, lane,
+                                               nullptr, 0, 0, true, g_stage);
+  wait_lds();
+  store_rows<D>(g_stage, 0, 32, q0 + wave * 32, seg1, static_cast<bf16 *>(a.dq) + h * D, HD, lane);
   __syncthreads();
   sum_wave_partials<D>(red, NWQ, part, tid);
 }
@@ -943,20 +967,21 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   float *red = reinterpret_cast<float *>(p_s);
   float *hand = reinterpret_cast<float *>(st0);  // [sub][HB * 16][64 lanes]
   float *xch = reinterpret_cast<float *>(st1);   // [role * 4 + sub][128]
+  // dV and dK rows go out whole through LDS copies of each sub-tile's 32
+  // key rows: dK in ring stage 2, dV in stage 3 (32 x d each per sub-tile).
+  static_assert(4 * 32 * D <= STAGE, "a stage holds four sub-tiles' rows");
+  bf16 *const dk_rows = st2 + sub * 32 * D, *const dv_rows = st3 + sub * 32 * D;
   if (role == 0) {
-    if (key_ok) {
-      bf16 *dvp = static_cast<bf16 *>(a.dv) + (int64_t)kr * HD + h * D;
 #pragma unroll
-      for (int b = 0; b < DB; ++b)
+    for (int b = 0; b < DB; ++b)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          bf16x4 v4;
-          const bf16x2 t0 = pack2(acc[b][4 * r4], acc[b][4 * r4 + 1]);
-          const bf16x2 t1 = pack2(acc[b][4 * r4 + 2], acc[b][4 * r4 + 3]);
-          v4[0] = t0[0]; v4[1] = t0[1]; v4[2] = t1[0]; v4[3] = t1[1];
-          *reinterpret_cast<bf16x4 *>(dvp + b * 32 + 8 * r4 + 4 * g) = v4;
-        }
-    }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 v4;
+        const bf16x2 t0 = pack2(acc[b][4 * r4], acc[b][4 * r4 + 1]);
+        const bf16x2 t1 = pack2(acc[b][4 * r4 + 2], acc[b][4 * r4 + 3]);
+        v4[0] = t0[0]; v4[1] = t0[1]; v4[2] = t1[0]; v4[3] = t1[1];
+        *reinterpret_cast<bf16x4 *>(dv_rows + swz_off<D, SWZ_ROWS>(lq, b * 32 + 8 * r4 + 4 * g)) = v4;
+      }
   } else {
 #pragma unroll
     for (int b = HB; b < DB; ++b)
@@ -977,12 +1002,16 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   bf16 *dkp = static_cast<bf16 *>(a.dk);
   const int64_t out = ((int64_t)kc * H + h) * D;
   if (role == 1)
-    prologue_bwd_rows<D, 0, HB, true>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope, p.rope_frame_pairs,
-                                      p.rms_eps, dkp, out, red + sub * 2 * D, lane, xch, 4 + sub, sub, true);
+    prologue_bwd_rows<D, 0, HB, true, true>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope, p.rope_frame_pairs,
+                                            p.rms_eps, dkp, out, red + sub * 2 * D, lane, xch, 4 + sub, sub, true,
+                                            dk_rows);
   else
-    prologue_bwd_rows<D, HB, HB, true>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope, p.rope_frame_pairs,
-                                       p.rms_eps, dkp, out, red + sub * 2 * D, lane, xch, sub, 4 + sub, false);
-  __syncthreads();
+    prologue_bwd_rows<D, HB, HB, true, true>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope,
+                                             p.rope_frame_pairs, p.rms_eps, dkp, out, red + sub * 2 * D, lane, xch,
+                                             sub, 4 + sub, false, dk_rows);
+  __syncthreads();  // both halves of the dK rows, and the dV rows, are in LDS
+  store_rows<D>(role ? dk_rows : dv_rows, 0, 32, k0 + sub * 32, seg1, static_cast<bf16 *>(role ? a.dk : a.dv) + h * D,
+                HD, lane);
   sum_wave_partials<D>(red, KV_NW / 2, part, tid);
 }
 
