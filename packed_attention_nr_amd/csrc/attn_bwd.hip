@@ -185,22 +185,25 @@ __device__ __forceinline__ void prologue_bwd_rows(f32x16 (&acc)[D / 32], float s
     }
   }
   // Sum the gain terms over the wave's 32 tokens (lanes lq = 0..31 of each
-  // half): for each register, DPP sums inside each 16-lane row, then one
-  // shuffle across lane bit 4, so every lane ends with the sums of all its
-  // registers; lane lq = i % 16 writes register i's. A wave whose valid
-  // tokens are all of one modality reduces once; a mixed wave once per
-  // modality.
+  // half): for each register, DPP sums inside each 16-lane row and a
+  // permlane16 swap across the two rows of the half, so every lane ends with
+  // the sums of all its registers, in VALU with no dependence from one
+  // register to the next; lane lq < 16 keeps register lq's sum by selects and
+  // writes it, one store per block. A wave whose valid tokens are all of one
+  // modality reduces once; a mixed wave once per modality.
   const uint64_t has_img = __ballot(valid && img), has_txt = __ballot(valid && !img);
   auto reduce_into = [&](int m, bool select, bool want_img) __attribute__((always_inline)) {
 #pragma unroll
-    for (int b = B0; b < B0 + NB; ++b)
+    for (int b = B0; b < B0 + NB; ++b) {
+      float mine = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float v = (!select || img == want_img) ? acc[b][i] : 0.f;
-        v = group_sum<16>(v);
-        v += __shfl_xor(v, 16);
-        if (lq == i) red[m * D + 32 * b + acc_row(i, g)] = v;
+        v = row_pair_sum(group_sum<16>(v));
+        mine = lq == i ? v : mine;
       }
+      if (lq < 16) red[m * D + 32 * b + acc_row(lq, g)] = mine;
+    }
   };
   auto zero_row = [&](int m) __attribute__((always_inline)) {
     for (int e = 32 * B0 + lane; e < 32 * (B0 + NB); e += 64) red[m * D + e] = 0.f;

@@ -99,6 +99,11 @@ __device__ __forceinline__ float half_sum(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
+// sum of x over lanes l and l^16 (the two 16-lane rows of each half), in VALU.
+__device__ __forceinline__ float row_pair_sum(float x) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
