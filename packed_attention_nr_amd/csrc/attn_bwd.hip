@@ -76,7 +76,7 @@ static_assert(bwd::QT == kFwdTileBf16 && bwd::KT == kBwdTile, "backward tiles mu
 // leaves in red[m * D + d] (m = 0 text, 1 image) this wave's sums of
 // rho*dy*x over its 32 tokens (invalid rows add nothing).
 // The pre-norm row's loads are issued before any arithmetic; the gradient
-// row is transformed in place (dX-hat -> dy -> gain terms), the pre-norm row
+// row is transformed in place (dX-hat/scale -> dy/scale -> gain terms), the pre-norm row
 // stays in bf16 and the RoPE entries are fetched per 16-pair block, so the
 // step keeps few registers live and the compiler need not spill.
 // B0, NB: the register blocks this wave finishes (d in [32 B0, 32 (B0 + NB))).
@@ -114,8 +114,6 @@ __device__ __forceinline__ void prologue_bwd_rows(f32x16 (&acc)[D / 32], float s
   const int re = fp + (D / 2 - fp) / 2;
 #pragma unroll
   for (int b = B0; b < B0 + NB; ++b) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[b][i] *= scale;
     if (img) {
       f32x4 cs[4];  // {cos, sin} of two consecutive pairs
 #pragma unroll
@@ -157,9 +155,13 @@ __device__ __forceinline__ void prologue_bwd_rows(f32x16 (&acc)[D / 32], float s
     ss = first ? ss + ss_p : ss_p + ss;
     dot = first ? dot + dot_p : dot_p + dot;
   }
+  // The row is linear in dX-hat, so its scale goes into rho's factors
+  // (rs for the output, rg for the gain terms, zero past the segment end)
+  // instead of into every element.
   if (rho < 0.f) rho = rsqrtf(half_sum(ss) * (1.0f / D) + eps);
   dot = half_sum(dot);
-  const float c3 = rho * rho * rho * dot * (1.0f / D);
+  const float c3 = rho * rho * rho * dot * (scale * (1.0f / D));
+  const float rs = rho * scale, rg = valid ? rs : 0.f;
 #pragma unroll
   for (int b = B0; b < B0 + NB; ++b) {
 #pragma unroll
@@ -172,8 +174,8 @@ __device__ __forceinline__ void prologue_bwd_rows(f32x16 (&acc)[D / 32], float s
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * r4 + j;
         const float x = (float)xb[j];
-        o[j] = rho * g4[j] * acc[b][i] - c3 * x;
-        acc[b][i] = valid ? rho * acc[b][i] * x : 0.f;  // gain-gradient term
+        o[j] = fmaf(rs, g4[j] * acc[b][i], -(c3 * x));
+        acc[b][i] = rg * acc[b][i] * x;  // gain-gradient term
       }
       const bf16x2 t0 = pack2(o[0], o[1]), t1 = pack2(o[2], o[3]);
       bf16x4 o4;
@@ -185,24 +187,39 @@ __device__ __forceinline__ void prologue_bwd_rows(f32x16 (&acc)[D / 32], float s
     }
   }
   // Sum the gain terms over the wave's 32 tokens (lanes lq = 0..31 of each
-  // half): for each register, DPP sums inside each 16-lane row and a
-  // permlane16 swap across the two rows of the half, so every lane ends with
-  // the sums of all its registers, in VALU with no dependence from one
-  // register to the next; lane lq < 16 keeps register lq's sum by selects and
-  // writes it, one store per block. A wave whose valid tokens are all of one
-  // modality reduces once; a mixed wave once per modality.
+  // half) by a transposing reduction in VALU: at each of four steps the
+  // registers pair up (2j, 2j + 1); a lane keeps the one that bit k of its
+  // index selects and adds the partner's copy of it, taken by DPP from a
+  // lane that differs in bit k and agrees in the bits below (xor 1, xor 2,
+  // then rotations by 4 and 8 inside the 16-lane row, which together cover
+  // the row). After them register j of lane l holds the row's sum of
+  // register 16j + l % 16, and a permlane16 swap adds the other row of the
+  // half: lane lq < 16 writes block j's sum for register lq. A wave whose
+  // valid tokens are all of one modality reduces once; a mixed wave once
+  // per modality.
   const uint64_t has_img = __ballot(valid && img), has_txt = __ballot(valid && !img);
   auto reduce_into = [&](int m, bool select, bool want_img) __attribute__((always_inline)) {
+    float v[NB * 16];
 #pragma unroll
-    for (int b = B0; b < B0 + NB; ++b) {
-      float mine = 0.f;
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = (!select || img == want_img) ? acc[b][i] : 0.f;
-        v = row_pair_sum(group_sum<16>(v));
-        mine = lq == i ? v : mine;
+      for (int i = 0; i < 16; ++i) v[16 * b + i] = (!select || img == want_img) ? acc[B0 + b][i] : 0.f;
+    auto step = [&](auto ctrl, int bit, int n) __attribute__((always_inline)) {
+      const bool hi = (lane & bit) != 0;
+#pragma unroll
+      for (int j = 0; j < n / 2; ++j) {
+        const float x = hi ? v[2 * j + 1] : v[2 * j], y = hi ? v[2 * j] : v[2 * j + 1];
+        v[j] = x + dpp<decltype(ctrl)::value>(y);
       }
-      if (lq < 16) red[m * D + 32 * b + acc_row(lq, g)] = mine;
+    };
+    step(std::integral_constant<int, 0xB1>{}, 1, NB * 16);   // quad_perm [1,0,3,2]
+    step(std::integral_constant<int, 0x4E>{}, 2, NB * 8);    // quad_perm [2,3,0,1]
+    step(std::integral_constant<int, 0x124>{}, 4, NB * 4);   // row_ror:4
+    step(std::integral_constant<int, 0x128>{}, 8, NB * 2);   // row_ror:8
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float t = row_pair_sum(v[b]);
+      if (lq < 16) red[m * D + 32 * (B0 + b) + acc_row(lq, g)] = t;
     }
   };
   auto zero_row = [&](int m) __attribute__((always_inline)) {
