@@ -75,10 +75,10 @@ static_assert(bwd::QT == kFwdTileBf16 && bwd::KT == kBwdTile, "backward tiles mu
 // the dense output. Writes dx (bf16) for a valid row and
 // leaves in red[m * D + d] (m = 0 text, 1 image) this wave's sums of
 // rho*dy*x over its 32 tokens (invalid rows add nothing).
-// The pre-norm row's loads are issued before any arithmetic; the gradient
-// row is transformed in place (dX-hat/scale -> dy/scale -> gain terms), the pre-norm row
-// stays in bf16 and the RoPE entries are fetched per 16-pair block, so the
-// step keeps few registers live and the compiler need not spill.
+// The pre-norm row's loads are issued before any arithmetic (or by the
+// caller, earlier: see RowInputs); the gradient row is transformed in place
+// (dX-hat/scale -> dy/scale -> gain terms) and the pre-norm row stays in
+// bf16, so the step keeps few registers live and the compiler need not spill.
 // B0, NB: the register blocks this wave finishes (d in [32 B0, 32 (B0 + NB))).
 // With XCH, another wave finishes the other blocks of the same rows: the two
 // exchange their partial row sums through xch (slots self and partner of
@@ -88,45 +88,94 @@ static_assert(bwd::QT == kFwdTileBf16 && bwd::KT == kBwdTile, "backward tiles mu
 // With LROWS the outputs go, for every row, to an LDS copy of the wave's 32
 // rows (lrows, [32][D], ROWS-swizzled) instead of dx; the caller stores the
 // valid rows whole.
-template <int D, int B0, int NB, bool XCH, bool LROWS = false, typename XA>
+// The inputs of NB register blocks of one lane's row that come from memory:
+// the pre-norm elements and the {cos, sin} RoPE entries. Lane pairs (d, d+1)
+// of register block b are pairs 16b + 4(k/2) + 2g + k%2, k = 0..7: two
+// consecutive pairs per k/2, in one RoPE section (section boundaries are
+// multiples of 4 pairs), so each k/2 is one 16-byte load; a text row loads
+// table row 0 and does not use it. A caller that has registers to spare
+// fetches them early (prologue_bwd_fetch), so that their latency overlaps
+// other work, and passes them in.
+template <int NB>
+struct RowInputs {
+  bf16x4 x4[NB][4];
+  f32x4 cs[NB][4];
+};
+template <int D, int B0, int NB, typename XA>
+__device__ __forceinline__ void prologue_bwd_fetch(RowInputs<NB> &in, int32_t meta, const XA &xa,
+                                                   const float2 *rope, int fp, int lane) {
+  const int g = lane >> 5;
+  bool img;
+  int row, col, frame;
+  tok_pos(meta, img, row, col, frame);
+  const int re = fp + (D / 2 - fp) / 2;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) in.x4[b][r4] = xa(32 * (B0 + b) + 8 * r4 + 4 * g);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const int pair = 16 * (B0 + b) + 4 * k2 + 2 * g;
+      const int pos = img ? rope_pos(pair, fp, re, row, col, frame) : 0;
+      in.cs[b][k2] = *reinterpret_cast<const f32x4 *>(rope + pos * (D / 2) + pair);
+    }
+}
+
+// PRE: `pre` holds the row inputs fetched by the caller (prologue_bwd_fetch);
+// otherwise they are loaded here (the pre-norm row first, then block by
+// block the RoPE entries, which keeps few registers live).
+template <int D, int B0, int NB, bool XCH, bool LROWS = false, bool PRE = false, typename XA>
 __device__ __forceinline__ void prologue_bwd_rows(f32x16 (&acc)[D / 32], float scale, int32_t meta,
                                                   float rho, bool valid, const XA &xa, const float *g2,
                                                   const float2 *rope, int fp, float eps, bf16 *dx, int64_t out,
                                                   float *red, int lane, float *xch = nullptr, int self = 0,
-                                                  int partner = 0, bool first = true, bf16 *lrows = nullptr) {
+                                                  int partner = 0, bool first = true, bf16 *lrows = nullptr,
+                                                  const RowInputs<NB> &pre = RowInputs<NB>{}) {
   constexpr int DB = D / 32;
   static_assert(B0 >= 0 && NB >= 1 && B0 + NB <= DB, "block range");
   const int lq = lane & 31, g = lane >> 5;
   bool img;
   int row, col, frame;
   tok_pos(meta, img, row, col, frame);
-  // The pre-norm row is loaded first (it stays in bf16); then, block by
-  // block, the RoPE entries of the block's pairs and the inverse rotation
-  // in place. Lane pairs (d, d+1) of register block b are pairs
-  // 16b + 4(k/2) + 2g + k%2, k = 0..7: two consecutive pairs per k/2, in one
-  // RoPE section (section boundaries are multiples of 4 pairs), so each k/2
-  // is one 16-byte load.
   bf16x4 x4[DB][4];
+  if constexpr (PRE) {
 #pragma unroll
-  for (int b = B0; b < B0 + NB; ++b)
+    for (int b = B0; b < B0 + NB; ++b) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) x4[b][r4] = xa(32 * b + 8 * r4 + 4 * g);
-  const int re = fp + (D / 2 - fp) / 2;
-#pragma unroll
-  for (int b = B0; b < B0 + NB; ++b) {
-    if (img) {
-      f32x4 cs[4];  // {cos, sin} of two consecutive pairs
-#pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        const int pair = 16 * b + 4 * k2 + 2 * g;
-        cs[k2] = *reinterpret_cast<const f32x4 *>(rope + rope_pos(pair, fp, re, row, col, frame) * (D / 2) + pair);
-      }
+      for (int r4 = 0; r4 < 4; ++r4) x4[b][r4] = pre.x4[b - B0][r4];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float c = cs[k >> 1][2 * (k & 1)], sn = cs[k >> 1][2 * (k & 1) + 1];
+        const f32x4 c4 = pre.cs[b - B0][k >> 1];
+        const float c = c4[2 * (k & 1)], sn = c4[2 * (k & 1) + 1];
         const float u = acc[b][2 * k], w = acc[b][2 * k + 1];
-        acc[b][2 * k] = u * c + w * sn;
-        acc[b][2 * k + 1] = w * c - u * sn;
+        acc[b][2 * k] = img ? u * c + w * sn : u;
+        acc[b][2 * k + 1] = img ? w * c - u * sn : w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b = B0; b < B0 + NB; ++b)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) x4[b][r4] = xa(32 * b + 8 * r4 + 4 * g);
+    const int re = fp + (D / 2 - fp) / 2;
+#pragma unroll
+    for (int b = B0; b < B0 + NB; ++b) {
+      if (img) {
+        f32x4 cs[4];  // {cos, sin} of two consecutive pairs (see RowInputs)
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          const int pair = 16 * b + 4 * k2 + 2 * g;
+          cs[k2] = *reinterpret_cast<const f32x4 *>(rope + rope_pos(pair, fp, re, row, col, frame) * (D / 2) + pair);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float c = cs[k >> 1][2 * (k & 1)], sn = cs[k >> 1][2 * (k & 1) + 1];
+          const float u = acc[b][2 * k], w = acc[b][2 * k + 1];
+          acc[b][2 * k] = u * c + w * sn;
+          acc[b][2 * k + 1] = w * c - u * sn;
+        }
       }
     }
   }
@@ -991,7 +1040,31 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   // key rows: dK in ring stage 2, dV in stage 3 (32 x d each per sub-tile).
   static_assert(4 * 32 * D <= STAGE, "a stage holds four sub-tiles' rows");
   bf16 *const dk_rows = st2 + sub * 32 * D, *const dv_rows = st3 + sub * 32 * D;
-  if (role == 0) {
+  // The pre-norm k elements and RoPE entries of this wave's half of the row
+  // are requested first; they arrive while the dV rows and the hand-over
+  // pass through LDS (a barrier on LDS operations only, so they stay in
+  // flight across it). Each role runs its whole epilogue in one branch, so
+  // the fetched values stay in registers; both pass the same barriers.
+  const bf16 *xg = static_cast<const bf16 *>(a.k) + (int64_t)kc * a.k_stride + h * D;
+  auto xa = [&](int d0) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x4 *>(xg + d0);
+  };
+  bf16 *dkp = static_cast<bf16 *>(a.dk);
+  const int64_t out = ((int64_t)kc * H + h) * D;
+  if (role == 1) {
+    RowInputs<HB> rin;
+    prologue_bwd_fetch<D, 0, HB>(rin, meta, xa, p.rope, p.rope_frame_pairs, lane);
+#pragma unroll
+    for (int b = HB; b < DB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) hand[((sub * HB + (b - HB)) * 16 + i) * 64 + lane] = acc[b][i];
+    lds_barrier();
+    prologue_bwd_rows<D, 0, HB, true, true, true>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope,
+                                                  p.rope_frame_pairs, p.rms_eps, dkp, out, red + sub * 2 * D, lane,
+                                                  xch, 4 + sub, sub, true, dk_rows, rin);
+  } else {
+    RowInputs<HB> rin;
+    prologue_bwd_fetch<D, HB, HB>(rin, meta, xa, p.rope, p.rope_frame_pairs, lane);
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -1002,33 +1075,15 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
         v4[0] = t0[0]; v4[1] = t0[1]; v4[2] = t1[0]; v4[3] = t1[1];
         *reinterpret_cast<bf16x4 *>(dv_rows + swz_off<D, SWZ_ROWS>(lq, b * 32 + 8 * r4 + 4 * g)) = v4;
       }
-  } else {
-#pragma unroll
-    for (int b = HB; b < DB; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) hand[((sub * HB + (b - HB)) * 16 + i) * 64 + lane] = acc[b][i];
-  }
-  __syncthreads();
-  if (role == 0) {
+    lds_barrier();
 #pragma unroll
     for (int b = HB; b < DB; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[b][i] = hand[((sub * HB + (b - HB)) * 16 + i) * 64 + lane];
+    prologue_bwd_rows<D, HB, HB, true, true, true>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope,
+                                                   p.rope_frame_pairs, p.rms_eps, dkp, out, red + sub * 2 * D, lane,
+                                                   xch, sub, 4 + sub, false, dk_rows, rin);
   }
-  const bf16 *xg = static_cast<const bf16 *>(a.k) + (int64_t)kc * a.k_stride + h * D;
-  auto xa = [&](int d0) __attribute__((always_inline)) {
-    return *reinterpret_cast<const bf16x4 *>(xg + d0);
-  };
-  bf16 *dkp = static_cast<bf16 *>(a.dk);
-  const int64_t out = ((int64_t)kc * H + h) * D;
-  if (role == 1)
-    prologue_bwd_rows<D, 0, HB, true, true>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope, p.rope_frame_pairs,
-                                            p.rms_eps, dkp, out, red + sub * 2 * D, lane, xch, 4 + sub, sub, true,
-                                            dk_rows);
-  else
-    prologue_bwd_rows<D, HB, HB, true, true>(acc, a.scale, meta, rho0, key_ok, xa, g_s, p.rope,
-                                             p.rope_frame_pairs, p.rms_eps, dkp, out, red + sub * 2 * D, lane, xch,
-                                             sub, 4 + sub, false, dk_rows);
   __syncthreads();  // both halves of the dK rows, and the dV rows, are in LDS
   store_rows<D>(role ? dk_rows : dv_rows, 0, 32, k0 + sub * 32, seg1, static_cast<bf16 *>(role ? a.dk : a.dv) + h * D,
                 HD, lane);
