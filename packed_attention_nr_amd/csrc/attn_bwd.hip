@@ -938,9 +938,10 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
   for (int u = 0; u < BMQ / 16; ++u) pb[u] = bf16x8{};
   for (int e = tid * 8; e < TILE; e += 64 * KV_NW * 8) st_bf16x8(st3 + e, bf16x8{});
 
-  // Both roles run the same whole number of 4-step groups (every step loads,
-  // waits and passes two barriers; work is skipped past the last tile), so the
-  // loop has a single exit and barrier counts match across roles.
+  // Both roles run one step per query tile (every step loads, waits and
+  // passes two barriers) and leave the loop after the same step, so barrier
+  // counts match across roles; the loads issued past the last tile are
+  // waited for after the loop.
   if (role == 0) {
     issue_q(S0{}, 0);
     issue_q(std::integral_constant<int, 1>{}, 1);
@@ -967,8 +968,11 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
     };
     for (int t = 0; t < ntq; t += KV_NS) {
       step(S0{}, t);
+      if (t + 1 >= ntq) break;
       step(std::integral_constant<int, 1>{}, t + 1);
+      if (t + 2 >= ntq) break;
       step(std::integral_constant<int, 2>{}, t + 2);
+      if (t + 3 >= ntq) break;
       step(std::integral_constant<int, 3>{}, t + 3);
     }
   } else {
@@ -1015,8 +1019,11 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
     };
     for (int t = 0; t < ntq; t += KV_NS) {
       step(S0{}, t);
+      if (t + 1 >= ntq) break;
       step(std::integral_constant<int, 1>{}, t + 1);
+      if (t + 2 >= ntq) break;
       step(std::integral_constant<int, 2>{}, t + 2);
+      if (t + 3 >= ntq) break;
       step(std::integral_constant<int, 3>{}, t + 3);
     }
   }
