@@ -951,13 +951,13 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
     auto step = [&](auto stage, int t) __attribute__((always_inline)) {
       constexpr int SG = decltype(stage)::value;
       issue_q(std::integral_constant<int, (SG + 2) % KV_NS>{}, t + 2);
-      if (t < ntq) softmax(lst(stage));
+      softmax(lst(stage));
       wait_vmem_le<PER_TILE>();  // this wave's loads of tile t+1
       phase_barrier();  // P(t) and tile t+1 visible
       __builtin_amdgcn_s_setprio(3);
-      if (t < ntq) {  // one basic block, scheduled as an MFMA / LDS-read pipeline
+      {  // one basic block, scheduled as an MFMA / LDS-read pipeline
         accumulate(gst(stage));  // dV(t)
-        // S(t+1); past the last tile the stage holds a repeat of the last
+        // S(t+1); after the last tile the stage holds a repeat of the last
         // tile and the result goes unused
         rows_x_key(qst(std::integral_constant<int, (SG + 1) % KV_NS>{}));
         pipeline_mfma_ds<(BMQ / 16) * DB + 2 * KS, (BMQ / 16) * DB, 2, 1, 4>();
@@ -984,7 +984,7 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
     auto step = [&](auto stage, int t) __attribute__((always_inline)) {
       constexpr int SG = decltype(stage)::value;
       __builtin_amdgcn_s_setprio(3);
-      if (t < ntq) {  // one basic block, scheduled as an MFMA / LDS-read pipeline
+      {  // one basic block, scheduled as an MFMA / LDS-read pipeline
         accumulate(qst(std::integral_constant<int, (SG + 3) % KV_NS>{}));  // dK(t-1)
         rows_x_key(gst(stage));  // dP(t)
         pipeline_mfma_ds<(BMQ / 16) * DB + 2 * KS, (BMQ / 16) * DB, 2, 1, 4>();
@@ -998,22 +998,18 @@ __global__ __launch_bounds__(64 * bwd::KV_NW, 1) void attn_bwd_dkdv_kernel(PlanD
       wait_vmem_le<PER_TILE>();
       phase_barrier();  // P(t) and tile t+1 visible
       if constexpr (DS) {
-        if (t < ntq) {
-          dscores(dst(stage));  // dS(t)
+        dscores(dst(stage));  // dS(t)
 #pragma unroll
-          for (int u = 0; u < BMQ / 16; ++u)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pb[u]), ds_rs,
-                                                   (int)(ds_off + (uint32_t)(4 * t + u) * kDsBlockBytes), 0,
-                                                   bwd::kDsCachePolicy);
-        }
+        for (int u = 0; u < BMQ / 16; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pb[u]), ds_rs,
+                                                 (int)(ds_off + (uint32_t)(4 * t + u) * kDsBlockBytes), 0,
+                                                 bwd::kDsCachePolicy);
         issue_g(std::integral_constant<int, (SG + 3) % KV_NS>{}, t + 3);
-        if (t < ntq && t + 1 == ntq) accumulate(qst(stage));  // last dK
+        if (t + 1 == ntq) accumulate(qst(stage));  // last dK
       } else {
         issue_g(std::integral_constant<int, (SG + 3) % KV_NS>{}, t + 3);
-        if (t < ntq) {
-          dscores(dst(stage));  // dS(t)
-          if (t + 1 == ntq) accumulate(qst(stage));  // last dK
-        }
+        dscores(dst(stage));  // dS(t)
+        if (t + 1 == ntq) accumulate(qst(stage));  // last dK
       }
       phase_barrier();  // P(t) consumed
     };
