@@ -278,7 +278,7 @@ typedef struct {
  *    writes dS (bf16, 2 bytes per score of every sample and head) to the
  *    workspace past bwd_workspace_bytes (rounded up to 4 KiB), and the DQ
  *    stage multiplies it by K-hat; stages in the order D, DKDV, DQ, GAINS.
- *    Measured within about 2% of the recompute mode on the mixed-resolution
+ *    Measured 2-3% slower than the recompute mode on the mixed-resolution
  *    pack; the area takes ds_base[S] KiB, about 2 * H * sum(L_i^2) bytes.
  * stages = 0 runs every stage of the recompute mode, stages =
  * MMDIT_STAGE_BWD_STORE_DS every stage of the stored-dS mode. The flag is
