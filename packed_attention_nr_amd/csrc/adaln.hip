@@ -75,9 +75,18 @@ struct Quad<float> {
 };
 
 __device__ __forceinline__ void zero4(float (&x)[4]) { x[0] = x[1] = x[2] = x[3] = 0.f; }
-__device__ __forceinline__ void ld_mod(const float *p, float (&x)[4]) {
-  const float4 v = *reinterpret_cast<const float4 *>(p);
-  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+
+// This thread's column groups of one fp32 modulation row of D values (zeros
+// past D, or everywhere for a null row). The loads carry no branch, so the
+// rows' loads are all in flight before the first value is used.
+template <int G>
+__device__ __forceinline__ void load_mod(const float *row, int D, const uint32_t (&moff)[G], float (&x)[G][4]) {
+  const rsrc_t r = make_rsrc(row, row ? 4u * (uint32_t)D : 0u);
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const f32x4 v = buf_load_f32x4(r, moff[j]);
+    x[j][0] = v[0]; x[j][1] = v[1]; x[j][2] = v[2]; x[j][3] = v[3];
+  }
 }
 
 // One token tensor seen by a chunk: resource over its rows [r_begin, r_end)
@@ -191,19 +200,18 @@ __global__ __launch_bounds__(kThreads) void adaln_fwd_kernel(PlanDev p, AdalnFwd
   load_rows<T, G, RB>(nx, tx, 0, coff);
   if constexpr (RES) load_rows<T, G, RB>(ny, ty, 0, coff);
   float sh[G][4], sc[G][4], gt[G][4];
+  {
+    uint32_t moff[G];
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    zero4(sh[j]);
-    zero4(sc[j]);
-    zero4(gt[j]);
-    if (ok[j]) {
-      ld_mod(a.shift + mrow + col[j], sh[j]);
-      ld_mod(a.scale + mrow + col[j], sc[j]);
-      if constexpr (RES) ld_mod(a.gate + mrow + col[j], gt[j]);
-    }
+    for (int j = 0; j < G; ++j) moff[j] = ok[j] ? 4u * (uint32_t)col[j] : kNoAccess;
+    load_mod<G>(a.shift + mrow, D, moff, sh);
+    load_mod<G>(a.scale + mrow, D, moff, sc);
+    load_mod<G>(RES ? a.gate + mrow : nullptr, D, moff, gt);
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[j][i] += 1.f;
-  }
   const float inv_d = 1.f / (float)D;
   int nb = 0;
   for (int k0 = 0; k0 < nrows; k0 += RB) {
@@ -268,26 +276,36 @@ __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwd
     ok[j] = col[j] < D;
     coff[j] = ok[j] ? (uint32_t)(col[j] * sizeof(T)) : kNoAccess;
   }
+  // The chunk's forward statistics, row r in lane r, requested before the
+  // first rows: a statistics load inside the loop would be issued behind the
+  // next row's loads, and waiting for it would wait for them as well.
+  static_assert(kModChunkRows <= 64, "one chunk row per lane");
+  float2 st_lane = make_float2(0.f, 0.f);
+  if (a.stats && lane < nrows) st_lane = a.stats[ch.x + lane];
   raw nx[RB][G], ny[RB][G], ng[RB][G], ne[RB][G];
   load_rows<T, G, RB>(nx, tx, 0, coff);
   if constexpr (RES) load_rows<T, G, RB>(ny, ty, 0, coff);
   load_rows<T, G, RB>(ng, tg, 0, coff);
   load_rows<T, G, RB>(ne, te, 0, coff);  // all zeros when dz is absent
   float sc[G][4], gt[G][4], ash[G][4], asc[G][4], agt[G][4];
+  {
+    uint32_t moff[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) moff[j] = ok[j] ? 4u * (uint32_t)col[j] : kNoAccess;
+    load_mod<G>(a.scale + mrow, D, moff, sc);
+    load_mod<G>(RES ? a.gate + mrow : nullptr, D, moff, gt);
+  }
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    zero4(sc[j]);
-    zero4(gt[j]);
     zero4(ash[j]);
     zero4(asc[j]);
     zero4(agt[j]);
-    if (ok[j]) {
-      ld_mod(a.scale + mrow + col[j], sc[j]);
-      if constexpr (RES) ld_mod(a.gate + mrow + col[j], gt[j]);
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[j][i] += 1.f;
   }
+  // Everything above arrives together with the first row; waiting for all of
+  // it here lets the loop's waits count the row loads alone.
+  wait_vmem();
   const float inv_d = 1.f / (float)D;
   int nb = 0;
   for (int k0 = 0; k0 < nrows; k0 += RB) {
@@ -316,9 +334,9 @@ __global__ __launch_bounds__(kThreads) void adaln_bwd_kernel(PlanDev p, AdalnBwd
     if (a.stats) {
 #pragma unroll
       for (int rr = 0; rr < RB; ++rr) {
-        const float2 st = a.stats[ch.x + min(k0 + rr, nrows - 1)];
-        mean[rr] = st.x;
-        rstd[rr] = st.y;
+        const int r = min(k0 + rr, nrows - 1);
+        mean[rr] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(st_lane.x), r));
+        rstd[rr] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(st_lane.y), r));
       }
     } else {
       row_stats<G, RB>(z, ok, inv_d, a.eps, mean, rstd, red, nb, wave, lane);
