@@ -423,15 +423,17 @@ __global__ __launch_bounds__(256) void adaln_reduce_kernel(BlobGuard guard, cons
   if (c < D) {
     const float *src = part + (int64_t)k * D + c;
     const int64_t step = 3 * (int64_t)D;
-    int q = c0 + w;
-    for (; q + 28 < c1; q += 32) {  // eight loads in flight, added in chunk order
-      float t[8];
+    // Up to 32 loads in flight per wave (every chunk of a range of up to 128
+    // in one round trip), added in chunk order.
+    constexpr int U = 32;
+    for (int q = c0 + w; q < c1; q += 4 * U) {
+      float t[U];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = src[(int64_t)(q + 4 * u) * step];
+      for (int u = 0; u < U; ++u) t[u] = q + 4 * u < c1 ? src[(int64_t)(q + 4 * u) * step] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += t[u];
+      for (int u = 0; u < U; ++u)
+        if (q + 4 * u < c1) s += t[u];
     }
-    for (; q < c1; q += 4) s += src[(int64_t)q * step];
   }
   red[w][lane] = s;
   __syncthreads();
