@@ -191,7 +191,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(PlanDev p, AttnFw
     // -inf) takes the exact online-softmax step: the row maxima, a raised
     // reference when they pass it by kRescaleThreshold, and P formed again.
     // Either way the result is the same softmax; only the reference differs.
-    float ts = exp_pack();
+    // On the first tile the reference is -inf and the exact step always runs,
+    // so P is formed only once there, after the maxima.
+    float ts = t == 0 ? INFINITY : exp_pack();
     if (__ballot(!(ts <= kSumLimit))) {
       float mx = -INFINITY;
 #pragma unroll
