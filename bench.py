@@ -407,7 +407,47 @@ def probes(pam, torch, dev):
             best = {"gbs": round(gbs, 1), "frac_of_spec": round(gbs / PEAK_HBM_GBS, 4), "blocks": blocks,
                     "what": "mmdit::copy_kernel over 1 GiB, non-temporal 16-byte accesses (read + write counted)"}
     del a, b
-    return {"mfma_loop": mfma, "hbm_copy_torch": copy, "hbm_copy": best}
+    return {"mfma_loop": mfma, "hbm_copy_torch": copy, "hbm_copy": best, "hbm_streams": stream_probes(pam, torch, dev)}
+
+
+STREAM_MIXES = {"1r0w": (1, 0), "1r1w": (1, 1), "2r2w": (2, 2), "4r2w": (4, 2)}
+
+
+def stream_probes(pam, torch, dev, mib=512):
+    """HBM rate of several read and write streams at once (mmdit_probe_streams,
+    `mib` MiB per stream, best over grid sizes and per-thread unroll): the
+    ceilings of the memory-bound kernels' own mixes -- two in, two out for the
+    QK prologue and the adaLN forward, four in, two out for the adaLN
+    backward."""
+    import ctypes as C
+    L = pam.lib()
+    L.mmdit_probe_streams.restype = C.c_int
+    L.mmdit_probe_streams.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.POINTER(C.c_void_p), C.c_int32,
+                                      C.c_uint64, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+    nbytes = mib << 20
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(6)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, (nr, nw) in STREAM_MIXES.items():
+        srcs = (C.c_void_p * 4)(*[b.data_ptr() for b in bufs[:nr]])
+        dsts = (C.c_void_p * 2)(*[b.data_ptr() for b in bufs[nr:nr + nw]])
+        best = None
+        for blocks in (2048, 4096, 8192, 16384):
+            for unroll in (1, 2):
+                run = lambda: L.mmdit_probe_streams(srcs, nr, dsts, nw, nbytes, blocks, unroll, sink.data_ptr(),
+                                                    stream.cuda_stream)
+                assert run() == 0, pam.mmdit_last_error()
+                t, _ = time_stage(torch, run, min_reps=10, max_reps=40, target_s=0.05)
+                gbs = (nr + nw) * nbytes / t / 1e6
+                if best is None or gbs > best["gbs"]:
+                    best = {"gbs": round(gbs, 1), "frac_of_spec": round(gbs / PEAK_HBM_GBS, 4),
+                            "blocks": blocks, "unroll": unroll}
+        out[name] = best
+    del bufs
+    return out
 
 
 def pass_runner(pam, torch, dev, text, hs, ws, H, d, backward, seed, src=None):
@@ -736,6 +776,18 @@ def main():
         "sclk_reported_step": step_clock,
     }
     result.update(extras)
+    # The memory-bound kernels against the measured rate of their own stream
+    # mix (context; the fractions above are of the 8 TB/s spec).
+    streams = (peaks or {}).get("hbm_streams")
+    if streams:
+        rel = {"prologue_fwd_step": round(pro_gbs / streams["2r2w"]["gbs"], 4)}
+        for name, c in per_config.items():
+            rel[f"prologue_fwd_{name}"] = round(c["prologue_fwd"]["gbs"] / streams["2r2w"]["gbs"], 4)
+        ad = result.get("adaln_gated_residual")
+        if ad:
+            rel["adaln_fwd"] = round(ad["fwd"]["gbs"] / streams["2r2w"]["gbs"], 4)
+            rel["adaln_bwd"] = round(ad["bwd"]["gbs"] / streams["4r2w"]["gbs"], 4)
+        result["frac_of_stream_probe"] = rel
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_heads)
     print(json.dumps(result), flush=True)

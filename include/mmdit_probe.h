@@ -36,6 +36,23 @@ mmdit_status mmdit_probe_mfma(int32_t blocks, int32_t iters, uint64_t *clocks, f
  * errors: INVALID_ARG, HIP. */
 mmdit_status mmdit_probe_copy(const void *src, void *dst, uint64_t bytes, int32_t blocks, void *hip_stream);
 
+/* Stream nsrc source buffers into ndst destination buffers at once, `bytes`
+ * (a positive multiple of 16) each: srcs and dsts are HOST arrays of device
+ * pointers (16-byte aligned, no two buffers overlapping); `blocks`
+ * workgroups of 256 threads, each thread loading `unroll` (1 or 2) 16-byte
+ * words of every source per grid-stride step with non-temporal accesses
+ * before storing to every destination. dsts[w] receives the XOR of the
+ * sources' words with w added to the first 32-bit component of each word
+ * (so the result can be checked). With ndst = 0 the loads are folded into a
+ * value written to *sink (a device uint32, required then) only in a case no
+ * input here produces. Supported (nsrc, ndst): (1,0) read-only, (1,1) copy,
+ * (2,1), (2,2) (the QK prologue's mix) and (4,2) (the adaLN backward's).
+ * Moved bytes = (nsrc + ndst) * bytes. Enqueues only; errors: INVALID_ARG
+ * (unsupported mix or unroll, NULL, misaligned or overlapping buffers),
+ * HIP. */
+mmdit_status mmdit_probe_streams(const void *const *srcs, int32_t nsrc, void *const *dsts, int32_t ndst,
+                                 uint64_t bytes, int32_t blocks, int32_t unroll, uint32_t *sink, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,7 +1,10 @@
 // Measurement probes (context for the rooflines, not part of the method): a
 // dense loop of bf16 matrix instructions that gives the throughput the chip
-// sustains on them and its core clock under that load, and a streaming copy
-// that gives the HBM bandwidth a plain read-once / write-once kernel reaches.
+// sustains on them and its core clock under that load, a streaming copy
+// that gives the HBM bandwidth a plain read-once / write-once kernel reaches,
+// and streams of several read and write tensors at once (the mixes of the
+// memory-bound kernels: two in, two out for the QK prologue; four in, two
+// out for the adaLN backward), whose rate falls with the number of streams.
 //
 // Every wave runs `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16
 // (32,768 FLOP each) on register operands, so nothing but the matrix pipes
@@ -66,7 +69,94 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *src, u32x4 *dst,
   }
 }
 
+// R source and W destination streams of n16 16-byte words each: per
+// grid-stride step every thread loads U words of each source (all loads
+// before the stores, non-temporal) and stores to each destination the XOR of
+// the sources' words with destination index w added to the first component.
+// With no destination the words are folded into one value that is written
+// to sink only if it equals a constant no input here produces, which keeps
+// the loads live.
+struct StreamPtrs {
+  const u32x4 *r[4];
+  u32x4 *w[2];
+};
+template <int R, int W, int U>
+__global__ __launch_bounds__(256) void stream_kernel(StreamPtrs p, int64_t n16, unsigned *sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * U;
+  unsigned x = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 * U + threadIdx.x; i < n16; i += stride) {
+    u32x4 v[R][U];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t k = i + 256 * u;
+        v[r][u] = k < n16 ? __builtin_nontemporal_load(p.r[r] + k) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      u32x4 t = v[0][u];
+#pragma unroll
+      for (int r = 1; r < R; ++r) t ^= v[r][u];
+      const int64_t k = i + 256 * u;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        u32x4 o = t;
+        o.x += (unsigned)w;
+        if (k < n16) __builtin_nontemporal_store(o, p.w[w] + k);
+      }
+      if constexpr (W == 0) x ^= t.x ^ t.y ^ t.z ^ t.w;
+    }
+  }
+  if constexpr (W == 0)
+    if (x == 0x9E3779B9u) sink[0] = x;
+}
+
 }  // namespace mmdit
+
+extern "C" mmdit_status mmdit_probe_streams(const void *const *srcs, int32_t nsrc, void *const *dsts, int32_t ndst,
+                                            uint64_t bytes, int32_t blocks, int32_t unroll, uint32_t *sink,
+                                            void *hip_stream) {
+  mmdit::clear_error();
+  const int kind = 10 * nsrc + ndst;
+  if (!(kind == 10 || kind == 11 || kind == 21 || kind == 22 || kind == 42) || (unroll != 1 && unroll != 2))
+    return mmdit::fail(MMDIT_ERR_INVALID_ARG,
+                       "streams (nsrc, ndst) must be (1,0), (1,1), (2,1), (2,2) or (4,2) and unroll 1 or 2");
+  if (!srcs || (ndst > 0 && !dsts) || bytes % 16 || bytes == 0 || blocks < 1)
+    return mmdit::fail(MMDIT_ERR_INVALID_ARG, "srcs/dsts must be host arrays, bytes a positive multiple of 16, blocks >= 1");
+  if (ndst == 0 && !sink) return mmdit::fail(MMDIT_ERR_INVALID_ARG, "a read-only probe needs a sink word");
+  mmdit::StreamPtrs sp{};
+  uintptr_t all[6];
+  for (int i = 0; i < nsrc + ndst; ++i) {
+    const void *q = i < nsrc ? srcs[i] : dsts[i - nsrc];
+    all[i] = reinterpret_cast<uintptr_t>(q);
+    if (!q || (all[i] & 15u)) return mmdit::fail(MMDIT_ERR_INVALID_ARG, "stream %d is NULL or not 16-byte aligned", i);
+    for (int j = 0; j < i; ++j)
+      if (all[i] < all[j] + bytes && all[j] < all[i] + bytes)
+        return mmdit::fail(MMDIT_ERR_INVALID_ARG, "streams %d and %d overlap", j, i);
+    if (i < nsrc) sp.r[i] = static_cast<const mmdit::u32x4 *>(q);
+    else sp.w[i - nsrc] = static_cast<mmdit::u32x4 *>(const_cast<void *>(q));
+  }
+  const int64_t n16 = (int64_t)(bytes / 16);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const dim3 grid((unsigned)blocks), blk(256);
+#define MMDIT_STREAM_CASE(R, W)                                                                     \
+  case 10 * R + W:                                                                                  \
+    if (unroll == 1) hipLaunchKernelGGL((mmdit::stream_kernel<R, W, 1>), grid, blk, 0, s, sp, n16, sink); \
+    else hipLaunchKernelGGL((mmdit::stream_kernel<R, W, 2>), grid, blk, 0, s, sp, n16, sink);             \
+    break;
+  switch (kind) {
+    MMDIT_STREAM_CASE(1, 0)
+    MMDIT_STREAM_CASE(1, 1)
+    MMDIT_STREAM_CASE(2, 1)
+    MMDIT_STREAM_CASE(2, 2)
+    MMDIT_STREAM_CASE(4, 2)
+  }
+#undef MMDIT_STREAM_CASE
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return mmdit::fail(MMDIT_ERR_HIP, "probe launch failed: %s", hipGetErrorString(e));
+  return MMDIT_OK;
+}
 
 extern "C" mmdit_status mmdit_probe_copy(const void *src, void *dst, uint64_t bytes, int32_t blocks,
                                          void *hip_stream) {

@@ -29,7 +29,7 @@ def test_exports_every_header_symbol(L):
     for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
         names |= set(re.findall(r"\b(mmdit_[a-z_]+)\s*\(", open(h).read()))
     assert {"mmdit_pack_plan", "mmdit_attn_fwd", "mmdit_attn_bwd", "mmdit_attn_bwd_noalloc",
-            "mmdit_device_faults", "mmdit_probe_mfma"} <= names
+            "mmdit_device_faults", "mmdit_probe_mfma", "mmdit_probe_streams"} <= names
     for n in sorted(names):
         assert hasattr(L, n), n
     assert pam.mmdit_abi_version() == pam.ABI_VERSION == 5
@@ -531,3 +531,27 @@ def test_noalloc_refuses_before_touching_a_device(L):
     assert _noalloc(big) == 3, pam.mmdit_last_error()
     assert "exceeds" in pam.mmdit_last_error()
     assert _noalloc(None) == 1
+
+
+def test_stream_probe_rejects_bad_arguments(L):
+    """mmdit_probe_streams checks its arguments before it launches anything
+    (no GPU needed): unsupported mixes and unrolls, misaligned and
+    overlapping buffers, a read-only probe without a sink."""
+    import ctypes as C
+    L.mmdit_probe_streams.restype = C.c_int
+    L.mmdit_probe_streams.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.POINTER(C.c_void_p), C.c_int32,
+                                      C.c_uint64, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+    base = 1 << 40
+    srcs = (C.c_void_p * 4)(base, base + (1 << 30), base + (2 << 30), base + (3 << 30))
+    dsts = (C.c_void_p * 2)(base + (4 << 30), base + (5 << 30))
+    INVALID = 1
+    for nr, nw in [(3, 1), (1, 2), (4, 1), (0, 1)]:
+        assert L.mmdit_probe_streams(srcs, nr, dsts, nw, 1 << 20, 8, 1, None, None) == INVALID
+    assert L.mmdit_probe_streams(srcs, 2, dsts, 2, 1 << 20, 8, 3, None, None) == INVALID     # unroll
+    assert L.mmdit_probe_streams(srcs, 2, dsts, 2, (1 << 20) + 8, 8, 1, None, None) == INVALID  # bytes
+    assert L.mmdit_probe_streams(srcs, 1, dsts, 0, 1 << 20, 8, 1, None, None) == INVALID     # no sink
+    bad = (C.c_void_p * 4)(base + 8, base + (1 << 30), 0, 0)
+    assert L.mmdit_probe_streams(bad, 2, dsts, 2, 1 << 20, 8, 1, None, None) == INVALID      # misaligned
+    ovl = (C.c_void_p * 4)(base, base + (1 << 19), 0, 0)
+    assert L.mmdit_probe_streams(ovl, 2, dsts, 2, 1 << 20, 8, 1, None, None) == INVALID      # overlap
+    assert "overlap" in pam.mmdit_last_error()
