@@ -80,7 +80,9 @@ typedef enum {
   MMDIT_ERR_UNSUPPORTED = 2,       /* valid but not built: e.g. head_dim not 64 or 128 */
   MMDIT_ERR_BUFFER_TOO_SMALL = 3,  /* host blob or workspace smaller than required */
   MMDIT_ERR_BUDGET = 4,            /* total tokens exceed the descriptor's token budget */
-  MMDIT_ERR_HIP = 5                /* a HIP launch failed; see mmdit_last_error() */
+  MMDIT_ERR_HIP = 5                /* a HIP launch failed; see mmdit_last_error(). Test hook: with
+                                      MMDIT_FAULT_INJECT=launch in the environment, mmdit_attn_fwd, mmdit_attn_bwd(_noalloc)
+                                      and mmdit_adaln_fwd/bwd return it where they would launch, having launched nothing */
 } mmdit_status;
 
 typedef enum { MMDIT_F32 = 0, MMDIT_BF16 = 1 } mmdit_dtype;

@@ -169,7 +169,7 @@ static mmdit_status attn_fwd(const mmdit_plan *plan, const void *blob, const mmd
   }
   if ((st = check_aliasing(spans))) return st;
   uint32_t *fault = nullptr;
-  if ((st = device_fault_word(stream, &fault))) return st;
+  if ((st = injected_launch_fault()) || (st = device_fault_word(stream, &fault))) return st;
 
   const PlanDev pd = plan_dev(*plan, blob, fault);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -278,7 +278,7 @@ mmdit_status attn_bwd(const mmdit_plan *plan, const void *blob, const mmdit_bwd_
   }
   if ((st = check_aliasing(spans))) return st;
   uint32_t *fault = nullptr;
-  if ((st = device_fault_word(stream, &fault))) return st;
+  if ((st = injected_launch_fault()) || (st = device_fault_word(stream, &fault))) return st;
 
   const PlanDev pd = plan_dev(*plan, blob, fault);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -370,7 +370,7 @@ static mmdit_status adaln_fwd(const mmdit_plan *plan, const void *blob, const mm
   }
   if ((st = check_aliasing(spans))) return st;
   uint32_t *fault = nullptr;
-  if ((st = device_fault_word(stream, &fault))) return st;
+  if ((st = injected_launch_fault()) || (st = device_fault_word(stream, &fault))) return st;
   const PlanDev pd = plan_dev(*plan, blob, fault);
   AdalnFwdArgs fa{a->x, a->y, a->x_stride, a->y_stride, a->shift, a->scale, a->gate, a->z, a->h,
                   reinterpret_cast<float2 *>(a->stats), a->model_dim, a->eps};
@@ -429,7 +429,7 @@ static mmdit_status adaln_bwd(const mmdit_plan *plan, const void *blob, const mm
   }
   if ((st = check_aliasing(spans))) return st;
   uint32_t *fault = nullptr;
-  if ((st = device_fault_word(stream, &fault))) return st;
+  if ((st = injected_launch_fault()) || (st = device_fault_word(stream, &fault))) return st;
   const PlanDev pd = plan_dev(*plan, blob, fault);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float *part = static_cast<float *>(ws);

@@ -95,6 +95,7 @@ struct BlobGuard {
 // The current device's fault word, after checking that `stream` (NULL =
 // the default stream) belongs to the current device.
 mmdit_status device_fault_word(void *stream, uint32_t **word);
+mmdit_status injected_launch_fault();  // test hook: MMDIT_FAULT_INJECT=launch
 
 struct PlanDev {
   const int32_t *cu_seqlens;   // [S+1]

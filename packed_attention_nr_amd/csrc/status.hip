@@ -7,6 +7,8 @@
 // __device__ object, one per GPU; in host code its name is only a handle, and
 // its device address comes from hipGetSymbolAddress (once per device, with
 // that device current). mmdit_device_faults reads and clears it.
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "internal.h"
@@ -39,6 +41,19 @@ mmdit_status current_device(void *stream, int *dev_out) {
   return MMDIT_OK;
 }
 }  // namespace
+
+// Test hook for the launch-failure path: with MMDIT_FAULT_INJECT=launch in the
+// environment, the entry points that launch the method's kernels fail where
+// they would launch (after their argument checks, before any HIP call) with
+// MMDIT_ERR_HIP and a message naming the hook; unset (or any other value), it
+// does nothing. The variable is read on every call, so a test can set and
+// clear it within one process.
+mmdit_status injected_launch_fault() {
+  const char *v = std::getenv("MMDIT_FAULT_INJECT");
+  if (v && std::strcmp(v, "launch") == 0)
+    return fail(MMDIT_ERR_HIP, "kernel launch failed: fault injected by MMDIT_FAULT_INJECT=launch (test hook)");
+  return MMDIT_OK;
+}
 
 mmdit_status device_fault_word(void *stream, uint32_t **word) {
   int dev = -1;

@@ -316,3 +316,33 @@ def test_explicit_side_stream():
     f2 = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"], stream=side.cuda_stream)
     side.synchronize()
     assert torch.equal(f2["o"], ref_f["o"])
+
+
+def test_fault_injection_hook_on_the_gpu(monkeypatch):
+    """With MMDIT_FAULT_INJECT=launch the calls fail with MMDIT_ERR_HIP and
+    write nothing; with the variable cleared, the same calls in the same
+    process give the results of a run before it was set."""
+    import packed_attention_nr_amd as pam
+    inp = workloads.random_pack(3, heads=2, head_dim=128, dtype="bf16", text=[21, 0], grids=[(6, 11), (9, 4)])
+    _say(f"fault injection N={inp.num_tokens}")
+    pack, t = _pack_and_inputs(inp)
+    ref = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"])
+    refb = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], ref, t["dout"])
+    torch.cuda.synchronize()
+    monkeypatch.setenv("MMDIT_FAULT_INJECT", "launch")
+    o = torch.full_like(ref["o"], 3.0)
+    with pytest.raises(pam.MmditError) as e:
+        pam.mmdit_attn_fwd(pack.plan, pack.blob_dev, q=t["q"], k=t["k"], v=t["v"], q_stride=pack.H * pack.d,
+                           k_stride=pack.H * pack.d, v_stride=pack.H * pack.d, gains=t["gains"], o=o,
+                           lse=torch.empty_like(ref["lse"]), q_hat=torch.empty_like(ref["q_hat"]),
+                           k_hat=torch.empty_like(ref["k_hat"]), rstd=torch.empty_like(ref["rstd"]))
+    assert e.value.status == 5 and "MMDIT_FAULT_INJECT" in str(e.value)
+    with pytest.raises(pam.MmditError):
+        pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], ref, t["dout"])
+    torch.cuda.synchronize()
+    assert bool((o == 3.0).all()), "a call with an injected fault wrote its output"
+    monkeypatch.delenv("MMDIT_FAULT_INJECT")
+    f = pam.forward(pack, t["q"], t["k"], t["v"], t["gains"])
+    b = pam.backward(pack, t["q"], t["k"], t["v"], t["gains"], f, t["dout"])
+    torch.cuda.synchronize()
+    assert torch.equal(f["o"], ref["o"]) and torch.equal(b["dq"], refb["dq"]) and torch.equal(b["dgains"], refb["dgains"])

@@ -456,6 +456,21 @@ def test_adaln_bwd_rejects_invalid_arguments(small_plan, kw, code):
     assert _adaln_bwd(small_plan, **kw) == code, pam.mmdit_last_error()
 
 
+def test_fault_injection_hook(small_plan, monkeypatch):
+    """MMDIT_FAULT_INJECT=launch: every entry point that launches kernels
+    returns MMDIT_ERR_HIP where it would launch, after its argument checks
+    (which still win) and before any HIP call, so this runs without a GPU."""
+    monkeypatch.setenv("MMDIT_FAULT_INJECT", "launch")
+    for call in (_fwd, _bwd, _adaln_fwd, _adaln_bwd):
+        assert call(small_plan) == 5, call.__name__
+        assert "MMDIT_FAULT_INJECT" in pam.mmdit_last_error()
+    assert _fwd(small_plan, q=None) == 1
+    assert _bwd(small_plan, dq=None) == 1
+    monkeypatch.setenv("MMDIT_FAULT_INJECT", "other")
+    assert _fwd(small_plan, q=None) == 1
+    assert "MMDIT_FAULT_INJECT" not in pam.mmdit_last_error()
+
+
 # --------------------------------------------------------------------------
 # packed classifier-free guidance: descriptor of conditional + unconditional
 # --------------------------------------------------------------------------
