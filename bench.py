@@ -38,6 +38,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -190,40 +191,58 @@ class Flush:
 
 
 def _sclk_path():
-    """hwmon core-clock file of the GPU in use (matched by PCI address when
-    several cards are listed), or None."""
-    paths = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/freq1_input"))
-    paths = [p for p in paths if os.access(p, os.R_OK)]
-    if len(paths) <= 1:
-        return paths[0] if paths else None
-    try:
-        import torch
-        pr = torch.cuda.get_device_properties(torch.cuda.current_device())
-        want = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}"
-    except Exception:
-        return None
-    for p in paths:
-        dev = os.path.basename(os.path.realpath(p.split("/hwmon/")[0]))
-        if dev.lower().startswith(want):
-            return p
+    """(kind, path) of a readable core-clock file of the GPU in use, or None:
+    hwmon freq1_input (Hz), else the DPM table pp_dpm_sclk, whose starred line
+    is the current clock in MHz (matched by PCI address when several cards
+    are listed)."""
+    for kind, pattern in (("hwmon", "/sys/class/drm/card*/device/hwmon/hwmon*/freq1_input"),
+                          ("dpm", "/sys/class/drm/card*/device/pp_dpm_sclk")):
+        paths = sorted(p for p in glob.glob(pattern) if os.access(p, os.R_OK))
+        if len(paths) == 1:
+            return kind, paths[0]
+        if len(paths) > 1:
+            try:
+                import torch
+                pr = torch.cuda.get_device_properties(torch.cuda.current_device())
+                want = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}"
+            except Exception:
+                return None
+            for p in paths:
+                dev = os.path.basename(os.path.realpath(p.split("/hwmon/")[0].replace("/pp_dpm_sclk", "")))
+                if dev.lower().startswith(want):
+                    return kind, p
+            return None
     return None
 
 
+def _read_mhz(kind, path):
+    with open(path) as fh:
+        text = fh.read()
+    if kind == "hwmon":
+        return int(text.strip()) / 1e6
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+            if m:
+                return float(m.group(1))
+    raise ValueError("no current level in " + path)
+
+
 class ClockSampler:
-    """Samples the GPU's reported core clock (hwmon freq1_input, in Hz) every
-    few milliseconds from a thread while work runs; summary() is None where
-    the file is not readable."""
+    """Samples the GPU's reported core clock (hwmon freq1_input, else the
+    current level of pp_dpm_sclk) every few milliseconds from a thread while
+    work runs; summary() is None where neither file is readable."""
 
     def __init__(self, period_s=0.005):
-        self.path = _sclk_path()
+        found = _sclk_path()
+        self.kind, self.path = found if found else (None, None)
         self.period = period_s
         self.samples = []
 
     def _run(self):
         while not self.stop.is_set():
             try:
-                with open(self.path) as fh:
-                    self.samples.append(int(fh.read().strip()) / 1e6)
+                self.samples.append(_read_mhz(self.kind, self.path))
             except (OSError, ValueError):
                 pass
             time.sleep(self.period)
@@ -246,7 +265,7 @@ class ClockSampler:
             return None
         a = np.asarray(self.samples)
         return {"mhz_median": round(float(np.median(a)), 1), "mhz_min": round(float(a.min()), 1),
-                "mhz_max": round(float(a.max()), 1), "samples": int(a.size)}
+                "mhz_max": round(float(a.max()), 1), "samples": int(a.size), "source": self.kind}
 
 
 def time_stage(torch, fn, flush=None, min_reps=50, max_reps=2000, target_s=0.5):
